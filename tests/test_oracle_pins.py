@@ -1,0 +1,264 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+The oracle is plain loops in C (oracle/lora_oracle.c).  None of these checks
+re-types its loops: each one evaluates the same quantity another way.
+
+* golden: a tiny integer example worked by hand from the per-row equation
+  (page "Multi-LoRA Serving: one base, many adapters", sections 2 and 3.1);
+* dense delta: Delta W = B A materialised with numpy's matmul, then applied
+  (section 3.1 says the factored form computes the same Delta W x);
+* merged weight: a single adapter equals serving the merged weight
+  W + (alpha/r) B A (page "LoRA serving: multi-adapter dynamic loading",
+  section 1 on merge vs adapter inference), exact on integer data;
+* rank-1 closed form: (alpha/r) b (a . x);
+* invariants: row permutation, slot relabelling, linearity in alpha, B = 0,
+  untouched none / bad rows;
+* segments: numpy's stable argsort of the routing key;
+* parameter count: r(d + k) with the values the pages print.
+
+``test_planted_mistake_is_caught`` compiles copies of the oracle with one
+plausible mistake each (dropped term, wrong sign, transposed operand, wrong
+scale, ...) and checks that at least one pin fails for every copy.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import compare
+from rank_adapter_gemm_lora_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden")
+
+
+def _f64(a, dtype):
+    return compare.to_f64(a, dtype)
+
+
+def _run(lib, p, rows=None, y=None, ranks=None, alphas=None, A=None, B=None, ids=None, x=None):
+    return oracle.apply_rows(p.dtype, p.k, p.slice_d,
+                             p.ranks if ranks is None else ranks,
+                             p.alphas if alphas is None else alphas,
+                             p.A if A is None else A, p.B if B is None else B,
+                             p.ids if ids is None else ids,
+                             p.x if x is None else x, p.y if y is None else y,
+                             rows=rows, lib=lib)
+
+
+def _valid(ids, ranks):
+    n_slots = len(ranks)
+    return np.array([0 <= s < n_slots and ranks[s] > 0 for s in ids], bool)
+
+
+def _small_problems():
+    """Seeded small problems covering slices, mixed ranks, empty slots, none and
+    bad ids, padded row strides, both dtypes."""
+    out = []
+    p = synth.make_random(11, n_rows=13, k=40, slice_d=[24, 8, 16], n_slots=5,
+                          ranks=[3, 0, 8, 1, 5], r_max=8, dtype="f32", alpha=[6, 1, 16, 3, 7],
+                          p_none=0.2, std_y=0.5)
+    p.ids[2] = 1    # empty slot -> bad id
+    p.ids[7] = 9    # out of range -> bad id
+    p.ids[9] = -4   # negative, not -1 -> bad id
+    out.append(synth.with_strides(p, 8, 5, seed=3))
+    q = synth.make_random(12, n_rows=9, k=64, slice_d=[32, 32], n_slots=4,
+                          ranks=[16, 8, 2, 16], r_max=16, dtype="bf16", alpha=32.0,
+                          p_none=0.3)
+    out.append(q)
+    return out
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_golden_worked(lib):
+    g = json.load(open(os.path.join(GOLDEN, "tiny_worked.json")))
+    ranks = np.array(g["ranks"], np.int32)
+    A = [None if a is None else np.array(a, np.float32) for a in g["A"]]
+    B = [None if b is None else np.array(b, np.float32) for b in g["B"]]
+    y = oracle.apply_rows("f32", g["k"], g["slice_d"], ranks, np.array(g["alphas"]), A, B,
+                          np.array(g["ids"], np.int32), np.array(g["x"], np.float32),
+                          np.array(g["y_in"], np.float32), lib=lib)
+    np.testing.assert_array_equal(y, np.array(g["expected_y"], np.float64))
+    seg = oracle.build_segments(np.array(g["ids"], np.int32), len(ranks), ranks, lib=lib)
+    np.testing.assert_array_equal(seg["perm"], g["expected_perm"])
+    np.testing.assert_array_equal(seg["seg_off"], g["expected_seg_off"])
+    n_act = g["expected_counts"][1]
+    np.testing.assert_array_equal(seg["active"][:n_act], g["expected_active"])
+    np.testing.assert_array_equal(seg["counts"], g["expected_counts"])
+
+
+def pin_dense_delta(lib):
+    """Materialise Delta W_q = B_q A_q (numpy matmul) and apply it."""
+    for p in _small_problems():
+        got = _run(lib, p)
+        x = _f64(p.x, p.dtype)[:, :p.k]
+        y = _f64(p.y, p.dtype)[:, :p.D]
+        want = y.copy()
+        offs = np.concatenate([[0], np.cumsum(p.slice_d)])
+        for i, s in enumerate(p.ids):
+            if not (0 <= s < p.n_slots and p.ranks[s] > 0):
+                continue
+            A = _f64(p.A[s], p.dtype)
+            B = _f64(p.B[s], p.dtype)
+            scale = float(p.alphas[s]) / float(p.ranks[s])
+            for q in range(p.n_slices):
+                dW = B[offs[q]:offs[q + 1], :] @ A[q]          # [d_q, k]
+                want[i, offs[q]:offs[q + 1]] += scale * (dW @ x[i])
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def pin_merged_weight(lib):
+    """Each slot alone on every row equals (W + (alpha/r) B A) x, exactly on
+    small integers (every intermediate is an exact integer in fp32 and fp64)."""
+    rng = np.random.default_rng(5)
+    k, slice_d, n = 12, [6, 10], 7
+    D = sum(slice_d)
+    ranks = np.array([2, 3, 1], np.int32)
+    alphas = np.array([4.0, 6.0, 2.0], np.float32)       # scale 2 for every slot
+    A = [rng.integers(-2, 3, size=(2, r, k)).astype(np.float32) for r in ranks]
+    B = [rng.integers(-2, 3, size=(D, r)).astype(np.float32) for r in ranks]
+    W = rng.integers(-3, 4, size=(D, k)).astype(np.float64)
+    x = rng.integers(-2, 3, size=(n, k)).astype(np.float32)
+    y_in = (x.astype(np.float64) @ W.T).astype(np.float32)
+    offs = np.concatenate([[0], np.cumsum(slice_d)])
+    for s in range(3):
+        ids = np.full(n, s, np.int32)
+        got = oracle.apply_rows("f32", k, slice_d, ranks, alphas, A, B, ids, x, y_in, lib=lib)
+        Wm = W.copy()
+        for q in range(2):
+            Wm[offs[q]:offs[q + 1]] += 2.0 * (B[s][offs[q]:offs[q + 1]].astype(np.float64)
+                                              @ A[s][q].astype(np.float64))
+        np.testing.assert_array_equal(got, x.astype(np.float64) @ Wm.T)
+
+
+def pin_rank1_closed_form(lib):
+    """A rank-1 adapter adds (alpha/1) * b * (a . x) to every row it serves."""
+    rng = np.random.default_rng(8)
+    k, D, n = 33, 17, 6
+    a = rng.standard_normal((1, 1, k)).astype(np.float32)
+    b = rng.standard_normal((D, 1)).astype(np.float32)
+    x = rng.standard_normal((n, k)).astype(np.float32)
+    y = rng.standard_normal((n, D)).astype(np.float32)
+    ids = np.zeros(n, np.int32)
+    got = oracle.apply_rows("f32", k, [D], np.array([1], np.int32), np.array([3.0]), [a], [b],
+                            ids, x, y, lib=lib)
+    for i in range(n):
+        dot = float(np.dot(a[0, 0].astype(np.float64), x[i].astype(np.float64)))
+        want = y[i].astype(np.float64) + 3.0 * b[:, 0].astype(np.float64) * dot
+        np.testing.assert_allclose(got[i], want, rtol=1e-13, atol=1e-13)
+
+
+def pin_invariants(lib):
+    for p in _small_problems():
+        base = _run(lib, p)
+        y_in = _f64(p.y, p.dtype)[:, :p.D]
+        ok = _valid(p.ids, p.ranks)
+        # none / bad rows keep the base output exactly
+        np.testing.assert_array_equal(base[~ok], y_in[~ok])
+        # row permutation: each row's result does not depend on its neighbours
+        perm = np.random.default_rng(1).permutation(p.n_rows)
+        got = _run(lib, p, ids=p.ids[perm], x=p.x[perm], y=p.y[perm])
+        np.testing.assert_array_equal(got, base[perm])
+        # slot relabelling: moving adapters to other slots changes nothing
+        sigma = np.random.default_rng(2).permutation(p.n_slots)   # old slot s -> sigma[s]
+        inv = np.argsort(sigma)
+        ids2 = np.array([sigma[s] if 0 <= s < p.n_slots else s for s in p.ids], np.int32)
+        got = _run(lib, p, ids=ids2, ranks=p.ranks[inv], alphas=p.alphas[inv],
+                   A=[p.A[j] for j in inv], B=[p.B[j] for j in inv])
+        np.testing.assert_array_equal(got, base)
+        # linearity in alpha (with y_in = 0 every step is exact)
+        zero = np.zeros_like(p.y)
+        d1 = _run(lib, p, y=zero)
+        d2 = _run(lib, p, y=zero, alphas=p.alphas * np.float32(2))
+        np.testing.assert_array_equal(d2, 2.0 * d1)
+        # B = 0: nothing is added
+        Bz = [None if b is None else np.zeros_like(b) for b in p.B]
+        np.testing.assert_array_equal(_run(lib, p, B=Bz), y_in)
+        # evaluating a subset of rows gives the same rows
+        rows = np.array([p.n_rows - 1, 0, 3], np.int64)
+        np.testing.assert_array_equal(_run(lib, p, rows=rows), base[rows])
+
+
+def pin_segments_stable_sort(lib):
+    rng = np.random.default_rng(4)
+    cases = [(0, 3), (1, 1), (7, 2), (64, 5), (1000, 37), (3000, 100)]
+    for n, n_slots in cases:
+        ranks = rng.integers(0, 3, size=n_slots).astype(np.int32) * 8
+        ranks[0] = 16
+        ids = rng.integers(-3, n_slots + 3, size=n).astype(np.int32)
+        seg = oracle.build_segments(ids, n_slots, ranks, lib=lib)
+        ok = _valid(ids, ranks)
+        key = np.where(ok, ids, n_slots)
+        np.testing.assert_array_equal(seg["perm"], np.argsort(key, kind="stable"))
+        cnt = np.bincount(ids[ok], minlength=n_slots)
+        np.testing.assert_array_equal(seg["seg_off"], np.concatenate([[0], np.cumsum(cnt)]))
+        act = np.nonzero(cnt)[0]
+        np.testing.assert_array_equal(seg["active"][:len(act)], act)
+        assert np.all(seg["active"][len(act):] == -1)
+        n_bad = int(np.sum(~ok & (ids != -1)))
+        np.testing.assert_array_equal(seg["counts"], [int(ok.sum()), len(act), n_bad])
+
+
+def pin_param_count(lib):
+    g = json.load(open(os.path.join(GOLDEN, "param_count.json")))
+    got = oracle.param_count(g["rank"], g["k"], [g["d"]], lib=lib)
+    assert got == g["adapter_params"]
+    assert g["d"] * g["k"] == g["full_params"]
+    assert g["full_params"] // got == g["ratio"] and g["full_params"] % got == 0
+    assert abs(got - g["printed_adapter_params_approx"]) / got < 0.01
+    # multi-slice: every slice carries its own pair of factors
+    assert oracle.param_count(16, 4096, [4096, 1024, 1024], lib=lib) == 16 * (3 * 4096 + 6144)
+    # the cost grows linearly in the rank (rank 128 costs 8x rank 16)
+    assert oracle.param_count(128, 4096, [4096], lib=lib) == 8 * got
+
+
+PINS = [pin_golden_worked, pin_dense_delta, pin_merged_weight, pin_rank1_closed_form,
+        pin_invariants, pin_segments_stable_sort, pin_param_count]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[f.__name__ for f in PINS])
+def test_pin(pin):
+    pin(oracle.load())
+
+
+# Plausible mistakes, planted in a copy of the oracle source (never in the real one).
+MUTATIONS = [
+    ("dropped_term", "acc += a * xv;", "acc += (t == 0) ? 0.0 : a * xv;"),
+    ("wrong_sign", "out[off + o] += scale * acc;", "out[off + o] -= scale * acc;"),
+    ("transposed_B", "B_off[s] + (off + o) * r + j", "B_off[s] + (int64_t)j * D + (off + o)"),
+    ("A_rank_slice_swapped", "((int64_t)q * r + j) * k + t", "((int64_t)j * n_slices + q) * k + t"),
+    ("scale_uses_pool_rank", "double scale = slot_alpha[s] / (double)r;",
+     "double scale = slot_alpha[s] / (double)max_rank;"),
+    ("slice_offset_dropped", "off += slice_d[q];", "off += 0;"),
+    ("ignores_ldx", "i * ldx + t", "i * k + t"),
+    ("ignores_ldy", "i * ldy + c", "i * D + c"),
+    ("unstable_group_order", "perm[seg_off[s] + fill[s]] = (int32_t)i;",
+     "perm[seg_off[s + 1] - 1 - fill[s]] = (int32_t)i;"),
+    ("empty_slot_routed", "return id >= 0 && id < n_slots && slot_rank[id] > 0;",
+     "return id >= 0 && id < n_slots;"),
+    ("none_counted_bad", "else if (ids[i] != -1)", "else"),
+    ("param_count_one_slice", "total += (int64_t)rank * k + slice_d[q] * (int64_t)rank;",
+     "total += (q == 0 ? (int64_t)rank * k : 0) + slice_d[q] * (int64_t)rank;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new, tmp_path):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "lora_oracle.c")).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mutated = tmp_path / f"oracle_{name}.c"
+    mutated.write_text(src.replace(old, new))
+    so = oracle.build(out_path=str(tmp_path / f"liboracle_{name}.so"), src=str(mutated))
+    lib = oracle.load(so)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
