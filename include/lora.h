@@ -1,0 +1,251 @@
+/*
+ * lora.h -- C ABI of the MI355X (gfx950) multi-adapter LoRA library.
+ *
+ * One batch, many adapters.  For every row i of a batch whose base output
+ * y_i = W x_i is already computed, the library adds the row's adapter delta
+ *
+ *      y_i += (alpha_s / r_s) * B_s (A_s x_i),     s = ids[i],
+ *
+ * and leaves rows with no adapter (id -1) untouched.  The delta is computed in
+ * two steps, add_shrink (v = A x, rank r) then add_expand (y += scale * B v),
+ * with the rows grouped by adapter so that one kernel serves the whole
+ * heterogeneous batch.  Sources: page "Multi-LoRA Serving: one base, many
+ * adapters", section 2 (per-row equation; flowchart: group rows by adapter id,
+ * shared base GEMM, add_shrink, add_expand, per-row merge) and section 3.1
+ * (LoRA math: B is d x r, A is r x k, Delta W = B A never formed); page "LoRA
+ * serving: multi-adapter dynamic loading", section 2 (all adapters' A and B
+ * stacked into one tensor, one integer id per request as the indirection, one
+ * batched kernel for the whole batch).
+ *
+ * Conventions shared by every call:
+ *   - Every call returns a lora_status; nothing aborts the process and no C++
+ *     exception crosses this boundary.  Host-checkable errors are returned
+ *     before anything is enqueued on the stream.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the default stream).
+ *     GPU work is asynchronous and stream-ordered: load -> apply -> evict on
+ *     one stream is safe without host synchronisation.
+ *   - Tensor pointers are device pointers unless an argument says otherwise.
+ *     Rows of x and y are dense along their width; row i starts at element
+ *     i * ldx (x) or i * ldy (y).
+ *   - Element types: LORA_F32 = IEEE float, LORA_BF16 = bfloat16 (the upper
+ *     half of an IEEE float).  x, y and the adapter weights of one stack share
+ *     the stack's dtype.  Arithmetic is fp32; each output element is rounded
+ *     once (round-to-nearest-even) from fp32(y_in) + scale * fp32(B v).
+ *   - Alignment: k, every slice width, ldx and ldy must be multiples of 8, and
+ *     x, y and weight sources 16-byte aligned.
+ *   - A stack or segments object must not be used from two host threads at
+ *     once, and calls that share one on different streams must be ordered by
+ *     the caller (they share device scratch).
+ */
+#ifndef RANK_ADAPTER_GEMM_LORA_AMD_LORA_H
+#define RANK_ADAPTER_GEMM_LORA_AMD_LORA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lora_stack lora_stack;       /* owns the adapter pool in HBM   */
+typedef struct lora_segments lora_segments; /* owns one batch's grouping      */
+
+typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+typedef enum lora_status {
+    LORA_OK = 0,
+    LORA_E_ARG = 1,       /* null pointer, bad size, misalignment, mismatch  */
+    LORA_E_RANK = 2,      /* rank < 1 or rank > r_max                        */
+    LORA_E_SLOT = 3,      /* slot index outside [0, n_slots)                 */
+    LORA_E_OCCUPIED = 4,  /* load into a slot that holds an adapter          */
+    LORA_E_EMPTY = 5,     /* evict of a slot that holds none                 */
+    LORA_E_NOMEM = 6,     /* device allocation failed                        */
+    LORA_E_HIP = 7,       /* a HIP runtime call failed                       */
+    LORA_E_BAD_IDS = 8,   /* (reported by lora_get_device_status)            */
+    LORA_E_UNSUPPORTED = 9 /* shape or option outside this build's limits    */
+} lora_status;
+
+/* Path of the row tiles of one segment (see lora_segments_set_dense_min). */
+typedef enum lora_path { LORA_PATH_BGMV = 0, LORA_PATH_SGMV = 1 } lora_path;
+
+/* Limits of this build. */
+#define LORA_MAX_SLOTS 1024
+#define LORA_MAX_RANK 128
+#define LORA_MAX_SLICES 8
+
+/* ------------------------------------------------------------------ stacks */
+
+/*
+ * Create a stack: the adapter pool of one layer projection group.
+ *
+ * The pool holds n_slots adapters of rank up to r_max; logically
+ * A_all[n_slots][n_slices][r_max][k] and B_all[n_slots][D][r_max] with
+ * D = sum(slice_d) (the slot count plays the part of the per-batch adapter cap
+ * and r_max that of the maximum LoRA rank that sizes the slots: page
+ * "Multi-LoRA Serving: one base, many adapters", section 3.2).  n_slices > 1
+ * fuses several projections that read the same x (q/k/v, gate/up): slice q
+ * writes columns [off_q, off_q + slice_d[q]) of y, each slice with its own A_q
+ * and B_q, all sharing the row's adapter id and scale.  max_rows bounds
+ * n_rows of every lora_apply on this stack (it sizes the stack's fp32 scratch
+ * for v).  The physical layout of the pool is private.
+ *
+ *   out       receives the new stack (set to NULL on failure)
+ *   dtype     element type of weights, x and y
+ *   n_slots   1 .. LORA_MAX_SLOTS;  r_max 1 .. LORA_MAX_RANK
+ *   k         input width (multiple of 8)
+ *   n_slices  1 .. LORA_MAX_SLICES; slice_d: HOST array [n_slices] of widths
+ *             (each a multiple of 8)
+ *   max_rows  >= 1
+ *
+ * The pool and slot table start empty (every slot rank 0).  Allocates device
+ * memory on the current HIP device; all later calls must run with that device
+ * current.  Errors: LORA_E_ARG, LORA_E_UNSUPPORTED, LORA_E_NOMEM, LORA_E_HIP.
+ */
+lora_status lora_stack_create(lora_stack **out, lora_dtype dtype, int n_slots, int r_max,
+                              int64_t k, int n_slices, const int64_t *slice_d,
+                              int64_t max_rows);
+
+/* Free a stack (NULL is accepted).  Synchronises the device first so no
+ * enqueued kernel still reads the pool. */
+lora_status lora_stack_destroy(lora_stack *st);
+
+/*
+ * Load one adapter into an empty slot (page "LoRA hot-loading and adapter
+ * routing", adapter-lifecycle section: validate the rank against the cap, copy
+ * A and B to GPU memory, register; page "Multi-LoRA Serving", section 6: an
+ * adapter above the rank cap is refused at load).
+ *
+ *   A      [n_slices][rank][k]  dense, true rank
+ *   B      [D][rank]            dense, true rank, slices stacked along D
+ *   alpha  the adapter's scaling numerator: scale = alpha / rank (true rank)
+ *   src_is_host  nonzero: A and B are host pointers; the call returns after
+ *                they have been consumed (it synchronises the stream).
+ *                zero: device pointers; the copy is stream-ordered and the
+ *                caller keeps them alive until the stream passes it.
+ *
+ * Errors: LORA_E_SLOT, LORA_E_RANK, LORA_E_OCCUPIED (evict first), LORA_E_ARG,
+ * LORA_E_HIP.
+ */
+lora_status lora_load_slot(lora_stack *st, int slot, int rank, float alpha, const void *A,
+                           const void *B, int src_is_host, void *stream);
+
+/* Mark a slot empty, in stream order (page "LoRA hot-loading and adapter
+ * routing", adapter-lifecycle section: unloading).  Rows that still name the
+ * slot in a later lora_build_segments count as bad ids.  Errors: LORA_E_SLOT,
+ * LORA_E_EMPTY. */
+lora_status lora_evict_slot(lora_stack *st, int slot, void *stream);
+
+/*
+ * Host view of one slot: rank (0 = empty), alpha, and the number of adapter
+ * parameters it holds, rank * (n_slices * k + D) -- the r(d + k) count of page
+ * "Multi-LoRA Serving", section 3.1, summed over slices.  Any output pointer
+ * may be NULL.  Errors: LORA_E_ARG, LORA_E_SLOT.
+ */
+lora_status lora_slot_info(const lora_stack *st, int slot, int *rank, float *alpha,
+                           int64_t *live_params);
+
+/* ---------------------------------------------------------------- segments */
+
+/*
+ * Create a segments object able to group up to max_rows rows over up to
+ * n_slots slots (device arrays: perm, seg_off, active, counts, tile plan).
+ * Errors: LORA_E_ARG, LORA_E_UNSUPPORTED, LORA_E_NOMEM.
+ */
+lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_slots);
+
+/* Free a segments object (NULL is accepted); synchronises the device first. */
+lora_status lora_segments_destroy(lora_segments *seg);
+
+/*
+ * Tile policy of later lora_build_segments calls: a slot whose group has at
+ * least m_min rows is served by the SGMV path (dense 64-row MFMA tiles), a
+ * smaller group by the BGMV path (16-row tiles, wavefront-reduction dot
+ * products).  m_min = 1 sends every group to SGMV; m_min > max_rows sends
+ * every group to BGMV.  Default 16.  fp32 stacks always take BGMV.
+ * Errors: LORA_E_ARG (m_min < 1).
+ */
+lora_status lora_segments_set_dense_min(lora_segments *seg, int m_min);
+
+/*
+ * Group the rows of one batch by adapter slot, on the device (page "LoRA
+ * hot-loading and adapter routing", batched multi-adapter execution section:
+ * one group of row indices per adapter id; page "Multi-LoRA Serving",
+ * section 2 flowchart: group rows by adapter id).
+ *
+ *   ids     DEVICE int32 [n_rows]; -1 = no adapter.  A row is valid when
+ *           0 <= ids[i] < n_slots and the slot holds an adapter at this
+ *           point of the stream; any other id except -1 is a bad id: counted,
+ *           and the row is left untouched like a none row.
+ *   n_rows  0 .. max_rows of seg
+ *
+ * Result (device, bit-exact and unique): perm = row indices grouped by slot in
+ * ascending slot order, ascending row index inside a group, then the rows
+ * without a valid adapter in ascending index order; seg_off[s] = first
+ * position of slot s in perm, seg_off[n_slots] = number of valid rows; active
+ * = slots with at least one row, ascending; counts = {valid rows, active
+ * slots, bad ids}.  The launch does not depend on the ids' values.  The
+ * segments remain bound to this stack's slot count and n_rows.
+ * Errors: LORA_E_ARG, LORA_E_HIP.
+ */
+lora_status lora_build_segments(const lora_stack *st, const int32_t *ids, int64_t n_rows,
+                                lora_segments *seg, void *stream);
+
+/* ------------------------------------------------------------------- apply */
+
+/*
+ * add_shrink: v = A_s x_i for every valid row, every slice, in fp32, into the
+ * stack's scratch (page "Multi-LoRA Serving", section 2 flowchart and section
+ * 3.4: add_shrink, rank-r, grouped per adapter).  x: [n_rows][ldx].
+ * Errors: LORA_E_ARG, LORA_E_HIP.
+ */
+lora_status lora_add_shrink(const lora_stack *st, const void *x, int64_t ldx,
+                            const lora_segments *seg, void *stream);
+
+/*
+ * add_expand with the per-row merge: y_i[off_q + o] = round(y_i + scale_s *
+ * (B_s v_i)[off_q + o]) for every valid row, using the v of the preceding
+ * lora_add_shrink on this stack (same page, same sections: add_expand, delta
+ * = B v * alpha / r, then the per-row merge y_i = base_i + delta_i).  Rows
+ * without a valid adapter and columns >= D are never written.
+ * y: [n_rows][ldy], updated in place.  Errors: LORA_E_ARG, LORA_E_HIP.
+ */
+lora_status lora_add_expand(const lora_stack *st, void *y, int64_t ldy,
+                            const lora_segments *seg, void *stream);
+
+/*
+ * lora_add_shrink followed by lora_add_expand: y_i += (alpha/r) B (A x_i) for
+ * every valid row of the batch grouped by seg.  The launch grid depends only on
+ * (n_rows, k, slice widths), never on the adapter mix, so the call can be
+ * captured in a HIP graph and replayed for any mix.  Errors: LORA_E_ARG,
+ * LORA_E_HIP.
+ */
+lora_status lora_apply(const lora_stack *st, void *y, int64_t ldy, const void *x, int64_t ldx,
+                       const lora_segments *seg, void *stream);
+
+/* --------------------------------------------------------------- inspection */
+
+/*
+ * Copy the grouping to HOST arrays and synchronise the stream.  perm
+ * [n_rows], seg_off [n_slots + 1], active [n_slots] (entries past counts[1]
+ * are -1), counts [3] = {valid rows, active slots, bad ids}.  Any output
+ * pointer may be NULL.  Errors: LORA_E_ARG, LORA_E_HIP.
+ */
+lora_status lora_segments_download(const lora_segments *seg, int32_t *perm, int32_t *seg_off,
+                                   int32_t *active, int32_t *counts, void *stream);
+
+/* Number of bad ids seen by the last lora_build_segments (synchronises the
+ * stream).  Returns LORA_E_BAD_IDS when it is nonzero, LORA_OK otherwise. */
+lora_status lora_get_device_status(const lora_segments *seg, int64_t *n_bad, void *stream);
+
+/* Number of row tiles the last lora_build_segments gave each path (host
+ * copy; synchronises the stream).  Either pointer may be NULL. */
+lora_status lora_segments_tile_counts(const lora_segments *seg, int32_t *n_bgmv,
+                                      int32_t *n_sgmv, void *stream);
+
+/* Static description of a status code. */
+const char *lora_status_string(lora_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RANK_ADAPTER_GEMM_LORA_AMD_LORA_H */

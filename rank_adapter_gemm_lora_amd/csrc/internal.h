@@ -1,0 +1,122 @@
+// internal.h -- host-side structures of the library and the launchers of its
+// kernels.  Not part of the public ABI (that is include/lora.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "lora.h"
+
+namespace lora {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };   // element types of x, y and the pool
+
+constexpr int kBgmvTileRows = 16;   // rows per BGMV tile (decode groups)
+constexpr int kSgmvTileRows = 64;   // rows per SGMV tile (dense groups, MFMA)
+constexpr int kTileBgmv = 0;
+constexpr int kTileSgmv = 1;
+constexpr int kExpandCols = 512;    // output columns per expand workgroup
+constexpr int kMaxKSplit = 16;      // most k-splits of one shrink
+constexpr int kMaxSliceRank = 256;  // n_slices * r_max bound (LDS staging of v)
+
+// Device counts written by the segment builder.
+enum : int {
+    kCntValid = 0,    // rows with a valid adapter (= seg_off[n_slots])
+    kCntActive = 1,   // slots with at least one row
+    kCntBad = 2,      // ids that are neither -1 nor a loaded slot
+    kCntSgmv = 3,     // SGMV tiles (stored first in the tile list)
+    kCntBgmv = 4,     // BGMV tiles (stored after the SGMV tiles)
+    kCntSlots = 8
+};
+
+struct SegBuildArgs {
+    const int32_t *ids;
+    int64_t n;
+    int n_slots;
+    const int32_t *slot_rank;
+    int dense_min;     // groups with >= dense_min rows go to SGMV
+    int sgmv_ok;       // 0: every group goes to BGMV
+    int32_t *perm;
+    int32_t *seg_off;
+    int32_t *active;
+    int32_t *counts;
+    int4 *tiles;       // {slot, first perm position, rows, path}
+};
+
+// Everything a shrink or expand kernel reads about the stack and the batch.
+struct ApplyArgs {
+    // stack
+    const void *A;             // pool [n_slots][n_slices][r_max][k]
+    const void *B;             // pool, slot s: [D][rp_s] at s * b_slot_stride
+    const int32_t *rank;       // [n_slots]
+    const float *scale;        // [n_slots] alpha / rank
+    int64_t k;
+    int n_slices;
+    int r_max;
+    int64_t D;
+    int64_t slice_off[LORA_MAX_SLICES + 1];
+    int64_t a_slot_stride;     // elements
+    int64_t b_slot_stride;     // elements
+    float *vws;                // [ks][max_rows][n_slices * r_max] fp32
+    int64_t max_rows;
+    int ks;                    // k-splits of the shrink
+    int mfma_ok;               // dense tiles may use MFMA (bf16, 64-aligned slices)
+    // batch
+    const int32_t *perm;
+    const int32_t *counts;
+    const int4 *tiles;
+    const void *x;
+    int64_t ldx;
+    void *y;
+    int64_t ldy;
+};
+
+hipError_t launch_seg_build(const SegBuildArgs &a, hipStream_t stream);
+hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream);
+hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
+hipError_t launch_set_slot(int32_t *rank, float *scale, int slot, int r, float s,
+                           hipStream_t stream);
+
+}  // namespace lora
+
+struct lora_stack {
+    int device;
+    lora_dtype dtype;
+    int esize;
+    int n_slots;
+    int r_max;
+    int rp_max;               // r_max rounded up to 8
+    int64_t k;
+    int n_slices;
+    int64_t slice_d[LORA_MAX_SLICES];
+    int64_t slice_off[LORA_MAX_SLICES + 1];
+    int64_t D;
+    int64_t max_rows;
+    void *A_pool;
+    void *B_pool;
+    int32_t *d_rank;
+    float *d_scale;
+    float *vws;
+    std::vector<int> h_rank;
+    std::vector<float> h_alpha;
+};
+
+struct lora_segments {
+    int device;
+    int64_t max_rows;
+    int n_slots_cap;
+    int max_tiles;
+    int dense_min;
+    int32_t *perm;
+    int32_t *seg_off;
+    int32_t *active;
+    int32_t *counts;
+    int4 *tiles;
+    // state of the last build
+    int built;
+    int64_t n_rows;
+    int n_slots;
+};

@@ -1,0 +1,498 @@
+// lora_api.cpp -- host runtime behind include/lora.h: argument checks, the
+// adapter pool and slot table, the segments object, and the kernel launches.
+// Every entry point returns a status; no exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+using namespace lora;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+lora_status from_hip(hipError_t e)
+{
+    if (e == hipSuccess)
+        return LORA_OK;
+    (void)hipGetLastError();   // clear the sticky error of this thread
+    return e == hipErrorOutOfMemory ? LORA_E_NOMEM : LORA_E_HIP;
+}
+
+#define LORA_TRY(expr)                              \
+    do {                                            \
+        const lora_status st_ = from_hip(expr);     \
+        if (st_ != LORA_OK)                         \
+            return st_;                             \
+    } while (0)
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// k-splits of the shrink: about 512 k per split, at most kMaxKSplit.  Depends
+// only on the shape, so add_shrink and add_expand agree without talking.
+int choose_ks(int64_t k, int64_t n_rows)
+{
+    (void)n_rows;
+    int64_t ks = (k + 511) / 512;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(ks, kMaxKSplit));
+}
+
+// Tiles of one batch never exceed ceil(rows / 16) plus one ragged tile per
+// group.
+int max_tiles_for(int64_t n_rows, int n_slots)
+{
+    return (int)((n_rows + kBgmvTileRows - 1) / kBgmvTileRows +
+                 std::min<int64_t>(n_slots, n_rows));
+}
+
+bool current_device_is(int dev)
+{
+    int cur = -1;
+    return hipGetDevice(&cur) == hipSuccess && cur == dev;
+}
+
+void free_stack(lora_stack *st)
+{
+    if (!st)
+        return;
+    (void)hipFree(st->A_pool);
+    (void)hipFree(st->B_pool);
+    (void)hipFree(st->d_rank);
+    (void)hipFree(st->d_scale);
+    (void)hipFree(st->vws);
+    delete st;
+}
+
+void free_segments(lora_segments *seg)
+{
+    if (!seg)
+        return;
+    (void)hipFree(seg->perm);
+    (void)hipFree(seg->seg_off);
+    (void)hipFree(seg->active);
+    (void)hipFree(seg->counts);
+    (void)hipFree(seg->tiles);
+    delete seg;
+}
+
+// MFMA tiles need bf16 and slices made of whole 64-column blocks; otherwise
+// the dense tiles of a batch are served by the vector code.
+bool stack_has_mfma_path(const lora_stack *st)
+{
+    if (st->dtype != LORA_BF16)
+        return false;
+    for (int q = 0; q < st->n_slices; ++q)
+        if (st->slice_d[q] % 64 != 0)
+            return false;
+    return true;
+}
+
+lora_status check_apply_common(const lora_stack *st, const lora_segments *seg)
+{
+    if (!st || !seg || !seg->built)
+        return LORA_E_ARG;
+    if (seg->n_slots != st->n_slots || seg->n_rows > st->max_rows)
+        return LORA_E_ARG;
+    if (!current_device_is(st->device) || seg->device != st->device)
+        return LORA_E_ARG;
+    return LORA_OK;
+}
+
+ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
+{
+    ApplyArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.A = st->A_pool;
+    a.B = st->B_pool;
+    a.rank = st->d_rank;
+    a.scale = st->d_scale;
+    a.k = st->k;
+    a.n_slices = st->n_slices;
+    a.r_max = st->r_max;
+    a.D = st->D;
+    for (int q = 0; q <= st->n_slices; ++q)
+        a.slice_off[q] = st->slice_off[q];
+    a.a_slot_stride = (int64_t)st->n_slices * st->r_max * st->k;
+    a.b_slot_stride = st->D * st->rp_max;
+    a.vws = st->vws;
+    a.max_rows = st->max_rows;
+    a.ks = choose_ks(st->k, seg->n_rows);
+    a.mfma_ok = stack_has_mfma_path(st) ? 1 : 0;
+    a.perm = seg->perm;
+    a.counts = seg->counts;
+    a.tiles = seg->tiles;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lora_status_string(lora_status s)
+{
+    switch (s) {
+    case LORA_OK: return "ok";
+    case LORA_E_ARG: return "invalid argument";
+    case LORA_E_RANK: return "rank outside [1, r_max]";
+    case LORA_E_SLOT: return "slot outside [0, n_slots)";
+    case LORA_E_OCCUPIED: return "slot already holds an adapter";
+    case LORA_E_EMPTY: return "slot holds no adapter";
+    case LORA_E_NOMEM: return "device allocation failed";
+    case LORA_E_HIP: return "HIP runtime error";
+    case LORA_E_BAD_IDS: return "batch contained ids naming no loaded slot";
+    case LORA_E_UNSUPPORTED: return "shape outside the limits of this build";
+    }
+    return "unknown status";
+}
+
+lora_status lora_stack_create(lora_stack **out, lora_dtype dtype, int n_slots, int r_max, int64_t k,
+                              int n_slices, const int64_t *slice_d, int64_t max_rows)
+{
+    if (!out)
+        return LORA_E_ARG;
+    *out = nullptr;
+    if ((dtype != LORA_F32 && dtype != LORA_BF16) || !slice_d || n_slots < 1 || r_max < 1 ||
+        k < 8 || k % 8 != 0 || n_slices < 1 || max_rows < 1)
+        return LORA_E_ARG;
+    if (n_slots > LORA_MAX_SLOTS || r_max > LORA_MAX_RANK || n_slices > LORA_MAX_SLICES ||
+        n_slices * r_max > kMaxSliceRank || max_rows > (int64_t)INT32_MAX / 2)
+        return LORA_E_UNSUPPORTED;
+    int64_t D = 0;
+    for (int q = 0; q < n_slices; ++q) {
+        if (slice_d[q] < 8 || slice_d[q] % 8 != 0)
+            return LORA_E_ARG;
+        D += slice_d[q];
+    }
+
+    lora_stack *st = new (std::nothrow) lora_stack();
+    if (!st)
+        return LORA_E_NOMEM;
+    st->A_pool = st->B_pool = nullptr;
+    st->d_rank = nullptr;
+    st->d_scale = nullptr;
+    st->vws = nullptr;
+    if (hipGetDevice(&st->device) != hipSuccess) {
+        delete st;
+        return LORA_E_HIP;
+    }
+    st->dtype = dtype;
+    st->esize = dtype == LORA_F32 ? 4 : 2;
+    st->n_slots = n_slots;
+    st->r_max = r_max;
+    st->rp_max = (int)round_up(r_max, 8);
+    st->k = k;
+    st->n_slices = n_slices;
+    st->slice_off[0] = 0;
+    for (int q = 0; q < n_slices; ++q) {
+        st->slice_d[q] = slice_d[q];
+        st->slice_off[q + 1] = st->slice_off[q] + slice_d[q];
+    }
+    st->D = D;
+    st->max_rows = max_rows;
+    st->h_rank.assign(n_slots, 0);
+    st->h_alpha.assign(n_slots, 0.f);
+
+    const size_t a_bytes = (size_t)n_slots * n_slices * r_max * k * st->esize;
+    const size_t b_bytes = (size_t)n_slots * D * st->rp_max * st->esize;
+    const size_t v_bytes = (size_t)kMaxKSplit * max_rows * n_slices * r_max * sizeof(float);
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = hipMalloc(&st->A_pool, a_bytes);
+    if (e == hipSuccess) e = hipMalloc(&st->B_pool, b_bytes);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->d_rank), sizeof(int32_t) * n_slots);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->d_scale), sizeof(float) * n_slots);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->vws), v_bytes);
+    if (e == hipSuccess) e = hipMemset(st->A_pool, 0, a_bytes);
+    if (e == hipSuccess) e = hipMemset(st->B_pool, 0, b_bytes);
+    if (e == hipSuccess) e = hipMemset(st->d_rank, 0, sizeof(int32_t) * n_slots);
+    if (e == hipSuccess) e = hipMemset(st->d_scale, 0, sizeof(float) * n_slots);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        free_stack(st);
+        return from_hip(e);
+    }
+    *out = st;
+    return LORA_OK;
+}
+
+lora_status lora_stack_destroy(lora_stack *st)
+{
+    if (!st)
+        return LORA_OK;
+    const hipError_t e = hipDeviceSynchronize();
+    free_stack(st);
+    return from_hip(e);
+}
+
+lora_status lora_load_slot(lora_stack *st, int slot, int rank, float alpha, const void *A,
+                           const void *B, int src_is_host, void *stream)
+{
+    if (!st)
+        return LORA_E_ARG;
+    if (slot < 0 || slot >= st->n_slots)
+        return LORA_E_SLOT;
+    if (rank < 1 || rank > st->r_max)
+        return LORA_E_RANK;
+    if (st->h_rank[slot] != 0)
+        return LORA_E_OCCUPIED;
+    if (!A || !B || !std::isfinite(alpha) || !current_device_is(st->device))
+        return LORA_E_ARG;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const hipMemcpyKind kind = src_is_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
+    const size_t es = st->esize;
+    char *a_dst = static_cast<char *>(st->A_pool) +
+                  (size_t)slot * st->n_slices * st->r_max * st->k * es;
+    char *b_dst = static_cast<char *>(st->B_pool) + (size_t)slot * st->D * st->rp_max * es;
+    const int rp = (int)round_up(rank, 8);
+
+    LORA_TRY(launch_zero(a_dst, (size_t)st->n_slices * st->r_max * st->k * es, s));
+    LORA_TRY(launch_zero(b_dst, (size_t)st->D * st->rp_max * es, s));
+    // A: [n_slices][rank][k] -> [n_slices][r_max][k]
+    LORA_TRY(hipMemcpy2DAsync(a_dst, (size_t)st->r_max * st->k * es, A, (size_t)rank * st->k * es,
+                              (size_t)rank * st->k * es, st->n_slices, kind, s));
+    // B: [D][rank] -> [D][rp], rp = rank rounded up to 8 (rank-contiguous rows)
+    if (rp == rank)
+        LORA_TRY(hipMemcpyAsync(b_dst, B, (size_t)st->D * rank * es, kind, s));
+    else
+        LORA_TRY(hipMemcpy2DAsync(b_dst, (size_t)rp * es, B, (size_t)rank * es, (size_t)rank * es,
+                                  st->D, kind, s));
+    LORA_TRY(launch_set_slot(st->d_rank, st->d_scale, slot, rank, alpha / (float)rank, s));
+    if (src_is_host)
+        LORA_TRY(hipStreamSynchronize(s));
+    st->h_rank[slot] = rank;
+    st->h_alpha[slot] = alpha;
+    return LORA_OK;
+}
+
+lora_status lora_evict_slot(lora_stack *st, int slot, void *stream)
+{
+    if (!st)
+        return LORA_E_ARG;
+    if (slot < 0 || slot >= st->n_slots)
+        return LORA_E_SLOT;
+    if (st->h_rank[slot] == 0)
+        return LORA_E_EMPTY;
+    if (!current_device_is(st->device))
+        return LORA_E_ARG;
+    LORA_TRY(launch_set_slot(st->d_rank, st->d_scale, slot, 0, 0.f,
+                             reinterpret_cast<hipStream_t>(stream)));
+    st->h_rank[slot] = 0;
+    st->h_alpha[slot] = 0.f;
+    return LORA_OK;
+}
+
+lora_status lora_slot_info(const lora_stack *st, int slot, int *rank, float *alpha,
+                           int64_t *live_params)
+{
+    if (!st)
+        return LORA_E_ARG;
+    if (slot < 0 || slot >= st->n_slots)
+        return LORA_E_SLOT;
+    const int r = st->h_rank[slot];
+    if (rank)
+        *rank = r;
+    if (alpha)
+        *alpha = st->h_alpha[slot];
+    if (live_params)
+        *live_params = (int64_t)r * (st->n_slices * st->k + st->D);
+    return LORA_OK;
+}
+
+lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_slots)
+{
+    if (!out)
+        return LORA_E_ARG;
+    *out = nullptr;
+    if (max_rows < 1 || n_slots < 1)
+        return LORA_E_ARG;
+    if (n_slots > LORA_MAX_SLOTS || max_rows > (int64_t)INT32_MAX / 2)
+        return LORA_E_UNSUPPORTED;
+    lora_segments *seg = new (std::nothrow) lora_segments();
+    if (!seg)
+        return LORA_E_NOMEM;
+    seg->perm = seg->seg_off = seg->active = seg->counts = nullptr;
+    seg->tiles = nullptr;
+    if (hipGetDevice(&seg->device) != hipSuccess) {
+        delete seg;
+        return LORA_E_HIP;
+    }
+    seg->max_rows = max_rows;
+    seg->n_slots_cap = n_slots;
+    seg->max_tiles = max_tiles_for(max_rows, n_slots);
+    seg->dense_min = 16;
+    seg->built = 0;
+    seg->n_rows = 0;
+    seg->n_slots = 0;
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->perm), sizeof(int32_t) * max_rows);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->seg_off), sizeof(int32_t) * (n_slots + 1));
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->active), sizeof(int32_t) * n_slots);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->counts), sizeof(int32_t) * kCntSlots);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->tiles), sizeof(int4) * seg->max_tiles);
+    if (e == hipSuccess) e = hipMemset(seg->counts, 0, sizeof(int32_t) * kCntSlots);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        free_segments(seg);
+        return from_hip(e);
+    }
+    *out = seg;
+    return LORA_OK;
+}
+
+lora_status lora_segments_destroy(lora_segments *seg)
+{
+    if (!seg)
+        return LORA_OK;
+    const hipError_t e = hipDeviceSynchronize();
+    free_segments(seg);
+    return from_hip(e);
+}
+
+lora_status lora_segments_set_dense_min(lora_segments *seg, int m_min)
+{
+    if (!seg || m_min < 1)
+        return LORA_E_ARG;
+    seg->dense_min = m_min;
+    return LORA_OK;
+}
+
+lora_status lora_build_segments(const lora_stack *st, const int32_t *ids, int64_t n_rows,
+                                lora_segments *seg, void *stream)
+{
+    if (!st || !seg || n_rows < 0 || n_rows > seg->max_rows || st->n_slots > seg->n_slots_cap)
+        return LORA_E_ARG;
+    if ((n_rows > 0 && !ids) || (reinterpret_cast<uintptr_t>(ids) & 3u) != 0)
+        return LORA_E_ARG;
+    if (!current_device_is(st->device) || seg->device != st->device)
+        return LORA_E_ARG;
+    SegBuildArgs a;
+    a.ids = ids;
+    a.n = n_rows;
+    a.n_slots = st->n_slots;
+    a.slot_rank = st->d_rank;
+    a.dense_min = seg->dense_min;
+    a.sgmv_ok = 1;
+    a.perm = seg->perm;
+    a.seg_off = seg->seg_off;
+    a.active = seg->active;
+    a.counts = seg->counts;
+    a.tiles = seg->tiles;
+    LORA_TRY(launch_seg_build(a, reinterpret_cast<hipStream_t>(stream)));
+    seg->built = 1;
+    seg->n_rows = n_rows;
+    seg->n_slots = st->n_slots;
+    return LORA_OK;
+}
+
+lora_status lora_add_shrink(const lora_stack *st, const void *x, int64_t ldx,
+                            const lora_segments *seg, void *stream)
+{
+    const lora_status c = check_apply_common(st, seg);
+    if (c != LORA_OK)
+        return c;
+    if (seg->n_rows == 0)
+        return LORA_OK;
+    if (!x || !aligned16(x) || ldx < st->k || ldx % 8 != 0)
+        return LORA_E_ARG;
+    ApplyArgs a = make_args(st, seg);
+    a.x = x;
+    a.ldx = ldx;
+    LORA_TRY(launch_shrink(st->dtype == LORA_BF16 ? DT_BF16 : DT_F32, a,
+                           max_tiles_for(seg->n_rows, st->n_slots),
+                           reinterpret_cast<hipStream_t>(stream)));
+    return LORA_OK;
+}
+
+lora_status lora_add_expand(const lora_stack *st, void *y, int64_t ldy, const lora_segments *seg,
+                            void *stream)
+{
+    const lora_status c = check_apply_common(st, seg);
+    if (c != LORA_OK)
+        return c;
+    if (seg->n_rows == 0)
+        return LORA_OK;
+    if (!y || !aligned16(y) || ldy < st->D || ldy % 8 != 0)
+        return LORA_E_ARG;
+    ApplyArgs a = make_args(st, seg);
+    a.y = y;
+    a.ldy = ldy;
+    LORA_TRY(launch_expand(st->dtype == LORA_BF16 ? DT_BF16 : DT_F32, a,
+                           max_tiles_for(seg->n_rows, st->n_slots),
+                           reinterpret_cast<hipStream_t>(stream)));
+    return LORA_OK;
+}
+
+lora_status lora_apply(const lora_stack *st, void *y, int64_t ldy, const void *x, int64_t ldx,
+                       const lora_segments *seg, void *stream)
+{
+    const lora_status c = check_apply_common(st, seg);
+    if (c != LORA_OK)
+        return c;
+    if (seg->n_rows == 0)
+        return LORA_OK;
+    // validate both halves before enqueueing either
+    if (!x || !aligned16(x) || ldx < st->k || ldx % 8 != 0)
+        return LORA_E_ARG;
+    if (!y || !aligned16(y) || ldy < st->D || ldy % 8 != 0)
+        return LORA_E_ARG;
+    const lora_status s1 = lora_add_shrink(st, x, ldx, seg, stream);
+    if (s1 != LORA_OK)
+        return s1;
+    return lora_add_expand(st, y, ldy, seg, stream);
+}
+
+lora_status lora_segments_download(const lora_segments *seg, int32_t *perm, int32_t *seg_off,
+                                   int32_t *active, int32_t *counts, void *stream)
+{
+    if (!seg || !seg->built)
+        return LORA_E_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (perm && seg->n_rows > 0)
+        LORA_TRY(hipMemcpyAsync(perm, seg->perm, sizeof(int32_t) * seg->n_rows, hipMemcpyDeviceToHost, s));
+    if (seg_off)
+        LORA_TRY(hipMemcpyAsync(seg_off, seg->seg_off, sizeof(int32_t) * (seg->n_slots + 1),
+                                hipMemcpyDeviceToHost, s));
+    if (active)
+        LORA_TRY(hipMemcpyAsync(active, seg->active, sizeof(int32_t) * seg->n_slots,
+                                hipMemcpyDeviceToHost, s));
+    if (counts)
+        LORA_TRY(hipMemcpyAsync(counts, seg->counts, sizeof(int32_t) * 3, hipMemcpyDeviceToHost, s));
+    LORA_TRY(hipStreamSynchronize(s));
+    return LORA_OK;
+}
+
+lora_status lora_get_device_status(const lora_segments *seg, int64_t *n_bad, void *stream)
+{
+    if (!seg || !seg->built)
+        return LORA_E_ARG;
+    int32_t c[kCntSlots];
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    LORA_TRY(hipMemcpyAsync(c, seg->counts, sizeof c, hipMemcpyDeviceToHost, s));
+    LORA_TRY(hipStreamSynchronize(s));
+    if (n_bad)
+        *n_bad = c[kCntBad];
+    return c[kCntBad] > 0 ? LORA_E_BAD_IDS : LORA_OK;
+}
+
+lora_status lora_segments_tile_counts(const lora_segments *seg, int32_t *n_bgmv, int32_t *n_sgmv,
+                                      void *stream)
+{
+    if (!seg || !seg->built)
+        return LORA_E_ARG;
+    int32_t c[kCntSlots];
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    LORA_TRY(hipMemcpyAsync(c, seg->counts, sizeof c, hipMemcpyDeviceToHost, s));
+    LORA_TRY(hipStreamSynchronize(s));
+    if (n_bgmv)
+        *n_bgmv = c[kCntBgmv];
+    if (n_sgmv)
+        *n_sgmv = c[kCntSgmv];
+    return LORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+"""Helpers for the GPU tests: move a synthetic problem to the device, drive the
+HIP library through its C ABI, and compute oracle references."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import compare
+from rank_adapter_gemm_lora_amd import binding as lb
+
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def note(msg: str):
+    """Name the case on stdout before a GPU step, flushed."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _dev_raw(a: np.ndarray, device) -> torch.Tensor:
+    """A host array of float32 values or bf16 bits as a device tensor of the same bytes."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def _host_raw(t: torch.Tensor, dtype: str) -> np.ndarray:
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if dtype == "bf16" else a
+
+
+class GpuRun:
+    """One stack + one segments object holding problem ``p`` on the GPU."""
+
+    def __init__(self, p, device="cuda:0", max_rows=None, dense_min=None, load_from_device=False,
+                 stream=None):
+        self.p = p
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        dt = lb.LORA_BF16 if p.dtype == "bf16" else lb.LORA_F32
+        self.max_rows = max_rows or max(p.n_rows, 1)
+        self.stack = lb.lora_stack_create(dt, p.n_slots, p.r_max, p.k, p.slice_d, self.max_rows)
+        self.seg = lb.lora_segments_create(self.max_rows, p.n_slots)
+        if dense_min is not None:
+            lb.lora_segments_set_dense_min(self.seg, dense_min)
+        self._keep = []
+        for s in range(p.n_slots):
+            if p.ranks[s] > 0:
+                self.load(s, p.A[s], p.B[s], float(p.alphas[s]), from_device=load_from_device)
+        self.ids = torch.from_numpy(p.ids.copy()).to(self.device)
+        self.x = _dev_raw(p.x, self.device)
+        self.y = _dev_raw(p.y, self.device)
+
+    def load(self, slot, A, B, alpha, from_device=False):
+        rank = A.shape[1]
+        if from_device:
+            dA, dB = _dev_raw(A, self.device), _dev_raw(B, self.device)
+            self._keep += [dA, dB]
+            lb.lora_load_slot(self.stack, slot, rank, alpha, dA.data_ptr(), dB.data_ptr(),
+                              False, self.stream)
+        else:
+            A = np.ascontiguousarray(A)
+            B = np.ascontiguousarray(B)
+            lb.lora_load_slot(self.stack, slot, rank, alpha, A.ctypes.data, B.ctypes.data,
+                              True, self.stream)
+
+    def build(self, n_rows=None):
+        n = self.p.n_rows if n_rows is None else n_rows
+        lb.lora_build_segments(self.stack, self.ids.data_ptr(), n, self.seg, self.stream)
+
+    def apply(self):
+        lb.lora_apply(self.stack, self.y.data_ptr(), self.p.ldy, self.x.data_ptr(), self.p.ldx,
+                      self.seg, self.stream)
+
+    def segments(self):
+        return lb.lora_segments_download(self.seg, self.p.n_rows, self.p.n_slots, self.stream)
+
+    def y_host(self) -> np.ndarray:
+        torch.cuda.synchronize(self.device)
+        return _host_raw(self.y, self.p.dtype)
+
+    def close(self):
+        torch.cuda.synchronize(self.device)
+        lb.lora_segments_destroy(self.seg)
+        lb.lora_stack_destroy(self.stack)
+        self.seg = self.stack = None
+
+
+def oracle_rows(p, rows=None, ranks=None):
+    return oracle.apply_rows(p.dtype, p.k, p.slice_d, p.ranks if ranks is None else ranks,
+                             p.alphas, p.A, p.B, p.ids, p.x, p.y, rows=rows,
+                             n_threads=ORACLE_THREADS)
+
+
+def valid_mask(p, ranks=None):
+    ranks = p.ranks if ranks is None else ranks
+    return np.array([0 <= s < p.n_slots and ranks[s] > 0 for s in p.ids], bool)
+
+
+def check_against_oracle(p, y_out: np.ndarray, rows=None, ranks=None, what=""):
+    """Gate ``y_out`` (raw dtype, full [n, ldy]) against the oracle.
+
+    Rows without a valid adapter and columns >= D must be bit-identical to the
+    input; the valid rows' D columns must pass the float gate.  ``rows`` limits
+    the float check to a sample (the bitwise checks always cover every row).
+    Returns the float metrics.
+    """
+    ok = valid_mask(p, ranks)
+    # bitwise: untouched rows and padding columns
+    np.testing.assert_array_equal(y_out[~ok], p.y[~ok], err_msg=f"untouched rows changed {what}")
+    np.testing.assert_array_equal(y_out[:, p.D:], p.y[:, p.D:], err_msg=f"padding columns changed {what}")
+    sel = np.nonzero(ok)[0] if rows is None else np.asarray(rows, np.int64)
+    sel = sel[ok[sel]]
+    if sel.size == 0:
+        return compare.metrics(np.zeros(0), np.zeros(0), p.dtype)
+    ref = oracle_rows(p, rows=sel, ranks=ranks)
+    got = y_out[sel, :p.D]
+    return compare.check(got, ref, p.dtype, what)
+
+
+def sample_rows(p, n_sample: int, seed: int = 0):
+    """Sorted sample of valid rows, always including the first and last valid
+    row and every group's first and last row."""
+    ok = np.nonzero(valid_mask(p))[0]
+    if ok.size <= n_sample:
+        return ok
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(ok, size=n_sample, replace=False).tolist())
+    pick.update([int(ok[0]), int(ok[-1])])
+    for s in np.unique(p.ids[ok]):
+        rows_s = ok[p.ids[ok] == s]
+        pick.update([int(rows_s[0]), int(rows_s[-1])])
+    return np.array(sorted(pick), np.int64)
