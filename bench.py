@@ -1,0 +1,395 @@
+"""Benchmark of one multi-adapter LoRA layer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is the whole hot path over one batch: lora_build_segments (group rows
+by adapter), lora_add_shrink (v = A x) and lora_add_expand (y += scale B v).
+Inputs are resident in HBM before the timed region.  Steps rotate through
+independent buffer sets (stack + ids + x + y) totalling >= 512 MB so that the
+256 MB MALL cannot serve them: every step reads its weights and rows from HBM.
+
+One JSON line goes to stdout:
+  value      LoRA-applied tokens/s (valid rows per second over the timed steps)
+  roofline   the dominant kernel's algorithmic bytes per launch over its mean
+             launch duration (that kernel launched K times back to back on the
+             rotating sets, HIP events on the launch stream), against the
+             8 TB/s HBM peak; traffic = HBM bytes per launch from rocprofv3
+             FETCH_SIZE/WRITE_SIZE (scaled by a copy-kernel calibration) when a
+             committed measurement matches the current kernel sources, else null
+  cpu_baseline  the CPU oracle on the host cores on a bounded sample
+
+Other modes: --all (every workload, lines to --out), --copy-probe (plain copy
+kernel at the decode size and at 1 GB: the achievable HBM ceiling, also the
+calibration run for the PMC counters), --pmc-summary DIR (fold rocprofv3
+counter output into profiles/).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+ROTATE_BYTES = 512 << 20       # 2x the 256 MB MALL
+DEFAULT_WORKLOAD = "decode_bgmv"
+KERNELS = ("seg_build", "shrink", "expand")
+KERNEL_SOURCES = ("seg_build.hip", "apply.hip", "sgmv.h", "device_common.h", "internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_bgmv.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- accounting
+
+def accounting(p) -> dict:
+    """Algorithmic bytes and flops of one step (what the method must move):
+    each valid row's x read once, each valid row's y read and written once, the
+    live A and B of every slot the batch references read once at true rank."""
+    b = p.elem_bytes
+    ok = np.array([0 <= s < p.n_slots and p.ranks[s] > 0 for s in p.ids], bool)
+    n_valid = int(ok.sum())
+    slots = np.unique(p.ids[ok])
+    live_a = sum(int(p.ranks[s]) * p.n_slices * p.k for s in slots) * b
+    live_b = sum(int(p.ranks[s]) * p.D for s in slots) * b
+    x_bytes = n_valid * p.k * b
+    y_bytes = 2 * n_valid * p.D * b
+    flops = sum(2 * int(p.ranks[s]) * (p.n_slices * p.k + p.D) + p.D for s in p.ids[ok])
+    shrink_flops = sum(2 * int(p.ranks[s]) * p.n_slices * p.k for s in p.ids[ok])
+    return dict(n_valid=n_valid, distinct_slots=int(slots.size),
+                bytes=dict(shrink=x_bytes + live_a, expand=y_bytes + live_b,
+                           seg_build=8 * p.n_rows + 4 * (p.n_slots + 1),
+                           total=x_bytes + y_bytes + live_a + live_b),
+                flops=dict(total=int(flops), shrink=int(shrink_flops),
+                           expand=int(flops - shrink_flops)))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rank_adapter_gemm_lora_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sources") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t
+
+
+# ----------------------------------------------------------------- GPU side
+
+class BufferSet:
+    """One independent copy of the stack, ids, x and y of a workload."""
+
+    def __init__(self, p, lb, torch, dev, stream, dA, dB, dense_min):
+        dt = lb.LORA_BF16 if p.dtype == "bf16" else lb.LORA_F32
+        self.stack = lb.lora_stack_create(dt, p.n_slots, p.r_max, p.k, p.slice_d, p.n_rows)
+        self.seg = lb.lora_segments_create(p.n_rows, p.n_slots)
+        if dense_min is not None:
+            lb.lora_segments_set_dense_min(self.seg, dense_min)
+        for s in range(p.n_slots):
+            if p.ranks[s] > 0:
+                lb.lora_load_slot(self.stack, s, int(p.ranks[s]), float(p.alphas[s]),
+                                  dA[s].data_ptr(), dB[s].data_ptr(), False, stream)
+        raw = torch.int16 if p.dtype == "bf16" else torch.float32
+        self.ids = torch.from_numpy(p.ids).to(dev)
+        self.x = torch.from_numpy(p.x.view(np.int16) if p.dtype == "bf16" else p.x).to(dev)
+        self.y = torch.from_numpy(p.y.view(np.int16) if p.dtype == "bf16" else p.y).to(dev)
+        assert self.x.dtype == raw and self.y.dtype == raw
+
+    def close(self, lb):
+        lb.lora_segments_destroy(self.seg)
+        lb.lora_stack_destroy(self.stack)
+
+
+def set_bytes(p) -> int:
+    b = p.elem_bytes
+    rp = (p.r_max + 7) // 8 * 8
+    pool = p.n_slots * (p.n_slices * p.r_max * p.k + p.D * rp) * b
+    return pool + p.x.nbytes + p.y.nbytes + p.ids.nbytes
+
+
+def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None) -> dict:
+    import torch
+    from rank_adapter_gemm_lora_amd import binding as lb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)        # default priority
+    sh = stream.cuda_stream
+    raw = (lambda a: a.view(np.int16)) if p.dtype == "bf16" else (lambda a: a)
+    dA = [None if p.ranks[s] == 0 else torch.from_numpy(raw(np.ascontiguousarray(p.A[s]))).to(dev)
+          for s in range(p.n_slots)]
+    dB = [None if p.ranks[s] == 0 else torch.from_numpy(raw(np.ascontiguousarray(p.B[s]))).to(dev)
+          for s in range(p.n_slots)]
+    torch.cuda.synchronize()               # staged weights complete before other streams read them
+    n_sets = max(2, math.ceil(ROTATE_BYTES / set_bytes(p))) if rotate else 1
+    n_sets = min(n_sets, 4096)
+    with torch.cuda.stream(stream):
+        sets = [BufferSet(p, lb, torch, dev, sh, dA, dB, dense_min) for _ in range(n_sets)]
+    torch.cuda.synchronize()
+    del dA, dB
+
+    def build(bs):
+        lb.lora_build_segments(bs.stack, bs.ids.data_ptr(), p.n_rows, bs.seg, sh)
+
+    def shrink(bs):
+        lb.lora_add_shrink(bs.stack, bs.x.data_ptr(), p.ldx, bs.seg, sh)
+
+    def expand(bs):
+        lb.lora_add_expand(bs.stack, bs.y.data_ptr(), p.ldy, bs.seg, sh)
+
+    def step(bs):
+        build(bs)
+        shrink(bs)
+        expand(bs)
+
+    for i in range(warmup):
+        step(sets[i % n_sets])
+    torch.cuda.synchronize()
+
+    # the step: K passes of the whole path, one buffer set each, events only
+    # around the region
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(sets[(warmup + i) % n_sets])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(stop)
+
+    # each kernel alone: K back-to-back launches over the rotating sets (every
+    # set already holds its segments and v, so each launch does its full work);
+    # mean launch duration = region time / K, events only at the region's ends
+    per = {}
+    for name, fn in (("seg_build", build), ("shrink", shrink), ("expand", expand)):
+        for i in range(min(warmup, n_sets)):
+            fn(sets[i % n_sets])
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            fn(sets[i % n_sets])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per[name] = e0.elapsed_time(e1) * 1e3 / steps
+    n_bgmv, n_sgmv = lb.lora_segments_tile_counts(sets[0].seg, sh)
+    for bs in sets:
+        bs.close(lb)
+    torch.cuda.synchronize()
+    return dict(wall_s=wall, gpu_ms=gpu_ms, n_sets=n_sets, set_bytes=set_bytes(p),
+                kernel_us=per, tiles=dict(bgmv=n_bgmv, sgmv=n_sgmv))
+
+
+# ----------------------------------------------------------------- CPU oracle
+
+def run_cpu_baseline(p, acct, budget_s: float = 10.0) -> dict:
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    ranks = p.ranks
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.build_segments(p.ids, p.n_slots, ranks)
+        oracle.apply_rows(p.dtype, p.k, p.slice_d, ranks, p.alphas, p.A, p.B, p.ids, p.x, p.y,
+                          n_threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return dict(value=acct["n_valid"] * reps / el, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{reps} full passes of the {p.name} batch ({p.n_rows} rows, "
+                       f"{acct['n_valid']} with an adapter): segments + fp64 apply, "
+                       f"{el:.1f} s, OpenMP over rows")
+
+
+# ----------------------------------------------------------------- modes
+
+def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -> dict:
+    from rank_adapter_gemm_lora_amd import synth
+    p = synth.make_workload(name)
+    acct = accounting(p)
+    log(f"[bench] {name}: {p.note}; valid rows {acct['n_valid']}, "
+        f"algorithmic bytes {acct['bytes']['total'] / 1e6:.2f} MB/step")
+    g = run_gpu(p, steps, warmup, rotate=rotate, dense_min=dense_min)
+    ms = g["gpu_ms"] / steps
+    ku = g["kernel_us"]
+    dom = max(KERNELS, key=lambda k: ku[k])
+    achieved = acct["bytes"][dom] / (ku[dom] * 1e-6) / 1e9
+    traffic = committed_traffic(name)
+    roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                traffic=(traffic["per_launch_bytes"][dom] if traffic else None),
+                algorithmic_bytes_per_launch=acct["bytes"][dom],
+                mean_launch_us=round(ku[dom], 3))
+    line = {
+        "metric": "LoRA-applied tokens/s per layer + achieved HBM GB/s (% of MI355X peak)",
+        "value": round(acct["n_valid"] * steps / (g["gpu_ms"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": p.dtype, "data": "synthetic (seeded, HBM-cold rotation)" if rotate else
+        "synthetic (seeded, warm: cache-served, not HBM)",
+        "config": {"workload": name, "rows": p.n_rows, "valid_rows": acct["n_valid"],
+                   "k": p.k, "slices": p.slice_d, "slots": p.n_slots, "r_max": p.r_max,
+                   "ranks": sorted({int(r) for r in p.ranks if r > 0}),
+                   "distinct_slots": acct["distinct_slots"], "buffer_sets": g["n_sets"],
+                   "parallelism": "single GPU"},
+        "step_hbm_gbs": round(acct["bytes"]["total"] / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(acct["bytes"]["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_us": {k: round(v, 3) for k, v in ku.items()},
+        "kernel_gbs": {k: round(acct["bytes"][k] / (ku[k] * 1e-6) / 1e9, 1)
+                       for k in ("shrink", "expand")},
+        "mfma_util": {k: round(acct["flops"][k] / (ku[k] * 1e-6) / 1e12
+                               / MFMA_BF16_PEAK_TFLOPS, 5) for k in ("shrink", "expand")},
+        "tiles": g["tiles"],
+        "roofline": roof,
+        "host_wall_ms_per_step": round(g["wall_s"] * 1e3 / steps, 4),
+    }
+    if cpu:
+        line["cpu_baseline"] = run_cpu_baseline(p, acct)
+    return line
+
+
+def copy_probe(reps: int = 50) -> list:
+    """A plain device copy at the decode step's size and at 1 GB (rotated past
+    the MALL): the achievable HBM ceiling, and the calibration kernel for the
+    PMC byte counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = []
+    for nbytes in (7_690_000 // 256 * 256, 1 << 30):
+        n_buf = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        src = [torch.empty(nbytes // 2, dtype=torch.int16, device=dev).fill_(1) for _ in range(n_buf)]
+        dst = [torch.empty_like(s) for s in src]
+        for i in range(5):
+            dst[i % n_buf].copy_(src[i % n_buf])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            dst[i % n_buf].copy_(src[i % n_buf])
+        e1.record()
+        torch.cuda.synchronize()
+        us = np.array([e0.elapsed_time(e1) * 1e3 / reps])
+        out.append(dict(bytes_moved=2 * nbytes, mean_us=float(us.mean()),
+                        gbs=round(2 * nbytes / (us.mean() * 1e-6) / 1e9, 1)))
+        del src, dst
+        torch.cuda.empty_cache()
+    return out
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str) -> dict:
+    """Fold two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) into bytes per launch, scaled so that the calibration copy
+    kernel (torch's elementwise copy of ``copy_bytes`` bytes read + written)
+    reads its true size."""
+    import csv
+
+    def per_kernel(d, counter):
+        vals = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(vals, key):
+        ks = [k for k in vals if key in k]
+        return float(np.median(vals[ks[0]])) * 1024 if ks else None
+
+    copy_key = "elementwise_kernel"
+    cf, cw = pick(fetch, copy_key), pick(write, copy_key)
+    f_scale = (copy_bytes / 2) / cf if cf else 1.0
+    w_scale = (copy_bytes / 2) / cw if cw else 1.0
+    names = {"seg_build": "seg_build_kernel", "shrink": "shrink_kernel", "expand": "expand_kernel"}
+    per = {}
+    for k, key in names.items():
+        fb, wb = pick(fetch, key), pick(write, key)
+        per[k] = None if fb is None or wb is None else round(fb * f_scale + wb * w_scale)
+    return dict(workload=workload, kernel_sources=kernel_source_hash(), fetch_scale=f_scale,
+                write_scale=w_scale, per_launch_bytes=per)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--all", action="store_true", help="bench every workload")
+    ap.add_argument("--out", default=None, help="also append JSON lines to this file")
+    ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-served)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--dense-min", type=int, default=None, help="SGMV threshold (rows per group)")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--copy-bytes", type=int, default=2 * (7_690_000 // 256 * 256))
+    args = ap.parse_args(argv)
+
+    if args.pmc_summary:
+        res = pmc_summary(*args.pmc_summary, args.copy_bytes, args.workload)
+        print(json.dumps(res))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(rows shard with no exchange; see the design notes). --gpus {args.gpus} "
+              "is not supported.", file=sys.stderr)
+        return 2
+    if "RANK" in os.environ and os.environ.get("WORLD_SIZE", "1") != "1":
+        print("bench.py runs on one GPU only", file=sys.stderr)
+        return 2
+    if args.copy_probe:
+        res = copy_probe()
+        print(json.dumps({"copy_probe": res}))
+        return 0
+
+    names = ["tiny_ref", "decode_bgmv", "prefill_sgmv", "mlp_gate_up", "mlp_down",
+             "many_adapter"] if args.all else [args.workload]
+    for name in names:
+        line = bench_workload(name, args.steps, args.warmup, rotate=not args.warm,
+                              cpu=not args.no_cpu and (not args.all or name == DEFAULT_WORKLOAD),
+                              dense_min=args.dense_min)
+        s = json.dumps(line)
+        print(s, flush=True)
+        if args.out:
+            with open(args.out, "a") as f:
+                f.write(s + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -17,7 +17,7 @@
  *   already in y (section 2 flowchart: the shared base GEMM runs once, then
  *   add_shrink v = A x, add_expand delta = B v * alpha / r, merge per row).
  *   Rows without an adapter keep the base output (same section: row with
- *   lora_id = none; page "LoRA hot-loading and adapter routing", section on
+ *   no adapter id; page "LoRA hot-loading and adapter routing", section on
  *   adapter routing: a None id means no LoRA).
  *
  *   Grouping by adapter id.  Page "LoRA hot-loading and adapter routing",

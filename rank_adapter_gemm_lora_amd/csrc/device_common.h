@@ -30,6 +30,16 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// n / d for 0 <= n, 1 <= d with n * d < 2^24, as one 64-bit multiply and a
+// shift: m = floor(2^24 / d) + 1 overshoots 2^24 / d by at most 1, so
+// n * m / 2^24 exceeds n / d by less than n / 2^24 < 1 / d, which never
+// carries past the next integer.
+__device__ __forceinline__ uint32_t div_magic(uint32_t d) { return (1u << 24) / d + 1u; }
+__device__ __forceinline__ int div_small(int n, uint32_t m)
+{
+    return (int)(((uint64_t)(uint32_t)n * m) >> 24);
+}
+
 // Eight consecutive elements of a row, held in their storage format.
 template <int DT> struct Vec8;
 

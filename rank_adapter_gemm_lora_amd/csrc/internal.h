@@ -13,11 +13,12 @@ namespace lora {
 
 enum : int { DT_F32 = 0, DT_BF16 = 1 };   // element types of x, y and the pool
 
-constexpr int kBgmvTileRows = 16;   // rows per BGMV tile (decode groups)
-constexpr int kSgmvTileRows = 64;   // rows per SGMV tile (dense groups, MFMA)
+constexpr int kBgmvTileRows = 16;   // rows per BGMV shrink tile (small groups)
+constexpr int kSgmvTileRows = 64;   // rows per SGMV shrink tile (dense groups, MFMA)
+constexpr int kExpandCols = 256;    // output columns per expand workgroup
+constexpr int kExpandVsFloats = 8192;  // LDS floats of v staging in the expand
 constexpr int kTileBgmv = 0;
 constexpr int kTileSgmv = 1;
-constexpr int kExpandCols = 512;    // output columns per expand workgroup
 constexpr int kMaxKSplit = 16;      // most k-splits of one shrink
 constexpr int kMaxSliceRank = 256;  // n_slices * r_max bound (LDS staging of v)
 
@@ -26,9 +27,17 @@ enum : int {
     kCntValid = 0,    // rows with a valid adapter (= seg_off[n_slots])
     kCntActive = 1,   // slots with at least one row
     kCntBad = 2,      // ids that are neither -1 nor a loaded slot
-    kCntSgmv = 3,     // SGMV tiles (stored first in the tile list)
-    kCntBgmv = 4,     // BGMV tiles (stored after the SGMV tiles)
+    kCntSgmv = 3,     // SGMV shrink tiles (stored first in the tile list)
+    kCntBgmv = 4,     // BGMV shrink tiles (stored after the SGMV tiles)
     kCntSlots = 8
+};
+
+// One tile: up to 64 rows of one slot (SGMV) or up to 16 (BGMV), with the
+// rows' indices inline so one load brings the whole work description.  The
+// shrink and the expand walk the same list.
+struct alignas(16) ShrinkTile {
+    int32_t slot, p0, cnt, path;   // p0: first position of the tile in the grouping
+    int32_t rows[kSgmvTileRows];
 };
 
 struct SegBuildArgs {
@@ -36,13 +45,13 @@ struct SegBuildArgs {
     int64_t n;
     int n_slots;
     const int32_t *slot_rank;
-    int dense_min;     // groups with >= dense_min rows go to SGMV
-    int sgmv_ok;       // 0: every group goes to BGMV
+    int dense_min;     // groups with >= dense_min rows take the SGMV path
+    int sgmv_rows;     // rows per SGMV tile (16 for small batches, 64 for large)
     int32_t *perm;
     int32_t *seg_off;
     int32_t *active;
     int32_t *counts;
-    int4 *tiles;       // {slot, first perm position, rows, path}
+    lora::ShrinkTile *tiles;
 };
 
 // Everything a shrink or expand kernel reads about the stack and the batch.
@@ -59,14 +68,13 @@ struct ApplyArgs {
     int64_t slice_off[LORA_MAX_SLICES + 1];
     int64_t a_slot_stride;     // elements
     int64_t b_slot_stride;     // elements
-    float *vws;                // [ks][max_rows][n_slices * r_max] fp32
+    float *vpart;              // [ks][max_rows][n_slices * r_max] k-split partials of v
     int64_t max_rows;
     int ks;                    // k-splits of the shrink
     int mfma_ok;               // dense tiles may use MFMA (bf16, 64-aligned slices)
     // batch
-    const int32_t *perm;
     const int32_t *counts;
-    const int4 *tiles;
+    const ShrinkTile *tiles;
     const void *x;
     int64_t ldx;
     void *y;
@@ -99,7 +107,7 @@ struct lora_stack {
     void *B_pool;
     int32_t *d_rank;
     float *d_scale;
-    float *vws;
+    float *vpart;
     std::vector<int> h_rank;
     std::vector<float> h_alpha;
 };
@@ -114,7 +122,7 @@ struct lora_segments {
     int32_t *seg_off;
     int32_t *active;
     int32_t *counts;
-    int4 *tiles;
+    lora::ShrinkTile *tiles;
     // state of the last build
     int built;
     int64_t n_rows;

@@ -33,13 +33,21 @@ lora_status from_hip(hipError_t e)
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// k-splits of the shrink: about 512 k per split, at most kMaxKSplit.  Depends
-// only on the shape, so add_shrink and add_expand agree without talking.
+// k-splits of the shrink.  Small batches split k (at least 512 per split) so
+// that the k-reduction spreads over many workgroups; the expand re-reads every
+// split's partials once per column chunk, so the split count also shrinks as
+// the batch grows (at most 4096 / rows).  Depends only on the shape, never on
+// the ids.
 int choose_ks(int64_t k, int64_t n_rows)
 {
-    (void)n_rows;
-    int64_t ks = (k + 511) / 512;
-    return (int)std::max<int64_t>(1, std::min<int64_t>(ks, kMaxKSplit));
+    int64_t ks = std::max<int64_t>(1, k / 512);
+    ks = std::min<int64_t>(ks, std::max<int64_t>(1, 4096 / std::max<int64_t>(1, n_rows)));
+    ks = std::min<int64_t>(ks, kMaxKSplit);
+    // powers of two keep blocks of one split on one XCD
+    int64_t p = 1;
+    while (p * 2 <= ks)
+        p *= 2;
+    return (int)p;
 }
 
 // Tiles of one batch never exceed ceil(rows / 16) plus one ragged tile per
@@ -64,7 +72,7 @@ void free_stack(lora_stack *st)
     (void)hipFree(st->B_pool);
     (void)hipFree(st->d_rank);
     (void)hipFree(st->d_scale);
-    (void)hipFree(st->vws);
+    (void)hipFree(st->vpart);
     delete st;
 }
 
@@ -80,8 +88,10 @@ void free_segments(lora_segments *seg)
     delete seg;
 }
 
-// MFMA tiles need bf16 and slices made of whole 64-column blocks; otherwise
-// the dense tiles of a batch are served by the vector code.
+// MFMA tiles need bf16, slices made of whole 64-column blocks, and the v of a
+// 64-row tile for the slices one 256-column chunk touches must fit the
+// expand's LDS; otherwise the dense tiles of a batch are served by the vector
+// code.
 bool stack_has_mfma_path(const lora_stack *st)
 {
     if (st->dtype != LORA_BF16)
@@ -89,7 +99,17 @@ bool stack_has_mfma_path(const lora_stack *st)
     for (int q = 0; q < st->n_slices; ++q)
         if (st->slice_d[q] % 64 != 0)
             return false;
-    return true;
+    int nq_max = 1;
+    for (int64_t c0 = 0; c0 < st->D; c0 += kExpandCols) {
+        const int64_t c1 = std::min<int64_t>(c0 + kExpandCols, st->D) - 1;
+        int q0 = 0, q1 = 0;
+        while (q0 + 1 < st->n_slices && c0 >= st->slice_off[q0 + 1])
+            ++q0;
+        while (q1 + 1 < st->n_slices && c1 >= st->slice_off[q1 + 1])
+            ++q1;
+        nq_max = std::max(nq_max, q1 - q0 + 1);
+    }
+    return (int64_t)kSgmvTileRows * nq_max * st->r_max <= kExpandVsFloats;
 }
 
 lora_status check_apply_common(const lora_stack *st, const lora_segments *seg)
@@ -119,11 +139,10 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
         a.slice_off[q] = st->slice_off[q];
     a.a_slot_stride = (int64_t)st->n_slices * st->r_max * st->k;
     a.b_slot_stride = st->D * st->rp_max;
-    a.vws = st->vws;
+    a.vpart = st->vpart;
     a.max_rows = st->max_rows;
     a.ks = choose_ks(st->k, seg->n_rows);
     a.mfma_ok = stack_has_mfma_path(st) ? 1 : 0;
-    a.perm = seg->perm;
     a.counts = seg->counts;
     a.tiles = seg->tiles;
     return a;
@@ -175,7 +194,7 @@ lora_status lora_stack_create(lora_stack **out, lora_dtype dtype, int n_slots, i
     st->A_pool = st->B_pool = nullptr;
     st->d_rank = nullptr;
     st->d_scale = nullptr;
-    st->vws = nullptr;
+    st->vpart = nullptr;
     if (hipGetDevice(&st->device) != hipSuccess) {
         delete st;
         return LORA_E_HIP;
@@ -199,13 +218,13 @@ lora_status lora_stack_create(lora_stack **out, lora_dtype dtype, int n_slots, i
 
     const size_t a_bytes = (size_t)n_slots * n_slices * r_max * k * st->esize;
     const size_t b_bytes = (size_t)n_slots * D * st->rp_max * st->esize;
-    const size_t v_bytes = (size_t)kMaxKSplit * max_rows * n_slices * r_max * sizeof(float);
+    const size_t v_bytes = (size_t)max_rows * n_slices * r_max * sizeof(float);
     hipError_t e = hipSuccess;
     if (e == hipSuccess) e = hipMalloc(&st->A_pool, a_bytes);
     if (e == hipSuccess) e = hipMalloc(&st->B_pool, b_bytes);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->d_rank), sizeof(int32_t) * n_slots);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->d_scale), sizeof(float) * n_slots);
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->vws), v_bytes);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->vpart), kMaxKSplit * v_bytes);
     if (e == hipSuccess) e = hipMemset(st->A_pool, 0, a_bytes);
     if (e == hipSuccess) e = hipMemset(st->B_pool, 0, b_bytes);
     if (e == hipSuccess) e = hipMemset(st->d_rank, 0, sizeof(int32_t) * n_slots);
@@ -333,7 +352,7 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->seg_off), sizeof(int32_t) * (n_slots + 1));
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->active), sizeof(int32_t) * n_slots);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->counts), sizeof(int32_t) * kCntSlots);
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->tiles), sizeof(int4) * seg->max_tiles);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->tiles), sizeof(ShrinkTile) * seg->max_tiles);
     if (e == hipSuccess) e = hipMemset(seg->counts, 0, sizeof(int32_t) * kCntSlots);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -376,7 +395,9 @@ lora_status lora_build_segments(const lora_stack *st, const int32_t *ids, int64_
     a.n_slots = st->n_slots;
     a.slot_rank = st->d_rank;
     a.dense_min = seg->dense_min;
-    a.sgmv_ok = 1;
+    // dense groups of small batches are cut into 16-row tiles (more workgroups
+    // for few rows), of large batches into 64-row tiles (B reused by 64 rows)
+    a.sgmv_rows = n_rows <= 4096 ? kBgmvTileRows : kSgmvTileRows;
     a.perm = seg->perm;
     a.seg_off = seg->seg_off;
     a.active = seg->active;

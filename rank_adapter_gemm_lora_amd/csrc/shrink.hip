@@ -1,0 +1,236 @@
+// shrink.hip -- add_shrink: v = A_s x_i for every valid row, every slice.
+//
+// Page "Multi-LoRA Serving: one base, many adapters", section 2 flowchart and
+// section 3.4: add_shrink computes the rank-r product v = A x grouped per
+// adapter; section 3.1: A is r x k.  v stays fp32 (it is never rounded to the
+// storage type).
+//
+// Grid: (k-splits, tile bound).  A workgroup reads its tile record (slot, first
+// grouping position, row count, path and the row indices) in one load, so the
+// only dependent round trip before the x and A loads is that record.  Blocks
+// with the same k-split sit on the same XCD when the split count is a multiple
+// of 8 (they read the same slice of A).
+//
+//   BGMV tile (<= 16 rows of one slot): each wavefront owns up to 4 rows and
+//     walks them two at a time; each lane reads 8 consecutive k of A and x per
+//     step (16-byte loads), accumulates 16 rank partials per row with packed
+//     bf16 dot products, and a wavefront reduce-scatter folds the 64 lanes.
+//   SGMV tile (<= 64 rows, bf16, MFMA): M = rows (4 M-tiles of 16), N = ranks
+//     (one N-tile per slice and 16-rank chunk), K = k; the four wavefronts
+//     split the workgroup's k-range so no operand is loaded twice, and their
+//     partial tiles are summed in LDS in wavefront order.
+//
+// Each k-split writes its fp32 partial of v, indexed by split and grouping
+// position; the expand sums the splits in split order, so results are
+// bit-reproducible and no workgroup waits on another.
+#include "device_common.h"
+#include "internal.h"
+#include "mfma.h"
+
+namespace lora {
+
+namespace {
+
+constexpr int kNT = 4;    // N-tiles (slice, 16-rank chunk) accumulated at once (SGMV)
+constexpr int kSt = 4;    // 8-element k groups per lane per SGMV step
+
+// Destination of one split's v for grouping position pos.
+__device__ __forceinline__ float *v_out(const ApplyArgs &a, int ks, int pos)
+{
+    const int SR = a.n_slices * a.r_max;
+    return a.vpart + ((int64_t)ks * a.max_rows + pos) * SR;
+}
+
+template <int DT>
+__device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int p0, int cnt,
+                                 int ks)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = a.rank[s];
+    const int64_t g8 = a.k >> 3;                       // 8-element groups along k
+    const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
+
+    // wavefront w owns rows w, w + 4, w + 8, w + 12, two at a time
+    for (int pair = 0; pair < 2; ++pair) {
+        const int u0 = wave + 8 * pair, u1 = u0 + 4;
+        if (u0 >= cnt)
+            break;
+        const bool has1 = u1 < cnt;
+        const int64_t x0 = (int64_t)rows[u0] * a.ldx;
+        const int64_t x1 = (int64_t)rows[has1 ? u1 : u0] * a.ldx;
+        for (int q = 0; q < a.n_slices; ++q) {
+            for (int j0 = 0; j0 < r; j0 += 16) {
+                const int64_t abase =
+                    ((int64_t)s * a.n_slices + q) * a.r_max * a.k + (int64_t)j0 * a.k;
+                float acc0[16], acc1[16];
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj)
+                    acc0[jj] = acc1[jj] = 0.f;
+#pragma nounroll
+                for (int64_t g = gb + lane; g < ge; g += 64) {
+                    Vec8<DT> xa, xb;
+                    xa.load(a.x, x0 + g * 8);
+                    if (has1)
+                        xb.load(a.x, x1 + g * 8);
+                    else
+                        xb.zero();
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj) {
+                        Vec8<DT> av;
+                        if (j0 + jj < r)
+                            av.load(a.A, abase + (int64_t)jj * a.k + g * 8);
+                        else
+                            av.zero();
+                        acc0[jj] = av.dot(xa, acc0[jj]);
+                        acc1[jj] = av.dot(xb, acc1[jj]);
+                    }
+                }
+                const int j = (lane >> 2) & 15;
+                const float t0 = wave_reduce_scatter16(acc0);
+                if ((lane & 3) == 0 && j0 + j < r)
+                    v_out(a, ks, p0 + u0)[q * a.r_max + j0 + j] = t0;
+                if (has1) {
+                    const float t1 = wave_reduce_scatter16(acc1);
+                    if ((lane & 3) == 0 && j0 + j < r)
+                        v_out(a, ks, p0 + u1)[q * a.r_max + j0 + j] = t1;
+                }
+            }
+        }
+    }
+}
+
+__device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int p0, int cnt,
+                                 int ks)
+{
+    __shared__ f32x4_t red[4][kNT * 64];   // [wave][tt * 64 + lane]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    int64_t xrow[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+        xrow[mt] = (int64_t)rows[min(16 * mt + m, cnt - 1)] * a.ldx;   // clamp: dropped later
+    const int r = a.rank[s];
+    const int nj = (r + 15) >> 4;
+    const int NT = a.n_slices * nj;
+    const int64_t g8 = a.k >> 3;
+    const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
+    const int64_t wb = gb + (ge - gb) * wave / 4, we = gb + (ge - gb) * (wave + 1) / 4;
+    const int n_mt = (cnt + 15) >> 4;
+
+    for (int t0 = 0; t0 < NT; t0 += kNT) {
+        int64_t arow[kNT];
+        bool aok[kNT];
+#pragma unroll
+        for (int tt = 0; tt < kNT; ++tt) {
+            const int t = t0 + tt;
+            const int q = t / nj, jc = t - q * nj;
+            const int j = jc * 16 + m;
+            aok[tt] = t < NT && j < r;
+            arow[tt] = aok[tt] ? (((int64_t)s * a.n_slices + q) * a.r_max + j) * a.k : 0;
+        }
+        f32x4_t acc[4][kNT];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int tt = 0; tt < kNT; ++tt)
+                acc[mt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        for (int64_t u0 = wb; u0 < we; u0 += 4 * kSt) {
+            uint4 xs[4][kSt], as[kNT][kSt];
+#pragma unroll
+            for (int st = 0; st < kSt; ++st) {
+                const int64_t unit = u0 + kSt * g + st;
+                const bool ok = unit < we;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    xs[mt][st] = (ok && mt < n_mt) ? load16(a.x, xrow[mt] + unit * 8)
+                                                  : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int tt = 0; tt < kNT; ++tt)
+                    as[tt][st] = (ok && aok[tt]) ? load16(a.A, arow[tt] + unit * 8)
+                                                 : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int st = 0; st < kSt; ++st)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    if (mt < n_mt) {
+#pragma unroll
+                        for (int tt = 0; tt < kNT; ++tt)
+                            acc[mt][tt] = mfma_bf16_16x16x32(xs[mt][st], as[tt][st], acc[mt][tt]);
+                    }
+        }
+
+        // fixed-order sum of the four k-quarters, one M-tile at a time
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            if (mt >= n_mt)
+                break;
+#pragma unroll
+            for (int tt = 0; tt < kNT; ++tt)
+                red[wave][tt * 64 + lane] = acc[mt][tt];
+            __syncthreads();
+            {
+                const int e = threadIdx.x;            // kNT * 64 == 256 entries
+                const f32x4_t v = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+                const int ln = e & 63, tt = e >> 6;
+                const int t = t0 + tt;
+                const int q = t / nj, jc = t - q * nj;
+                const int j = jc * 16 + (ln & 15);
+                if (t < NT && j < r) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int u = 16 * mt + 4 * (ln >> 4) + i;
+                        if (u < cnt)
+                            v_out(a, ks, p0 + u)[q * a.r_max + j] = v[i];
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+static_assert(kNT * 64 == 256, "one reduction entry per thread");
+
+template <int DT>
+__global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
+{
+    __shared__ int32_t rows[kSgmvTileRows];
+    const int ks = blockIdx.x, t = blockIdx.y;
+    const ShrinkTile *T = a.tiles + t;
+    // header, row indices and counts in one round trip
+    const int4 h = *reinterpret_cast<const int4 *>(T);
+    const int32_t my_row = threadIdx.x < kSgmvTileRows ? T->rows[threadIdx.x] : 0;
+    const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
+    if (t >= n_tiles)
+        return;
+    if (threadIdx.x < kSgmvTileRows)
+        rows[threadIdx.x] = my_row;
+    __syncthreads();
+    const int s = h.x, p0 = h.y, cnt = h.z;
+    if constexpr (DT == DT_BF16) {
+        if (h.w == kTileSgmv && a.mfma_ok) {
+            sgmv_shrink_tile(a, rows, s, p0, cnt, ks);
+            return;
+        }
+    }
+    // BGMV tile, or a dense tile of a stack without the MFMA path
+    for (int sub = 0; sub < cnt; sub += kBgmvTileRows)
+        bgmv_shrink_tile<DT>(a, rows + sub, s, p0 + sub, min(kBgmvTileRows, cnt - sub), ks);
+}
+
+}  // namespace
+
+hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream)
+{
+    if (max_tiles <= 0)
+        return hipSuccess;
+    const dim3 grid(a.ks, max_tiles);
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(shrink_kernel<DT_BF16>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(shrink_kernel<DT_F32>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace lora

@@ -249,3 +249,35 @@ def test_shrink_expand_split_equals_apply():
     finally:
         r1.close()
         r2.close()
+
+
+SEG_CASES = [(1, 1), (63, 3), (64, 3), (65, 3), (1000, 100), (2048, 254), (2049, 254),
+             (2048, 255), (2048, 256), (700, 300), (4097, 10), (9000, 7)]
+
+
+@pytest.mark.parametrize("n,n_slots", SEG_CASES)
+def test_segments_across_builders(n, n_slots):
+    """Both segment builders (one wavefront for small batches, one 1024-thread
+    workgroup beyond) give the oracle's grouping bit for bit, bad ids included."""
+    rng = np.random.default_rng(n * 7 + n_slots)
+    ranks = np.full(n_slots, 8, np.int32)
+    ranks[rng.random(n_slots) < 0.1] = 0
+    p = synth.make_random(3, n_rows=n, k=8, slice_d=[8], n_slots=n_slots, ranks=ranks, r_max=8,
+                          ids=rng.integers(-2, n_slots + 2, size=n).astype(np.int32))
+    note(f"segments n={n} slots={n_slots}")
+    for dm in (1, 16, 1 << 30):
+        run = GpuRun(p, dense_min=dm)
+        try:
+            run.build()
+            got = run.segments()
+            nb, ns = lb.lora_segments_tile_counts(run.seg, run.stream)
+        finally:
+            run.close()
+        ref = oracle.build_segments(p.ids, p.n_slots, p.ranks)
+        for key in ("perm", "seg_off", "active", "counts"):
+            np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{key} dense_min={dm}")
+        cnt = np.diff(ref["seg_off"])
+        dense = cnt >= dm
+        tile = 16 if n <= 4096 else 64
+        assert ns == int(np.sum((cnt[dense] + tile - 1) // tile))
+        assert nb == int(np.sum((cnt[~dense & (cnt > 0)] + 15) // 16))

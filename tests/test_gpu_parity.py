@@ -94,5 +94,5 @@ def test_tile_plan_follows_policy():
         finally:
             run.close()
         dense = counts >= dm
-        assert ns == int(np.sum((counts[dense] + 63) // 64))
+        assert ns == int(np.sum((counts[dense] + 15) // 16))   # small batch: 16-row dense tiles
         assert nb == int(np.sum((counts[~dense & (counts > 0)] + 15) // 16))
