@@ -2,8 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is the whole hot path over one batch: lora_build_segments (group rows
-by adapter), lora_add_shrink (v = A x) and lora_add_expand (y += scale B v).
+A step is the whole hot path over one batch, one lora_build_apply call: group
+the rows by adapter, shrink (v = A x), expand (y += scale B v).  Up to 1024
+rows that is two kernels (grouping fused into the shrink, then the expand);
+larger batches take three (grouping, shrink, expand).
 Inputs are resident in HBM before the timed region.  Steps rotate through
 independent buffer sets (stack + ids + x + y) totalling >= 512 MB so that the
 256 MB MALL cannot serve them: every step reads its weights and rows from HBM.
@@ -18,10 +20,11 @@ One JSON line goes to stdout:
              committed measurement matches the current kernel sources, else null
   cpu_baseline  the CPU oracle on the host cores on a bounded sample
 
-Other modes: --all (every workload, lines to --out), --copy-probe (plain copy
-kernel at the decode size and at 1 GB: the achievable HBM ceiling, also the
-calibration run for the PMC counters), --pmc-summary DIR (fold rocprofv3
-counter output into profiles/).
+Other modes: --all (every workload, lines to --out); --copy-probe (plain copy
+kernel at the decode size and at 1 GB: the achievable HBM ceiling);
+--copy-calib MB (a plain copy of known size, the calibration run for the PMC
+byte counters); --pmc-summary (fold two rocprofv3 --pmc runs and their
+calibration runs into bytes per launch).
 """
 from __future__ import annotations
 
@@ -44,8 +47,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATE_BYTES = 512 << 20       # 2x the 256 MB MALL
 DEFAULT_WORKLOAD = "decode_bgmv"
-KERNELS = ("seg_build", "shrink", "expand")
-KERNEL_SOURCES = ("seg_build.hip", "apply.hip", "sgmv.h", "device_common.h", "internal.h")
+FUSED_MAX_ROWS = 1024           # lora_build_shrink groups inside the shrink up to this many
+FUSED_MAX_BLOCKS = 256          # rows and shrink workgroups (the library's own rule)
+KERNEL_SOURCES = ("seg_build.hip", "shrink.hip", "expand.hip", "group.h", "mfma.h",
+                  "device_common.h", "internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_bgmv.json")
 
 
@@ -72,9 +77,26 @@ def accounting(p) -> dict:
     return dict(n_valid=n_valid, distinct_slots=int(slots.size),
                 bytes=dict(shrink=x_bytes + live_a, expand=y_bytes + live_b,
                            seg_build=8 * p.n_rows + 4 * (p.n_slots + 1),
+                           build_shrink=x_bytes + live_a + 8 * p.n_rows + 4 * (p.n_slots + 1),
                            total=x_bytes + y_bytes + live_a + live_b),
                 flops=dict(total=int(flops), shrink=int(shrink_flops),
-                           expand=int(flops - shrink_flops)))
+                           build_shrink=int(shrink_flops), expand=int(flops - shrink_flops)))
+
+
+def shrink_blocks(p) -> int:
+    """Workgroups of the shrink launch: k-splits x tile bound (the library's
+    choice of split count and its tile bound, restated to label the timings)."""
+    ks = max(1, p.k // 512)
+    ks = min(ks, max(1, 4096 // max(1, p.n_rows)), 16)
+    ks = 1 << (ks.bit_length() - 1)
+    return ks * ((p.n_rows + 15) // 16 + min(p.n_slots, p.n_rows))
+
+
+def step_kernels(p) -> tuple:
+    """The kernels one step launches, in order."""
+    if 0 < p.n_rows <= FUSED_MAX_ROWS and shrink_blocks(p) <= FUSED_MAX_BLOCKS:
+        return ("build_shrink", "expand")
+    return ("seg_build", "shrink", "expand")
 
 
 def kernel_source_hash() -> str:
@@ -158,13 +180,16 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None) -> 
     def shrink(bs):
         lb.lora_add_shrink(bs.stack, bs.x.data_ptr(), p.ldx, bs.seg, sh)
 
+    def build_shrink(bs):
+        lb.lora_build_shrink(bs.stack, bs.x.data_ptr(), p.ldx, bs.ids.data_ptr(), p.n_rows,
+                             bs.seg, sh)
+
     def expand(bs):
         lb.lora_add_expand(bs.stack, bs.y.data_ptr(), p.ldy, bs.seg, sh)
 
     def step(bs):
-        build(bs)
-        shrink(bs)
-        expand(bs)
+        lb.lora_build_apply(bs.stack, bs.y.data_ptr(), p.ldy, bs.x.data_ptr(), p.ldx,
+                            bs.ids.data_ptr(), p.n_rows, bs.seg, sh)
 
     for i in range(warmup):
         step(sets[i % n_sets])
@@ -186,9 +211,14 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None) -> 
 
     # each kernel alone: K back-to-back launches over the rotating sets (every
     # set already holds its segments and v, so each launch does its full work);
-    # mean launch duration = region time / K, events only at the region's ends
+    # mean launch duration = region time / K, events only at the region's ends.
+    # The split path's grouping and shrink are timed too, for comparison.
+    fns = dict(seg_build=build, shrink=shrink, build_shrink=build_shrink, expand=expand)
+    names = list(step_kernels(p)) + [k for k in ("seg_build", "shrink")
+                                     if k not in step_kernels(p)]
     per = {}
-    for name, fn in (("seg_build", build), ("shrink", shrink), ("expand", expand)):
+    for name in names:
+        fn = fns[name]
         for i in range(min(warmup, n_sets)):
             fn(sets[i % n_sets])
         e0 = torch.cuda.Event(enable_timing=True)
@@ -240,12 +270,12 @@ def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -
     g = run_gpu(p, steps, warmup, rotate=rotate, dense_min=dense_min)
     ms = g["gpu_ms"] / steps
     ku = g["kernel_us"]
-    dom = max(KERNELS, key=lambda k: ku[k])
+    dom = max(step_kernels(p), key=lambda k: ku[k])
     achieved = acct["bytes"][dom] / (ku[dom] * 1e-6) / 1e9
     traffic = committed_traffic(name)
     roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                traffic=(traffic["per_launch_bytes"][dom] if traffic else None),
+                traffic=(traffic["per_launch_bytes"].get(dom) if traffic else None),
                 algorithmic_bytes_per_launch=acct["bytes"][dom],
                 mean_launch_us=round(ku[dom], 3))
     line = {
@@ -264,11 +294,12 @@ def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -
                    "parallelism": "single GPU"},
         "step_hbm_gbs": round(acct["bytes"]["total"] / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(acct["bytes"]["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_kernels": list(step_kernels(p)),
         "kernel_us": {k: round(v, 3) for k, v in ku.items()},
         "kernel_gbs": {k: round(acct["bytes"][k] / (ku[k] * 1e-6) / 1e9, 1)
-                       for k in ("shrink", "expand")},
+                       for k in ku if k != "seg_build"},
         "mfma_util": {k: round(acct["flops"][k] / (ku[k] * 1e-6) / 1e12
-                               / MFMA_BF16_PEAK_TFLOPS, 5) for k in ("shrink", "expand")},
+                               / MFMA_BF16_PEAK_TFLOPS, 5) for k in ku if k != "seg_build"},
         "tiles": g["tiles"],
         "roofline": roof,
         "host_wall_ms_per_step": round(g["wall_s"] * 1e3 / steps, 4),
@@ -307,41 +338,74 @@ def copy_probe(reps: int = 50) -> list:
     return out
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str) -> dict:
-    """Fold two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
-    dispatch) into bytes per launch, scaled so that the calibration copy
-    kernel (torch's elementwise copy of ``copy_bytes`` bytes read + written)
-    reads its true size."""
+def copy_calibration(mbytes: int, reps: int = 20):
+    """A plain device copy of ``mbytes`` MB, ``reps`` times: the calibration
+    kernel for the PMC byte counters (it reads and writes exactly that much)."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = (mbytes << 20) // 2
+    src = torch.ones(n, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _counter_per_dispatch(d: str, counter: str) -> dict:
+    """Median value of ``counter`` per dispatch, by kernel name, from a
+    rocprofv3 --pmc output directory (csv)."""
     import csv
+    vals = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (row["Kernel_Name"], row.get("Dispatch_Id", row.get("Correlation_Id", "")))
+                vals.setdefault(row["Kernel_Name"], {}).setdefault(key[1], 0.0)
+                vals[row["Kernel_Name"]][key[1]] += float(row["Counter_Value"])
+    return {k: float(np.median(list(v.values()))) for k, v in vals.items()}
 
-    def per_kernel(d, counter):
-        vals = {}
-        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            with open(path) as f:
-                for row in csv.DictReader(f):
-                    if row.get("Counter_Name") != counter:
-                        continue
-                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-        return vals
 
-    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
-    write = per_kernel(write_dir, "WRITE_SIZE")
+def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, copy_mb, workload) -> dict:
+    """HBM bytes per launch of each kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for a plain copy of copy_mb MB (read copy_mb, wrote copy_mb)."""
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    cf = _counter_per_dispatch(cal_fetch_dir, "FETCH_SIZE")
+    cw = _counter_per_dispatch(cal_write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mb << 20
 
-    def pick(vals, key):
-        ks = [k for k in vals if key in k]
-        return float(np.median(vals[ks[0]])) * 1024 if ks else None
+    def biggest(d):
+        return max(d.values()) if d else None
 
-    copy_key = "elementwise_kernel"
-    cf, cw = pick(fetch, copy_key), pick(write, copy_key)
-    f_scale = (copy_bytes / 2) / cf if cf else 1.0
-    w_scale = (copy_bytes / 2) / cw if cw else 1.0
-    names = {"seg_build": "seg_build_kernel", "shrink": "shrink_kernel", "expand": "expand_kernel"}
-    per = {}
-    for k, key in names.items():
-        fb, wb = pick(fetch, key), pick(write, key)
-        per[k] = None if fb is None or wb is None else round(fb * f_scale + wb * w_scale)
-    return dict(workload=workload, kernel_sources=kernel_source_hash(), fetch_scale=f_scale,
-                write_scale=w_scale, per_launch_bytes=per)
+    f_scale = copy_bytes / (biggest(cf) * 1024.0) if cf else None
+    w_scale = copy_bytes / (biggest(cw) * 1024.0) if cw else None
+    # kernel functions behind each timed name (the grouping has a small-batch
+    # and a chunked variant)
+    names = {"seg_build": ("seg_build_kernel", "seg_build_small_kernel"),
+             "shrink": ("shrink_kernel",), "build_shrink": ("build_shrink_kernel",),
+             "expand": ("expand_kernel",)}
+
+    def bare(kname):
+        head = kname.replace("(anonymous namespace)", "").split("(")[0].split("<")[0]
+        return head.split("::")[-1].strip()
+
+    per, raw = {}, {}
+    for k, keys in names.items():
+        fb = next((v for n, v in fetch.items() if bare(n) in keys), None)
+        wb = next((v for n, v in write.items() if bare(n) in keys), None)
+        if fb is None and wb is None:
+            continue
+        raw[k] = {"fetch_kib": fb, "write_kib": wb}
+        if fb is None or wb is None or f_scale is None or w_scale is None:
+            per[k] = None
+        else:
+            per[k] = int(round(fb * 1024.0 * f_scale + wb * 1024.0 * w_scale))
+    return dict(workload=workload, kernel_sources=kernel_source_hash(), copy_mb=copy_mb,
+                fetch_scale=f_scale, write_scale=w_scale, raw_per_dispatch=raw,
+                per_launch_bytes=per)
 
 
 def main(argv=None):
@@ -356,13 +420,16 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--dense-min", type=int, default=None, help="SGMV threshold (rows per group)")
     ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--copy-bytes", type=int, default=2 * (7_690_000 // 256 * 256))
+    ap.add_argument("--copy-calib", type=int, default=None, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (PMC calibration)")
+    ap.add_argument("--pmc-summary", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"))
+    ap.add_argument("--copy-mb", type=int, default=256)
     args = ap.parse_args(argv)
 
     if args.pmc_summary:
-        res = pmc_summary(*args.pmc_summary, args.copy_bytes, args.workload)
-        print(json.dumps(res))
+        res = pmc_summary(*args.pmc_summary, args.copy_mb, args.workload)
+        print(json.dumps(res, indent=1))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -372,6 +439,9 @@ def main(argv=None):
     if "RANK" in os.environ and os.environ.get("WORLD_SIZE", "1") != "1":
         print("bench.py runs on one GPU only", file=sys.stderr)
         return 2
+    if args.copy_calib is not None:
+        copy_calibration(args.copy_calib)
+        return 0
     if args.copy_probe:
         res = copy_probe()
         print(json.dumps({"copy_probe": res}))

@@ -221,6 +221,33 @@ lora_status lora_add_expand(const lora_stack *st, void *y, int64_t ldy,
 lora_status lora_apply(const lora_stack *st, void *y, int64_t ldy, const void *x, int64_t ldx,
                        const lora_segments *seg, void *stream);
 
+/*
+ * lora_build_segments followed by lora_add_shrink, as one call: the grouping
+ * of the rows by adapter id that comes before add_shrink (page "Multi-LoRA
+ * Serving", section 2 flowchart; page "LoRA hot-loading and adapter
+ * routing", batched multi-adapter execution) and the shrink itself.  The
+ * segments left in seg and the v left in the stack's scratch are the same as
+ * those of the two calls.  For small batches (n_rows <= 1024 and a shrink
+ * grid of at most 256 workgroups, one per compute unit) the grouping runs
+ * inside the shrink kernel (each of its workgroups groups the ids in LDS): one
+ * launch instead of two on the decode critical path.  Other batches take the
+ * two launches.  ids is read at the call's stream position.  All argument checks
+ * happen before anything is enqueued.  Errors: LORA_E_ARG, LORA_E_HIP.
+ */
+lora_status lora_build_shrink(const lora_stack *st, const void *x, int64_t ldx,
+                              const int32_t *ids, int64_t n_rows, lora_segments *seg,
+                              void *stream);
+
+/*
+ * lora_build_shrink followed by lora_add_expand: one call for a whole batch
+ * (grouping, add_shrink, add_expand with the per-row merge), with the results
+ * and segments of lora_build_segments + lora_apply.  n_rows == 0 only writes
+ * the (empty) segments.  Errors: LORA_E_ARG, LORA_E_HIP.
+ */
+lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const void *x,
+                             int64_t ldx, const int32_t *ids, int64_t n_rows, lora_segments *seg,
+                             void *stream);
+
 /* --------------------------------------------------------------- inspection */
 
 /*

@@ -6,7 +6,9 @@ The compute lives in a C-ABI HIP library (include/lora.h, sources in csrc/);
 it, only provides device memory and streams.
 """
 from .binding import (EXPORTS, LORA_BF16, LORA_F32, LoraError, lora_add_expand,  # noqa: F401
-                      lora_add_shrink, lora_apply, lora_build_segments, lora_evict_slot,
+                      lora_add_shrink, lora_apply, lora_build_apply, lora_build_segments,
+                      lora_build_shrink,
+                      lora_evict_slot,
                       lora_get_device_status, lora_load_slot, lora_segments_create,
                       lora_segments_destroy, lora_segments_download, lora_segments_set_dense_min,
                       lora_segments_tile_counts, lora_slot_info, lora_stack_create,

@@ -25,7 +25,9 @@ STATUS_NAMES = {0: "LORA_OK", 1: "LORA_E_ARG", 2: "LORA_E_RANK", 3: "LORA_E_SLOT
 EXPORTS = ("lora_stack_create", "lora_stack_destroy", "lora_load_slot", "lora_evict_slot",
            "lora_slot_info", "lora_segments_create", "lora_segments_destroy",
            "lora_segments_set_dense_min", "lora_build_segments", "lora_add_shrink",
-           "lora_add_expand", "lora_apply", "lora_segments_download", "lora_get_device_status",
+           "lora_add_expand", "lora_apply", "lora_build_shrink", "lora_build_apply",
+           "lora_segments_download",
+           "lora_get_device_status",
            "lora_segments_tile_counts", "lora_status_string")
 
 _lock = threading.Lock()
@@ -73,6 +75,8 @@ def load(path: str | None = None):
             "lora_add_shrink": [P, P, I64, P, P],
             "lora_add_expand": [P, P, I64, P, P],
             "lora_apply": [P, P, I64, P, I64, P, P],
+            "lora_build_shrink": [P, P, I64, P, I64, P, P],
+            "lora_build_apply": [P, P, I64, P, I64, P, I64, P, P],
             "lora_segments_download": [P, P, P, P, P, P],
             "lora_get_device_status": [P, P, P],
             "lora_segments_tile_counts": [P, P, P, P],
@@ -162,6 +166,18 @@ def lora_add_expand(stack, y: int, ldy: int, seg, stream=None):
 def lora_apply(stack, y: int, ldy: int, x: int, ldx: int, seg, stream=None):
     _check(load().lora_apply(stack, ctypes.c_void_p(y), int(ldy), ctypes.c_void_p(x), int(ldx),
                              seg, _stream(stream)), "lora_apply")
+
+
+def lora_build_shrink(stack, x: int, ldx: int, ids: int, n_rows: int, seg, stream=None):
+    _check(load().lora_build_shrink(stack, ctypes.c_void_p(x), int(ldx), ctypes.c_void_p(ids),
+                                    int(n_rows), seg, _stream(stream)), "lora_build_shrink")
+
+
+def lora_build_apply(stack, y: int, ldy: int, x: int, ldx: int, ids: int, n_rows: int, seg,
+                     stream=None):
+    _check(load().lora_build_apply(stack, ctypes.c_void_p(y), int(ldy), ctypes.c_void_p(x),
+                                   int(ldx), ctypes.c_void_p(ids), int(n_rows), seg,
+                                   _stream(stream)), "lora_build_apply")
 
 
 def lora_segments_download(seg, n_rows: int, n_slots: int, stream=None):

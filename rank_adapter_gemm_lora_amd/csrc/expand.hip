@@ -108,8 +108,8 @@ __device__ __forceinline__ void merge16(const ApplyArgs &a, int64_t yi, bool h0,
     }
 }
 
-__device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int p0, int cnt,
-                                 int64_t c0, float *vs)
+__device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
+                                 int p0, int cnt, int64_t c0, float *vs)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, m = lane & 15;
@@ -129,13 +129,8 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
             y1[nt].load(a.y, yi[nt] + 8);
         }
     }
-    const int r = a.rank[s];
-    const float scale = a.scale[s];
-    const int q_lo = slice_of(a, c0);
-    const int nq = slice_of(a, min(c0 + kExpandCols, a.D) - 1) - q_lo + 1;
-    stage_v(a, p0, cnt, r, q_lo, nq, vs);
-
-    const int rp = (r + 7) & ~7, nj = (r + 15) >> 4, pitch = nq * r;
+    // the first 16 ranks of B for the lane's columns, also in flight
+    const int rp = (r + 7) & ~7, nj = (r + 15) >> 4;
     const int64_t bslot = (int64_t)s * a.b_slot_stride;
     const int64_t cbw = c0 + 64 * wave;
     int64_t col[4];
@@ -147,6 +142,10 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     for (int mt = 0; mt < 4; ++mt)
         bop[mt] = (in_d && 8 * (g & 1) < rp) ? load16(a.B, bslot + col[mt] * rp + 8 * (g & 1))
                                              : make_uint4(0, 0, 0, 0);
+    const int q_lo = slice_of(a, c0);
+    const int nq = slice_of(a, min(c0 + kExpandCols, a.D) - 1) - q_lo + 1;
+    const int pitch = nq * r;
+    stage_v(a, p0, cnt, r, q_lo, nq, vs);
     __syncthreads();   // v staged
     if (!in_d)
         return;
@@ -203,12 +202,32 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     }
 }
 
+// One pass of B for the vector path: the 256 columns' ranks [4 quad .. 4 quad + 3]
+// of pass base j0 (bf16: rank pairs 2 (pc + 4 quad) .., fp32: ranks j0 + 4 quad ..),
+// as 16-byte words; thread c owns column c0 + c.
 template <int DT>
-__device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int p0, int cnt,
-                                 int64_t c0, float *lds)
+__device__ __forceinline__ uint4 b_word(const ApplyArgs &a, int64_t bslot, int64_t gc, int rp,
+                                        int elem0)
 {
+    if (gc >= a.D || elem0 >= rp)
+        return make_uint4(0, 0, 0, 0);
+    if constexpr (DT == DT_BF16)
+        return load16(a.B, bslot + gc * rp + elem0);
+    else
+        return *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.B) + bslot +
+                                                gc * rp + elem0);
+}
+
+template <int DT>
+__device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
+                                 int p0, int cnt, int64_t c0, float *lds)
+{
+    // per pass: bf16 16 rank pairs (4 words of 4 pairs per column), fp32 16 ranks
+    // (4 words of 4 ranks per column)
+    constexpr int kWords = 4;
+    constexpr int kPassElems = DT == DT_BF16 ? 2 * kPairChunk : 16;
     float *vs = lds;
-    uint32_t *bsh = reinterpret_cast<uint32_t *>(lds + kVecVsFloats);   // [pp][col]
+    uint32_t *bsh = reinterpret_cast<uint32_t *>(lds + kVecVsFloats);   // [word lane][col]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, m = lane & 15;
     const bool row_ok = m < cnt;
@@ -221,13 +240,20 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     if (h1)
         y1.load(a.y, yi + 8);
 
-    const int r = a.rank[s];
-    const float scale = a.scale[s];
+    const int rp = (r + 7) & ~7;
+    const int64_t bslot = (int64_t)s * a.b_slot_stride;
+    const int64_t gcol = c0 + threadIdx.x;            // the column this thread stages
+    constexpr int kElemsPerWord = DT == DT_BF16 ? 8 : 4;
+    // the first pass of B in flight while v is staged
+    uint4 w[kWords];
+#pragma unroll
+    for (int q4 = 0; q4 < kWords; ++q4)
+        w[q4] = b_word<DT>(a, bslot, gcol, rp, kElemsPerWord * q4);
+
     const int q_lo = slice_of(a, c0);
     const int nq = slice_of(a, min(c0 + kExpandCols, a.D) - 1) - q_lo + 1;
     stage_v(a, p0, cnt, r, q_lo, nq, vs);
-    const int pitch = nq * r, rp = (r + 7) & ~7;
-    const int64_t bslot = (int64_t)s * a.b_slot_stride;
+    const int pitch = nq * r;
     const int cl = 64 * wave + 16 * g;               // lane's first column in the chunk
     int qh[2];
 #pragma unroll
@@ -239,24 +265,24 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     for (int c = 0; c < 16; ++c)
         acc[c] = 0.f;
 
-    if constexpr (DT == DT_BF16) {
-        const int npair = rp / 2;                    // multiple of 4
-        for (int pc = 0; pc < npair; pc += kPairChunk) {
-            const int np = min(kPairChunk, npair - pc);
-            // B rank pairs [pc, pc + np) of the 256 columns -> bsh[pp][col]
-            for (int e = threadIdx.x; e < kExpandCols * (np / 4); e += blockDim.x) {
-                const int c = e % kExpandCols, quad = e / kExpandCols;
-                const int64_t gc = c0 + c;
-                const uint4 w4 = gc < a.D ? load16(a.B, bslot + gc * rp + 2 * (pc + 4 * quad))
-                                          : make_uint4(0, 0, 0, 0);
-                bsh[(4 * quad + 0) * kExpandCols + c] = w4.x;
-                bsh[(4 * quad + 1) * kExpandCols + c] = w4.y;
-                bsh[(4 * quad + 2) * kExpandCols + c] = w4.z;
-                bsh[(4 * quad + 3) * kExpandCols + c] = w4.w;
-            }
-            __syncthreads();   // v and this pass of B staged
+    for (int j0 = 0; j0 < rp; j0 += kPassElems) {
+        if (j0 > 0) {
+#pragma unroll
+            for (int q4 = 0; q4 < kWords; ++q4)
+                w[q4] = b_word<DT>(a, bslot, gcol, rp, j0 + kElemsPerWord * q4);
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < kWords; ++q4) {
+            bsh[(4 * q4 + 0) * kExpandCols + threadIdx.x] = w[q4].x;
+            bsh[(4 * q4 + 1) * kExpandCols + threadIdx.x] = w[q4].y;
+            bsh[(4 * q4 + 2) * kExpandCols + threadIdx.x] = w[q4].z;
+            bsh[(4 * q4 + 3) * kExpandCols + threadIdx.x] = w[q4].w;
+        }
+        __syncthreads();   // v and this pass of B staged
+        if constexpr (DT == DT_BF16) {
+            const int np = min(kPairChunk, (rp - j0) / 2);
             for (int pp = 0; pp < np; ++pp) {
-                const int j = 2 * (pc + pp);
+                const int j = j0 + 2 * pp;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const float *vr = vs + m * pitch + qh[hh] * r;
@@ -274,26 +300,8 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                     }
                 }
             }
-            __syncthreads();   // bsh is restaged by the next pass
-        }
-    } else {
-        // fp32: 16 ranks of the 256 columns per pass, as floats; fp32 FMA
-        float *bf = reinterpret_cast<float *>(bsh);   // [jj][col]
-        for (int j0 = 0; j0 < r; j0 += 16) {
-            for (int e = threadIdx.x; e < kExpandCols * 4; e += blockDim.x) {
-                const int c = e % kExpandCols, quad = e / kExpandCols;
-                const int64_t gc = c0 + c;
-                const int j = j0 + 4 * quad;
-                float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (gc < a.D && j < rp)
-                    w4 = *reinterpret_cast<const float4 *>(
-                        reinterpret_cast<const float *>(a.B) + bslot + gc * rp + j);
-                bf[(4 * quad + 0) * kExpandCols + c] = w4.x;
-                bf[(4 * quad + 1) * kExpandCols + c] = w4.y;
-                bf[(4 * quad + 2) * kExpandCols + c] = w4.z;
-                bf[(4 * quad + 3) * kExpandCols + c] = w4.w;
-            }
-            __syncthreads();
+        } else {
+            const float *bf = reinterpret_cast<const float *>(bsh);   // [jj][col]
             for (int jj = 0; jj < 16 && j0 + jj < r; ++jj) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
@@ -304,8 +312,8 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                                                acc[8 * hh + c]);
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();   // bsh is restaged by the next pass
     }
     merge16<DT>(a, yi, h0, h1, y0, y1, scale, acc);
 }
@@ -315,32 +323,41 @@ __global__ __launch_bounds__(256) void expand_kernel(ApplyArgs a)
 {
     __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
     __shared__ int32_t rows[kSgmvTileRows];
+    __shared__ int32_t srank[LORA_MAX_SLOTS];
+    __shared__ float sscale[LORA_MAX_SLOTS];
     const int t = blockIdx.y;
     const ShrinkTile *T = a.tiles + t;
-    // header, row indices and counts in one round trip
+    // header, row indices, counts and the slot table in one round trip
     const int4 h = *reinterpret_cast<const int4 *>(T);
     const int32_t my_row = threadIdx.x < kSgmvTileRows ? T->rows[threadIdx.x] : 0;
     const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
+    for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x) {
+        srank[e] = a.rank[e];
+        sscale[e] = a.scale[e];
+    }
     if (t >= n_tiles)
         return;
     const int64_t c0 = (int64_t)blockIdx.x * kExpandCols;
     if (c0 >= a.D)
         return;
     const int s = h.x, p0 = h.y, cnt = h.z;
-    if (a.rank[s] == 0)
-        return;   // slot emptied since the grouping was built: rows stay untouched
     if (threadIdx.x < kSgmvTileRows)
         rows[threadIdx.x] = my_row;
     __syncthreads();
+    const int r = srank[s];
+    const float scale = sscale[s];
+    if (r == 0)
+        return;   // slot emptied since the grouping was built: rows stay untouched
     if constexpr (DT == DT_BF16) {
         if (h.w == kTileSgmv && a.mfma_ok) {
-            sgmv_expand_tile(a, rows, s, p0, cnt, c0, lds);
+            sgmv_expand_tile(a, rows, s, r, scale, p0, cnt, c0, lds);
             return;
         }
     }
     // BGMV tile, or a dense tile of a stack without the MFMA path
     for (int sub = 0; sub < cnt; sub += kBgmvTileRows) {
-        bgmv_expand_tile<DT>(a, rows + sub, s, p0 + sub, min(kBgmvTileRows, cnt - sub), c0, lds);
+        bgmv_expand_tile<DT>(a, rows + sub, s, r, scale, p0 + sub, min(kBgmvTileRows, cnt - sub),
+                             c0, lds);
         __syncthreads();   // LDS is restaged by the next sub-tile
     }
 }

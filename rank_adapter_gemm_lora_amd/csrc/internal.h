@@ -61,6 +61,7 @@ struct ApplyArgs {
     const void *B;             // pool, slot s: [D][rp_s] at s * b_slot_stride
     const int32_t *rank;       // [n_slots]
     const float *scale;        // [n_slots] alpha / rank
+    int n_slots;
     int64_t k;
     int n_slices;
     int r_max;
@@ -83,6 +84,10 @@ struct ApplyArgs {
 
 hipError_t launch_seg_build(const SegBuildArgs &a, hipStream_t stream);
 hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream);
+// grouping and shrink in one launch; batches of at most 1024 rows
+constexpr int kFusedMaxRows = 1024;
+hipError_t launch_build_shrink(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
+                               hipStream_t stream);
 hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_set_slot(int32_t *rank, float *scale, int slot, int r, float s,

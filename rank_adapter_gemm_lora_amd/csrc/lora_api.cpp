@@ -131,6 +131,7 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     a.B = st->B_pool;
     a.rank = st->d_rank;
     a.scale = st->d_scale;
+    a.n_slots = st->n_slots;
     a.k = st->k;
     a.n_slices = st->n_slices;
     a.r_max = st->r_max;
@@ -380,8 +381,10 @@ lora_status lora_segments_set_dense_min(lora_segments *seg, int m_min)
     return LORA_OK;
 }
 
-lora_status lora_build_segments(const lora_stack *st, const int32_t *ids, int64_t n_rows,
-                                lora_segments *seg, void *stream)
+namespace {
+
+lora_status check_build(const lora_stack *st, const int32_t *ids, int64_t n_rows,
+                        const lora_segments *seg)
 {
     if (!st || !seg || n_rows < 0 || n_rows > seg->max_rows || st->n_slots > seg->n_slots_cap)
         return LORA_E_ARG;
@@ -389,6 +392,12 @@ lora_status lora_build_segments(const lora_stack *st, const int32_t *ids, int64_
         return LORA_E_ARG;
     if (!current_device_is(st->device) || seg->device != st->device)
         return LORA_E_ARG;
+    return LORA_OK;
+}
+
+SegBuildArgs make_seg_args(const lora_stack *st, const int32_t *ids, int64_t n_rows,
+                           lora_segments *seg)
+{
     SegBuildArgs a;
     a.ids = ids;
     a.n = n_rows;
@@ -403,10 +412,50 @@ lora_status lora_build_segments(const lora_stack *st, const int32_t *ids, int64_
     a.active = seg->active;
     a.counts = seg->counts;
     a.tiles = seg->tiles;
-    LORA_TRY(launch_seg_build(a, reinterpret_cast<hipStream_t>(stream)));
+    return a;
+}
+
+void mark_built(lora_segments *seg, const lora_stack *st, int64_t n_rows)
+{
     seg->built = 1;
     seg->n_rows = n_rows;
     seg->n_slots = st->n_slots;
+}
+
+// Grouping inside the shrink pays while the shrink grid fits on the chip in one
+// go: every workgroup repeats the grouping, so a grid of several waves of
+// workgroups would pay it several times over, more than the separate launch.
+constexpr int kFusedMaxBlocks = 256;   // one workgroup per compute unit
+
+bool fused_build_pays(const lora_stack *st, int64_t n_rows)
+{
+    if (n_rows <= 0 || n_rows > kFusedMaxRows)
+        return false;
+    return (int64_t)choose_ks(st->k, n_rows) * max_tiles_for(n_rows, st->n_slots) <=
+           kFusedMaxBlocks;
+}
+
+bool x_ok(const lora_stack *st, const void *x, int64_t ldx)
+{
+    return x && aligned16(x) && ldx >= st->k && ldx % 8 == 0;
+}
+
+bool y_ok(const lora_stack *st, const void *y, int64_t ldy)
+{
+    return y && aligned16(y) && ldy >= st->D && ldy % 8 == 0;
+}
+
+}  // namespace
+
+lora_status lora_build_segments(const lora_stack *st, const int32_t *ids, int64_t n_rows,
+                                lora_segments *seg, void *stream)
+{
+    const lora_status c = check_build(st, ids, n_rows, seg);
+    if (c != LORA_OK)
+        return c;
+    LORA_TRY(launch_seg_build(make_seg_args(st, ids, n_rows, seg),
+                              reinterpret_cast<hipStream_t>(stream)));
+    mark_built(seg, st, n_rows);
     return LORA_OK;
 }
 
@@ -418,7 +467,7 @@ lora_status lora_add_shrink(const lora_stack *st, const void *x, int64_t ldx,
         return c;
     if (seg->n_rows == 0)
         return LORA_OK;
-    if (!x || !aligned16(x) || ldx < st->k || ldx % 8 != 0)
+    if (!x_ok(st, x, ldx))
         return LORA_E_ARG;
     ApplyArgs a = make_args(st, seg);
     a.x = x;
@@ -437,7 +486,7 @@ lora_status lora_add_expand(const lora_stack *st, void *y, int64_t ldy, const lo
         return c;
     if (seg->n_rows == 0)
         return LORA_OK;
-    if (!y || !aligned16(y) || ldy < st->D || ldy % 8 != 0)
+    if (!y_ok(st, y, ldy))
         return LORA_E_ARG;
     ApplyArgs a = make_args(st, seg);
     a.y = y;
@@ -457,12 +506,51 @@ lora_status lora_apply(const lora_stack *st, void *y, int64_t ldy, const void *x
     if (seg->n_rows == 0)
         return LORA_OK;
     // validate both halves before enqueueing either
-    if (!x || !aligned16(x) || ldx < st->k || ldx % 8 != 0)
-        return LORA_E_ARG;
-    if (!y || !aligned16(y) || ldy < st->D || ldy % 8 != 0)
+    if (!x_ok(st, x, ldx) || !y_ok(st, y, ldy))
         return LORA_E_ARG;
     const lora_status s1 = lora_add_shrink(st, x, ldx, seg, stream);
     if (s1 != LORA_OK)
+        return s1;
+    return lora_add_expand(st, y, ldy, seg, stream);
+}
+
+lora_status lora_build_shrink(const lora_stack *st, const void *x, int64_t ldx,
+                              const int32_t *ids, int64_t n_rows, lora_segments *seg, void *stream)
+{
+    const lora_status c = check_build(st, ids, n_rows, seg);
+    if (c != LORA_OK)
+        return c;
+    if (n_rows > st->max_rows || (n_rows > 0 && !x_ok(st, x, ldx)))
+        return LORA_E_ARG;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const SegBuildArgs sb = make_seg_args(st, ids, n_rows, seg);
+    if (!fused_build_pays(st, n_rows)) {
+        LORA_TRY(launch_seg_build(sb, s));
+        mark_built(seg, st, n_rows);
+        return lora_add_shrink(st, x, ldx, seg, stream);
+    }
+    mark_built(seg, st, n_rows);
+    ApplyArgs a = make_args(st, seg);
+    a.x = x;
+    a.ldx = ldx;
+    LORA_TRY(launch_build_shrink(st->dtype == LORA_BF16 ? DT_BF16 : DT_F32, a, sb,
+                                 max_tiles_for(n_rows, st->n_slots), s));
+    return LORA_OK;
+}
+
+lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const void *x,
+                             int64_t ldx, const int32_t *ids, int64_t n_rows, lora_segments *seg,
+                             void *stream)
+{
+    const lora_status c = check_build(st, ids, n_rows, seg);
+    if (c != LORA_OK)
+        return c;
+    if (n_rows > st->max_rows)
+        return LORA_E_ARG;
+    if (n_rows > 0 && (!x_ok(st, x, ldx) || !y_ok(st, y, ldy)))
+        return LORA_E_ARG;
+    const lora_status s1 = lora_build_shrink(st, x, ldx, ids, n_rows, seg, stream);
+    if (s1 != LORA_OK || n_rows == 0)
         return s1;
     return lora_add_expand(st, y, ldy, seg, stream);
 }

@@ -11,6 +11,7 @@
 // how it is laid out on the GPU.  The launch shape depends only on the slot
 // count, never on the ids.
 #include "device_common.h"
+#include "group.h"
 #include "internal.h"
 
 namespace lora {
@@ -268,11 +269,53 @@ __global__ __launch_bounds__(kParThreads) void seg_build_kernel(SegBuildArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Batches of at most kGroupRows rows: one workgroup per bucket again, but every
+// row sits in a register of its own thread (group.h), so the ranks inside a
+// bucket come from ballots instead of a block scan per chunk, and each bucket's
+// workgroup writes the headers of its own tiles.
+__global__ __launch_bounds__(kGroupThreads) void seg_build_small_kernel(SegBuildArgs a)
+{
+    __shared__ GroupLds g;
+    __shared__ int wc[kGroupPer * kGroupWaves];
+    const int b = blockIdx.x, N = a.n_slots, tid = threadIdx.x;
+    const int sg_shift = a.sgmv_rows == 64 ? 6 : 4;
+    int key[kGroupPer];
+    group_hist(a.ids, (int)a.n, N, a.slot_rank, g, key);
+    group_scan(g, N, a.dense_min, sg_shift);
+    int rank[kGroupPer];
+    group_rank(key, b, wc, rank);
+    const BucketPlan p = bucket_plan(g, b, N, a.dense_min, sg_shift);
+    const int mask = (1 << p.shift) - 1;
+#pragma unroll
+    for (int j = 0; j < kGroupPer; ++j) {
+        if (rank[j] >= 0) {
+            const int row = j * kGroupThreads + tid;
+            a.perm[p.first + rank[j]] = row;
+            if (b < N)
+                a.tiles[p.tile0 + (rank[j] >> p.shift)].rows[rank[j] & mask] = row;
+        }
+    }
+    if (b < N) {
+        const int nt = (p.count + mask) >> p.shift;
+        for (int m = tid; m < nt; m += kGroupThreads)
+            *reinterpret_cast<int4 *>(&a.tiles[p.tile0 + m]) =
+                make_int4(b, p.first + (m << p.shift), min(1 << p.shift, p.count - (m << p.shift)),
+                          p.path);
+    }
+    if (b == 0)
+        group_store(g, N, a.seg_off, a.active, a.counts);
+}
+
 }  // namespace
 
 hipError_t launch_seg_build(const SegBuildArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(seg_build_kernel, dim3(a.n_slots + 1), dim3(kParThreads), 0, stream, a);
+    if (a.n <= kGroupRows)
+        hipLaunchKernelGGL(seg_build_small_kernel, dim3(a.n_slots + 1), dim3(kGroupThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(seg_build_kernel, dim3(a.n_slots + 1), dim3(kParThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@
 // position; the expand sums the splits in split order, so results are
 // bit-reproducible and no workgroup waits on another.
 #include "device_common.h"
+#include "group.h"
 #include "internal.h"
 #include "mfma.h"
 
@@ -42,11 +43,10 @@ __device__ __forceinline__ float *v_out(const ApplyArgs &a, int ks, int pos)
 }
 
 template <int DT>
-__device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int p0, int cnt,
-                                 int ks)
+__device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, int p0,
+                                 int cnt, int ks)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = a.rank[s];
     const int64_t g8 = a.k >> 3;                       // 8-element groups along k
     const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
 
@@ -99,8 +99,8 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
     }
 }
 
-__device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int p0, int cnt,
-                                 int ks)
+__device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, int p0,
+                                 int cnt, int ks)
 {
     __shared__ f32x4_t red[4][kNT * 64];   // [wave][tt * 64 + lane]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -109,7 +109,6 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
         xrow[mt] = (int64_t)rows[min(16 * mt + m, cnt - 1)] * a.ldx;   // clamp: dropped later
-    const int r = a.rank[s];
     const int nj = (r + 15) >> 4;
     const int NT = a.n_slices * nj;
     const int64_t g8 = a.k >> 3;
@@ -192,31 +191,104 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 }
 static_assert(kNT * 64 == 256, "one reduction entry per thread");
 
+// One tile, its rows already in LDS; r is the slot's rank.
 template <int DT>
-__global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
+__device__ __forceinline__ void shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r,
+                                            int p0, int cnt, int path, int ks)
 {
-    __shared__ int32_t rows[kSgmvTileRows];
-    const int ks = blockIdx.x, t = blockIdx.y;
-    const ShrinkTile *T = a.tiles + t;
-    // header, row indices and counts in one round trip
-    const int4 h = *reinterpret_cast<const int4 *>(T);
-    const int32_t my_row = threadIdx.x < kSgmvTileRows ? T->rows[threadIdx.x] : 0;
-    const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
-    if (t >= n_tiles)
-        return;
-    if (threadIdx.x < kSgmvTileRows)
-        rows[threadIdx.x] = my_row;
-    __syncthreads();
-    const int s = h.x, p0 = h.y, cnt = h.z;
     if constexpr (DT == DT_BF16) {
-        if (h.w == kTileSgmv && a.mfma_ok) {
-            sgmv_shrink_tile(a, rows, s, p0, cnt, ks);
+        if (path == kTileSgmv && a.mfma_ok) {
+            sgmv_shrink_tile(a, rows, s, r, p0, cnt, ks);
             return;
         }
     }
     // BGMV tile, or a dense tile of a stack without the MFMA path
     for (int sub = 0; sub < cnt; sub += kBgmvTileRows)
-        bgmv_shrink_tile<DT>(a, rows + sub, s, p0 + sub, min(kBgmvTileRows, cnt - sub), ks);
+        bgmv_shrink_tile<DT>(a, rows + sub, s, r, p0 + sub, min(kBgmvTileRows, cnt - sub), ks);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
+{
+    __shared__ int32_t rows[kSgmvTileRows];
+    __shared__ int32_t rank[LORA_MAX_SLOTS];
+    const int ks = blockIdx.x, t = blockIdx.y;
+    const ShrinkTile *T = a.tiles + t;
+    // header, row indices, counts and the slot ranks in one round trip
+    const int4 h = *reinterpret_cast<const int4 *>(T);
+    const int32_t my_row = threadIdx.x < kSgmvTileRows ? T->rows[threadIdx.x] : 0;
+    const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
+    for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x)
+        rank[e] = a.rank[e];
+    if (t >= n_tiles)
+        return;
+    if (threadIdx.x < kSgmvTileRows)
+        rows[threadIdx.x] = my_row;
+    __syncthreads();
+    const int r = rank[h.x];
+    if (r == 0)
+        return;   // slot emptied since the grouping was built: nothing to compute
+    shrink_tile<DT>(a, rows, h.x, r, h.y, h.z, h.w, ks);
+}
+
+// Grouping and shrink in one launch, for small batches.  Every workgroup
+// groups the whole batch in LDS (group.h) -- the ids are a few KB, read from
+// L2 by all but the first -- and takes its tile from the plan.  The segments
+// object receives exactly what the grouping kernel would write: workgroups of
+// split 0 store their tile (header and rows) and its stretch of perm,
+// workgroup (0, 0) stores seg_off, active, the counts and the rows without an
+// adapter.  Those stores come last, after the products, so no barrier waits
+// on them.  The expand reads the tiles from memory as usual.
+template <int DT>
+__global__ __launch_bounds__(256) void build_shrink_kernel(ApplyArgs a, SegBuildArgs sb)
+{
+    __shared__ GroupLds g;
+    __shared__ int wc[2][kGroupPer * kGroupWaves];
+    __shared__ int32_t rows[kSgmvTileRows];
+    const int ks = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+    const int N = sb.n_slots;
+    const int sg_shift = sb.sgmv_rows == 64 ? 6 : 4;
+    int key[kGroupPer], rank[kGroupPer];
+    group_hist(sb.ids, (int)sb.n, N, sb.slot_rank, g, key);
+    group_scan(g, N, sb.dense_min, sg_shift);
+    if (t < g.n_sg + g.n_bg) {
+        int s, m;
+        locate_tile(g, N, t, s, m);
+        const BucketPlan p = bucket_plan(g, s, N, sb.dense_min, sg_shift);
+        const int lo = m << p.shift;
+        const int cnt = min(1 << p.shift, p.count - lo), p0 = p.first + lo;
+        group_rank(key, s, wc[0], rank);
+#pragma unroll
+        for (int j = 0; j < kGroupPer; ++j) {
+            const int u = rank[j] - lo;
+            if (rank[j] >= 0 && u >= 0 && u < cnt)
+                rows[u] = j * kGroupThreads + tid;
+        }
+        __syncthreads();
+        shrink_tile<DT>(a, rows, s, g.rank[s], p0, cnt, p.path, ks);
+        if (ks == 0) {
+#pragma unroll
+            for (int j = 0; j < kGroupPer; ++j) {
+                const int u = rank[j] - lo;
+                if (rank[j] >= 0 && u >= 0 && u < cnt) {
+                    const int row = j * kGroupThreads + tid;
+                    sb.perm[p0 + u] = row;
+                    sb.tiles[t].rows[u] = row;
+                }
+            }
+            if (tid == 0)
+                *reinterpret_cast<int4 *>(&sb.tiles[t]) = make_int4(s, p0, cnt, p.path);
+        }
+    }
+    if (ks == 0 && t == 0) {
+        // rows without an adapter, then seg_off, active and the counts
+        group_rank(key, N, wc[1], rank);
+#pragma unroll
+        for (int j = 0; j < kGroupPer; ++j)
+            if (rank[j] >= 0)
+                sb.perm[g.seg[N] + rank[j]] = j * kGroupThreads + tid;
+        group_store(g, N, sb.seg_off, sb.active, sb.counts);
+    }
 }
 
 }  // namespace
@@ -230,6 +302,19 @@ hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream
         hipLaunchKernelGGL(shrink_kernel<DT_BF16>, grid, dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(shrink_kernel<DT_F32>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_shrink(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
+                               hipStream_t stream)
+{
+    if (max_tiles <= 0 || sb.n > kGroupRows)
+        return hipErrorInvalidValue;
+    const dim3 grid(a.ks, max_tiles);
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(build_shrink_kernel<DT_BF16>, grid, dim3(256), 0, stream, a, sb);
+    else
+        hipLaunchKernelGGL(build_shrink_kernel<DT_F32>, grid, dim3(256), 0, stream, a, sb);
     return hipGetLastError();
 }
 

@@ -76,6 +76,11 @@ class GpuRun:
         lb.lora_apply(self.stack, self.y.data_ptr(), self.p.ldy, self.x.data_ptr(), self.p.ldx,
                       self.seg, self.stream)
 
+    def build_apply(self, n_rows=None):
+        n = self.p.n_rows if n_rows is None else n_rows
+        lb.lora_build_apply(self.stack, self.y.data_ptr(), self.p.ldy, self.x.data_ptr(),
+                            self.p.ldx, self.ids.data_ptr(), n, self.seg, self.stream)
+
     def segments(self):
         return lb.lora_segments_download(self.seg, self.p.n_rows, self.p.n_slots, self.stream)
 

@@ -251,14 +251,16 @@ def test_shrink_expand_split_equals_apply():
         r2.close()
 
 
-SEG_CASES = [(1, 1), (63, 3), (64, 3), (65, 3), (1000, 100), (2048, 254), (2049, 254),
-             (2048, 255), (2048, 256), (700, 300), (4097, 10), (9000, 7)]
+SEG_CASES = [(1, 1), (63, 3), (64, 3), (65, 3), (1000, 100), (1024, 8), (1025, 8),
+             (1024, 1024), (2048, 254), (2049, 254), (2048, 255), (2048, 256), (700, 300),
+             (4097, 10), (9000, 7)]
 
 
 @pytest.mark.parametrize("n,n_slots", SEG_CASES)
 def test_segments_across_builders(n, n_slots):
-    """Both segment builders (one wavefront for small batches, one 1024-thread
-    workgroup beyond) give the oracle's grouping bit for bit, bad ids included."""
+    """Both segment builders (the one-workgroup grouping up to 1024 rows, the
+    chunked one beyond) give the oracle's grouping bit for bit, bad ids
+    included, and the tile plan the policy asks for."""
     rng = np.random.default_rng(n * 7 + n_slots)
     ranks = np.full(n_slots, 8, np.int32)
     ranks[rng.random(n_slots) < 0.1] = 0

@@ -1,0 +1,131 @@
+"""lora_build_apply: grouping and apply in one call.
+
+For small batches the grouping runs inside the shrink kernel; the call must
+leave the same segments as lora_build_segments (bit for bit, checked against
+the oracle), give bit-identical y to lora_build_segments + lora_apply (the
+products run the same tile code on the same tile plan), and pass the oracle's
+float gate.  Larger batches, and an empty one, take the two-call path; the
+ragged cases cover both sides of that switch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rank_adapter_gemm_lora_amd import binding as lb
+from rank_adapter_gemm_lora_amd import synth
+from gpu_helpers import GpuRun, check_against_oracle, note
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"auto": None, "bgmv": 1 << 30, "sgmv": 1}
+WORKLOADS = ("tiny_ref", "decode_bgmv", "mlp_gate_up", "mlp_down", "many_adapter")
+
+
+def _seg_equal(got, p, what):
+    ref = oracle.build_segments(p.ids, p.n_slots, p.ranks)
+    for key in ("perm", "seg_off", "active", "counts"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{what} {key}")
+
+
+def _fused_vs_split(p, dm, what):
+    """(y, segments, tile counts) of build_apply and of build + apply."""
+    out = []
+    for fused in (True, False):
+        run = GpuRun(p, dense_min=dm)
+        try:
+            if fused:
+                run.build_apply()
+            else:
+                run.build()
+                run.apply()
+            y = run.y_host()
+            seg = run.segments()
+            tc = lb.lora_segments_tile_counts(run.seg, run.stream)
+        finally:
+            run.close()
+        out.append((y, seg, tc))
+    (yf, sf, tf), (ys, ss, ts) = out
+    np.testing.assert_array_equal(yf, ys, err_msg=f"{what}: fused y differs from split y")
+    assert tf == ts, what
+    _seg_equal(sf, p, what)
+    return yf
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_build_apply_workloads(name, path):
+    p = synth.make_workload(name)
+    note(f"build_apply {name} path={path} n={p.n_rows}")
+    y = _fused_vs_split(p, PATHS[path], f"{name}/{path}")
+    check_against_oracle(p, y, what=f"{name}/{path}/fused")
+
+
+RAGGED = [(1, 1), (15, 2), (16, 2), (17, 2), (200, 300), (255, 9), (256, 9), (257, 9),
+          (1000, 100), (1023, 5), (1024, 5), (1024, 1024), (1025, 5), (1500, 40)]
+
+
+@pytest.mark.parametrize("n,n_slots", RAGGED)
+def test_build_apply_ragged(n, n_slots):
+    """Row counts around the wavefront, tile and 1024-row limits, bad ids,
+    empty slots; bf16 and fp32."""
+    rng = np.random.default_rng(1000 + n + n_slots)
+    ranks = np.full(n_slots, 16, np.int32)
+    ranks[rng.random(n_slots) < 0.15] = 0
+    ids = rng.integers(-2, n_slots + 2, size=n).astype(np.int32)
+    for dtype in ("bf16", "f32"):
+        p = synth.make_random(11, n_rows=n, k=128, slice_d=[64, 64], n_slots=n_slots,
+                              ranks=ranks, r_max=16, dtype=dtype, ids=ids)
+        for path, dm in PATHS.items():
+            note(f"build_apply ragged n={n} slots={n_slots} {dtype} {path}")
+            y = _fused_vs_split(p, dm, f"n={n}/{dtype}/{path}")
+            check_against_oracle(p, y, what=f"n={n}/{dtype}/{path}")
+
+
+def test_build_apply_empty_and_errors():
+    p = synth.make_random(5, n_rows=32, k=64, slice_d=[64], n_slots=3, ranks=[8, 8, 8], r_max=8)
+    run = GpuRun(p, max_rows=32)
+    try:
+        note("build_apply empty batch")
+        run.build_apply(n_rows=0)
+        seg = lb.lora_segments_download(run.seg, 0, p.n_slots, run.stream)
+        assert list(seg["counts"]) == [0, 0, 0]
+        assert list(seg["seg_off"]) == [0] * (p.n_slots + 1)
+        assert list(seg["active"]) == [-1] * p.n_slots
+        np.testing.assert_array_equal(run.y_host(), p.y)
+        note("build_apply errors")
+        with pytest.raises(lb.LoraError) as e:
+            run.build_apply(n_rows=33)                      # beyond max_rows
+        assert e.value.status == lb.LORA_E_ARG
+        with pytest.raises(lb.LoraError) as e:
+            lb.lora_build_apply(run.stack, run.y.data_ptr(), p.ldy, 0, p.ldx,
+                                run.ids.data_ptr(), 32, run.seg, run.stream)   # null x
+        assert e.value.status == lb.LORA_E_ARG
+        with pytest.raises(lb.LoraError) as e:
+            lb.lora_build_apply(run.stack, run.y.data_ptr(), p.ldy, run.x.data_ptr() + 2, p.ldx,
+                                run.ids.data_ptr(), 32, run.seg, run.stream)   # misaligned x
+        assert e.value.status == lb.LORA_E_ARG
+        # nothing was enqueued by the failed calls: y is still the input
+        np.testing.assert_array_equal(run.y_host(), p.y)
+    finally:
+        run.close()
+
+
+def test_build_apply_repeated_layers():
+    """One grouping per batch, then the call repeated on new x/y (the layers of
+    a model): each result matches the oracle for its own inputs."""
+    base = synth.make_workload("decode_bgmv")
+    run = GpuRun(base)
+    try:
+        for layer in range(3):
+            p = synth.make_random(200 + layer, n_rows=base.n_rows, k=base.k, slice_d=base.slice_d,
+                                  n_slots=base.n_slots, ranks=base.ranks, r_max=base.r_max,
+                                  ids=base.ids, dtype=base.dtype)
+            p.A, p.B, p.alphas = base.A, base.B, base.alphas
+            note(f"build_apply layer {layer}")
+            run.x.copy_(torch.from_numpy(p.x.view(np.int16)).to(run.device))
+            run.y.copy_(torch.from_numpy(p.y.view(np.int16)).to(run.device))
+            run.build_apply()
+            check_against_oracle(p, run.y_host(), what=f"layer {layer}")
+    finally:
+        run.close()
