@@ -9,28 +9,31 @@
 //
 // Grid: (column chunks of 256, tile bound), over the same tile list as the
 // shrink.  Each workgroup loads its tile record (slot, first grouping
-// position, row count, path, row indices) in one round trip, issues the y
-// loads of its rows x 256 block before anything else (so the HBM round trip
-// for y overlaps the v and B staging), and stages v of its rows for the
-// slices the chunk touches, summing the shrink's k-split partials in split
-// order.  Dense tiles have 16 rows in small batches (more workgroups) and 64
-// in large ones (a B chunk then serves 64 rows).
-// Lane (g, m) of wavefront w owns the 16 columns c0 + 64 w + 16 g .. + 15 of
-// rows m, m + 16, ...  The column chunks of one tile are consecutive block
-// indices, so with 8 | chunks per row every tile of a slot meets a given chunk
-// of B on the same XCD.
+// position, row count, path, row indices) and the slot table in one round
+// trip, then puts every load of its chunk in flight at once -- the y of its
+// rows x 256 columns, the B chunk and the k-split partials of v -- so the
+// chunk costs one more round trip before the arithmetic.  v (the sum of the
+// partials in split order) and B are staged in dynamically sized LDS; y stays
+// in registers.  The column chunks of one tile are consecutive block indices,
+// so with 8 | chunks per row every tile of a slot meets a given chunk of B on
+// the same XCD.
 //
 //   SGMV tile (<= 64 rows of a dense group, bf16, 64-aligned slices), MFMA:
-//     M = 16 columns, N = 16 rows (up to 4 N-tiles), K = 32 = 16 ranks of v
-//     rounded to bf16 ("hi") then the same 16 ranks of the rounding residual
-//     ("lo"); the B operand repeats those 16 B values and is reused by every
-//     N-tile.  hi + lo carries v to about 16 significant bits, so B v keeps
-//     fp32-level accuracy on bf16 inputs.  Inside a wavefront's 64 columns,
-//     M-tile mt, index mu is column 16 (mu / 4) + 4 mt + mu % 4, so the
-//     accumulators land on the lane's 16 contiguous columns.
+//     M = 16 columns, N = 16 rows, K = 32 = 16 ranks of v rounded to bf16
+//     ("hi") then the same 16 ranks of the rounding residual ("lo"); the B
+//     operand repeats those 16 B values.  hi + lo carries v to about 16
+//     significant bits, so B v keeps fp32-level accuracy on bf16 inputs.
+//     Inside a wavefront's 64 columns, M-tile mt, index mu is column
+//     16 (mu / 4) + 4 mt + mu % 4, so the accumulators land on the lane's 16
+//     contiguous columns.  The N-tiles (16 rows each) are done one after the
+//     other with four accumulators, which keeps the register count -- and so
+//     the number of workgroups resident per CU -- where a streaming kernel
+//     needs it.  B sits in LDS as the chunk's contiguous [256 columns][rp]
+//     block, copied with 16-byte loads.
 //   BGMV tile (<= 16 rows), vector ALU: the tile's B columns are staged in LDS
-//     as bf16 rank pairs; each lane forms the bf16 hi/lo pairs of its row's v
-//     and accumulates packed bf16 dot products (v_dot2c_f32_bf16).
+//     in passes (bf16: 8 rank pairs, fp32: 8 ranks); each lane forms the bf16
+//     hi/lo pairs of its row's v and accumulates packed bf16 dot products
+//     (v_dot2c_f32_bf16), or fp32 FMAs.
 #include "device_common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -39,9 +42,7 @@ namespace lora {
 
 namespace {
 
-constexpr int kPairChunk = 16;                       // rank pairs of B per LDS pass (vector path)
-constexpr int kLdsFloats = kExpandVsFloats;          // v staging; the vector path shares it with B
-constexpr int kVecVsFloats = kLdsFloats - kPairChunk * kExpandCols;
+constexpr int kCols = kExpandCols;
 
 __device__ __forceinline__ int slice_of(const ApplyArgs &a, int64_t c)
 {
@@ -59,29 +60,64 @@ __device__ __forceinline__ void split_pair(float v0, float v1, uint32_t &hi, uin
 }
 
 // v of rows [p0, p0 + cnt) for slices [q_lo, q_lo + nq) -> vs[u][qq * r + j],
-// the sum of the k-split partials in split order.
+// the sum of the KS k-split partials in split order.  Each pass puts 8 loads
+// per thread in flight (8 / KS elements, every split of each; 16 splits go in
+// two batches of 8) before the first add, so a tile's v costs one round trip
+// per pass.  Indexes past the tile are clamped to its last element (read, not
+// stored).
+template <int KS>
+__device__ __forceinline__ void stage_v_ks(const ApplyArgs &a, int p0, int cnt, int r, int q_lo,
+                                           int nq, float *vs)
+{
+    constexpr int kL = KS < 8 ? KS : 8;              // splits per batch of loads
+    constexpr int kE = 8 / kL;                       // elements per thread per pass
+    const int SR = a.n_slices * a.r_max, pitch = nq * r, total = cnt * pitch;
+    const int64_t split = a.max_rows * (int64_t)SR;
+    const uint32_t m_pitch = div_magic(pitch), m_r = div_magic(r);   // cnt * pitch <= 2^14
+    for (int base = 0; base < total; base += kE * (int)blockDim.x) {
+        const float *src[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const int idx = min(base + e * (int)blockDim.x + (int)threadIdx.x, total - 1);
+            const int u = div_small(idx, m_pitch);
+            const int rem = idx - u * pitch;
+            const int qq = div_small(rem, m_r);
+            const int j = rem - qq * r;
+            src[e] = a.vpart + (int64_t)(p0 + u) * SR + (q_lo + qq) * a.r_max + j;
+        }
+        float sum[kE];
+#pragma unroll
+        for (int k0 = 0; k0 < KS; k0 += kL) {
+            float part[kE][kL];
+#pragma unroll
+            for (int e = 0; e < kE; ++e)
+#pragma unroll
+                for (int kk = 0; kk < kL; ++kk)
+                    part[e][kk] = src[e][(k0 + kk) * split];
+#pragma unroll
+            for (int e = 0; e < kE; ++e)
+#pragma unroll
+                for (int kk = 0; kk < kL; ++kk)
+                    sum[e] = (k0 + kk == 0) ? part[e][0] : sum[e] + part[e][kk];
+        }
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const int idx = base + e * (int)blockDim.x + (int)threadIdx.x;
+            if (idx < total)
+                vs[idx] = sum[e];
+        }
+    }
+}
+
 __device__ __forceinline__ void stage_v(const ApplyArgs &a, int p0, int cnt, int r, int q_lo,
                                         int nq, float *vs)
 {
-    const int SR = a.n_slices * a.r_max, pitch = nq * r;
-    const int64_t split = a.max_rows * (int64_t)SR;
-    const uint32_t m_pitch = div_magic(pitch), m_r = div_magic(r);   // cnt * pitch <= 2^14
-    for (int idx = threadIdx.x; idx < cnt * pitch; idx += blockDim.x) {
-        const int u = div_small(idx, m_pitch);
-        const int rem = idx - u * pitch;
-        const int qq = div_small(rem, m_r);
-        const int j = rem - qq * r;
-        const float *src = a.vpart + (int64_t)(p0 + u) * SR + (q_lo + qq) * a.r_max + j;
-        float part[kMaxKSplit];   // every split's load in flight before the first add
-#pragma unroll
-        for (int kk = 0; kk < kMaxKSplit; ++kk)
-            part[kk] = kk < a.ks ? src[kk * split] : 0.f;
-        float sum = part[0];
-#pragma unroll
-        for (int kk = 1; kk < kMaxKSplit; ++kk)
-            if (kk < a.ks)
-                sum += part[kk];
-        vs[idx] = sum;
+    switch (a.ks) {
+    case 1: stage_v_ks<1>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 2: stage_v_ks<2>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 4: stage_v_ks<4>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 8: stage_v_ks<8>(a, p0, cnt, r, q_lo, nq, vs); break;
+    default: stage_v_ks<16>(a, p0, cnt, r, q_lo, nq, vs); break;
     }
 }
 
@@ -108,67 +144,73 @@ __device__ __forceinline__ void merge16(const ApplyArgs &a, int64_t yi, bool h0,
     }
 }
 
+// ---------------------------------------------------------------- SGMV (MFMA)
+
 __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
-                                 int p0, int cnt, int64_t c0, float *vs)
+                                 int p0, int cnt, int64_t c0, float *vs, uint16_t *bs)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, m = lane & 15;
     const int n_nt = (cnt + 15) >> 4;
     const int64_t cb = c0 + 64 * wave + 16 * g;      // lane's 16 columns
     const bool in_d = cb < a.D;                      // whole 64-column blocks (slices % 64 == 0)
+    const int rp = (r + 7) & ~7, nj = (r + 15) >> 4;
 
-    // y of this lane's rows, in flight from here on
-    int64_t yi[4];
+    // y of this lane's rows
     Vec8<DT_BF16> y0[4], y1[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         const int u = 16 * nt + m;
-        yi[nt] = (int64_t)rows[min(u, cnt - 1)] * a.ldy + cb;   // rows[0 .. cnt) only
         if (nt < n_nt && u < cnt && in_d) {
-            y0[nt].load(a.y, yi[nt]);
-            y1[nt].load(a.y, yi[nt] + 8);
+            const int64_t yi = (int64_t)rows[u] * a.ldy + cb;
+            y0[nt].load(a.y, yi);
+            y1[nt].load(a.y, yi + 8);
         }
     }
-    // the first 16 ranks of B for the lane's columns, also in flight
-    const int rp = (r + 7) & ~7, nj = (r + 15) >> 4;
-    const int64_t bslot = (int64_t)s * a.b_slot_stride;
-    const int64_t cbw = c0 + 64 * wave;
-    int64_t col[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-        col[mt] = in_d ? cbw + 16 * (m >> 2) + 4 * mt + (m & 3) : 0;
-    uint4 bop[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-        bop[mt] = (in_d && 8 * (g & 1) < rp) ? load16(a.B, bslot + col[mt] * rp + 8 * (g & 1))
-                                             : make_uint4(0, 0, 0, 0);
+    // the B chunk: columns [c0, c0 + 256) of the slot are one contiguous
+    // [256][rp] block; 16-byte granules, consecutive threads on consecutive
+    // granules
+    // (granules go global -> LDS directly, 16 bytes per lane, with no register
+    // staging; thread t takes granules t, t + 256, ...  They are in flight with
+    // y while v is staged, so B, v and y share one round trip.  Granules of
+    // columns past D are not loaded: those columns are whole 64-column blocks
+    // (D % 64 == 0 on this path) whose wavefronts never read B.)
+    const int64_t bchunk = (int64_t)s * a.b_slot_stride + c0 * rp;
+    const int gpc = rp >> 3;                         // granules per column
+    const int n_gran = (int)min((int64_t)kCols, a.D - c0) * gpc;
+    for (int i = 0; i < gpc; ++i) {
+        const int e = i * kCols + threadIdx.x;
+        if (e < n_gran)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(
+                    reinterpret_cast<const uint16_t *>(a.B) + bchunk + 8 * (int64_t)e),
+                (__attribute__((address_space(3))) void *)(bs + 8 * (i * kCols + 64 * wave)), 16, 0,
+                0);
+    }
     const int q_lo = slice_of(a, c0);
-    const int nq = slice_of(a, min(c0 + kExpandCols, a.D) - 1) - q_lo + 1;
+    const int nq = slice_of(a, min(c0 + kCols, a.D) - 1) - q_lo + 1;
     const int pitch = nq * r;
     stage_v(a, p0, cnt, r, q_lo, nq, vs);
-    __syncthreads();   // v staged
+    __syncthreads();   // B and v staged
     if (!in_d)
         return;
-    const int qq = slice_of(a, cbw) - q_lo;
-
-    f32x4_t acc[4][4];   // [mt][nt]
+    const int qq = slice_of(a, c0 + 64 * wave) - q_lo;
+    int bcol[4];                                     // LDS offset of M-tile mt's column for row m
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
+        bcol[mt] = (64 * wave + 16 * (m >> 2) + 4 * mt + (m & 3)) * rp;
+
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-            acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int jc = 0; jc < nj; ++jc) {
-        const int jo = jc * 16 + 8 * (g & 1);
-        if (jc > 0) {
+    for (int nt = 0; nt < 4; ++nt) {
+        if (nt >= n_nt)
+            continue;   // (uniform) fully unrolled: y0[nt] / y1[nt] stay in registers
+        const int u = 16 * nt + m;
+        f32x4_t acc[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                bop[mt] = jo < rp ? load16(a.B, bslot + col[mt] * rp + jo) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            if (nt >= n_nt)
-                break;
-            const int u = 16 * nt + m;
+        for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int jc = 0; jc < nj; ++jc) {
+            const int jo = jc * 16 + 8 * (g & 1);
             float f[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -182,29 +224,29 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
             vop.z = pack_bf16x2(f[4], f[5]);
             vop.w = pack_bf16x2(f[6], f[7]);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                acc[mt][nt] = mfma_bf16_16x16x32(bop[mt], vop, acc[mt][nt]);
+            for (int mt = 0; mt < 4; ++mt) {
+                const uint4 bop = jo < rp ? *reinterpret_cast<const uint4 *>(bs + bcol[mt] + jo)
+                                          : make_uint4(0, 0, 0, 0);
+                acc[mt] = mfma_bf16_16x16x32(bop, vop, acc[mt]);
+            }
         }
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        if (nt >= n_nt)
-            break;
-        if (16 * nt + m < cnt) {
+        if (u < cnt) {
             float f[16];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    f[4 * mt + i] = acc[mt][nt][i];
-            merge16<DT_BF16>(a, yi[nt], true, true, y0[nt], y1[nt], scale, f);
+                    f[4 * mt + i] = acc[mt][i];
+            merge16<DT_BF16>(a, (int64_t)rows[u] * a.ldy + cb, true, true, y0[nt], y1[nt], scale,
+                             f);
         }
     }
 }
 
-// One pass of B for the vector path: the 256 columns' ranks [4 quad .. 4 quad + 3]
-// of pass base j0 (bf16: rank pairs 2 (pc + 4 quad) .., fp32: ranks j0 + 4 quad ..),
-// as 16-byte words; thread c owns column c0 + c.
+// ------------------------------------------------------------ BGMV (vector)
+
+// One 16-byte word of a B pass: ranks [elem0, elem0 + 8) (bf16) or
+// [elem0, elem0 + 4) (fp32) of column gc; zero past D or past rp.
 template <int DT>
 __device__ __forceinline__ uint4 b_word(const ApplyArgs &a, int64_t bslot, int64_t gc, int rp,
                                         int elem0)
@@ -220,14 +262,13 @@ __device__ __forceinline__ uint4 b_word(const ApplyArgs &a, int64_t bslot, int64
 
 template <int DT>
 __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
-                                 int p0, int cnt, int64_t c0, float *lds)
+                                 int p0, int cnt, int64_t c0, float *vs, uint32_t *bsh)
 {
-    // per pass: bf16 16 rank pairs (4 words of 4 pairs per column), fp32 16 ranks
-    // (4 words of 4 ranks per column)
-    constexpr int kWords = 4;
-    constexpr int kPassElems = DT == DT_BF16 ? 2 * kPairChunk : 16;
-    float *vs = lds;
-    uint32_t *bsh = reinterpret_cast<uint32_t *>(lds + kVecVsFloats);   // [word lane][col]
+    // a pass: 2 words per column = 8 rank pairs (bf16) or 8 ranks (fp32);
+    // bsh[word lane w][column] holds rank pair / rank (pass base + w)
+    constexpr int kWords = 2;
+    constexpr int kElemsPerWord = DT == DT_BF16 ? 8 : 4;
+    constexpr int kPassElems = kWords * kElemsPerWord;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, m = lane & 15;
     const bool row_ok = m < cnt;
@@ -243,7 +284,6 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     const int rp = (r + 7) & ~7;
     const int64_t bslot = (int64_t)s * a.b_slot_stride;
     const int64_t gcol = c0 + threadIdx.x;            // the column this thread stages
-    constexpr int kElemsPerWord = DT == DT_BF16 ? 8 : 4;
     // the first pass of B in flight while v is staged
     uint4 w[kWords];
 #pragma unroll
@@ -251,7 +291,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
         w[q4] = b_word<DT>(a, bslot, gcol, rp, kElemsPerWord * q4);
 
     const int q_lo = slice_of(a, c0);
-    const int nq = slice_of(a, min(c0 + kExpandCols, a.D) - 1) - q_lo + 1;
+    const int nq = slice_of(a, min(c0 + kCols, a.D) - 1) - q_lo + 1;
     stage_v(a, p0, cnt, r, q_lo, nq, vs);
     const int pitch = nq * r;
     const int cl = 64 * wave + 16 * g;               // lane's first column in the chunk
@@ -273,14 +313,14 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
         }
 #pragma unroll
         for (int q4 = 0; q4 < kWords; ++q4) {
-            bsh[(4 * q4 + 0) * kExpandCols + threadIdx.x] = w[q4].x;
-            bsh[(4 * q4 + 1) * kExpandCols + threadIdx.x] = w[q4].y;
-            bsh[(4 * q4 + 2) * kExpandCols + threadIdx.x] = w[q4].z;
-            bsh[(4 * q4 + 3) * kExpandCols + threadIdx.x] = w[q4].w;
+            bsh[(4 * q4 + 0) * kCols + threadIdx.x] = w[q4].x;
+            bsh[(4 * q4 + 1) * kCols + threadIdx.x] = w[q4].y;
+            bsh[(4 * q4 + 2) * kCols + threadIdx.x] = w[q4].z;
+            bsh[(4 * q4 + 3) * kCols + threadIdx.x] = w[q4].w;
         }
         __syncthreads();   // v and this pass of B staged
         if constexpr (DT == DT_BF16) {
-            const int np = min(kPairChunk, (rp - j0) / 2);
+            const int np = min(kPassElems, rp - j0) / 2;
             for (int pp = 0; pp < np; ++pp) {
                 const int j = j0 + 2 * pp;
 #pragma unroll
@@ -290,8 +330,8 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                     const float v1 = (row_ok && j + 1 < r) ? vr[j + 1] : 0.f;
                     uint32_t hi, lo;
                     split_pair(v0, v1, hi, lo);
-                    const uint4 b0 = *reinterpret_cast<const uint4 *>(&bsh[pp * kExpandCols + cl + 8 * hh]);
-                    const uint4 b1 = *reinterpret_cast<const uint4 *>(&bsh[pp * kExpandCols + cl + 8 * hh + 4]);
+                    const uint4 b0 = *reinterpret_cast<const uint4 *>(&bsh[pp * kCols + cl + 8 * hh]);
+                    const uint4 b1 = *reinterpret_cast<const uint4 *>(&bsh[pp * kCols + cl + 8 * hh + 4]);
                     const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
                     for (int c = 0; c < 8; ++c) {
@@ -302,13 +342,13 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
             }
         } else {
             const float *bf = reinterpret_cast<const float *>(bsh);   // [jj][col]
-            for (int jj = 0; jj < 16 && j0 + jj < r; ++jj) {
+            for (int jj = 0; jj < kPassElems && j0 + jj < r; ++jj) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const float vj = row_ok ? vs[m * pitch + qh[hh] * r + j0 + jj] : 0.f;
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
-                        acc[8 * hh + c] = fmaf(bf[jj * kExpandCols + cl + 8 * hh + c], vj,
+                        acc[8 * hh + c] = fmaf(bf[jj * kCols + cl + 8 * hh + c], vj,
                                                acc[8 * hh + c]);
                 }
             }
@@ -318,46 +358,54 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     merge16<DT>(a, yi, h0, h1, y0, y1, scale, acc);
 }
 
+// Dynamic LDS: [rows: 64 int][slot table: rank, scale (when n_slots <= 256)]
+// [v staging at lds_v_off][B staging at lds_b_off]; the host sizes it.
 template <int DT>
 __global__ __launch_bounds__(256) void expand_kernel(ApplyArgs a)
 {
-    __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
-    __shared__ int32_t rows[kSgmvTileRows];
-    __shared__ int32_t srank[LORA_MAX_SLOTS];
-    __shared__ float sscale[LORA_MAX_SLOTS];
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    int32_t *rows = reinterpret_cast<int32_t *>(lds);
+    int32_t *srank = reinterpret_cast<int32_t *>(lds + kExpandLdsTable);
+    float *sscale = reinterpret_cast<float *>(lds + kExpandLdsTable + 4 * kExpandTableSlots);
+    float *vs = reinterpret_cast<float *>(lds + a.lds_v_off);
+    unsigned char *bst = lds + a.lds_b_off;
     const int t = blockIdx.y;
     const ShrinkTile *T = a.tiles + t;
     // header, row indices, counts and the slot table in one round trip
     const int4 h = *reinterpret_cast<const int4 *>(T);
     const int32_t my_row = threadIdx.x < kSgmvTileRows ? T->rows[threadIdx.x] : 0;
     const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
-    for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x) {
-        srank[e] = a.rank[e];
-        sscale[e] = a.scale[e];
+    const bool table = a.n_slots <= kExpandTableSlots;
+    if (table) {
+        for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x) {
+            srank[e] = a.rank[e];
+            sscale[e] = a.scale[e];
+        }
     }
     if (t >= n_tiles)
         return;
-    const int64_t c0 = (int64_t)blockIdx.x * kExpandCols;
+    const int64_t c0 = (int64_t)blockIdx.x * kCols;
     if (c0 >= a.D)
         return;
     const int s = h.x, p0 = h.y, cnt = h.z;
     if (threadIdx.x < kSgmvTileRows)
         rows[threadIdx.x] = my_row;
     __syncthreads();
-    const int r = srank[s];
-    const float scale = sscale[s];
+    const int r = table ? srank[s] : a.rank[s];
+    const float scale = table ? sscale[s] : a.scale[s];
     if (r == 0)
         return;   // slot emptied since the grouping was built: rows stay untouched
     if constexpr (DT == DT_BF16) {
         if (h.w == kTileSgmv && a.mfma_ok) {
-            sgmv_expand_tile(a, rows, s, r, scale, p0, cnt, c0, lds);
+            sgmv_expand_tile(a, rows, s, r, scale, p0, cnt, c0, vs,
+                             reinterpret_cast<uint16_t *>(bst));
             return;
         }
     }
     // BGMV tile, or a dense tile of a stack without the MFMA path
     for (int sub = 0; sub < cnt; sub += kBgmvTileRows) {
         bgmv_expand_tile<DT>(a, rows + sub, s, r, scale, p0 + sub, min(kBgmvTileRows, cnt - sub),
-                             c0, lds);
+                             c0, vs, reinterpret_cast<uint32_t *>(bst));
         __syncthreads();   // LDS is restaged by the next sub-tile
     }
 }
@@ -368,11 +416,11 @@ hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream
 {
     if (max_tiles <= 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((a.D + kExpandCols - 1) / kExpandCols), max_tiles);
+    const dim3 grid((unsigned)((a.D + kCols - 1) / kCols), max_tiles);
     if (dtype == DT_BF16)
-        hipLaunchKernelGGL(expand_kernel<DT_BF16>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(expand_kernel<DT_BF16>, grid, dim3(256), a.lds_bytes, stream, a);
     else
-        hipLaunchKernelGGL(expand_kernel<DT_F32>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(expand_kernel<DT_F32>, grid, dim3(256), a.lds_bytes, stream, a);
     return hipGetLastError();
 }
 

@@ -16,7 +16,9 @@ enum : int { DT_F32 = 0, DT_BF16 = 1 };   // element types of x, y and the pool
 constexpr int kBgmvTileRows = 16;   // rows per BGMV shrink tile (small groups)
 constexpr int kSgmvTileRows = 64;   // rows per SGMV shrink tile (dense groups, MFMA)
 constexpr int kExpandCols = 256;    // output columns per expand workgroup
-constexpr int kExpandVsFloats = 8192;  // LDS floats of v staging in the expand
+constexpr int kExpandLdsTable = 256;   // expand LDS: row indices first, then the slot table
+constexpr int kExpandTableSlots = 256; // slot table in LDS up to this many slots
+constexpr int kExpandLdsMax = 65536;   // dynamic LDS of one expand workgroup, at most
 constexpr int kTileBgmv = 0;
 constexpr int kTileSgmv = 1;
 constexpr int kMaxKSplit = 16;      // most k-splits of one shrink
@@ -73,6 +75,9 @@ struct ApplyArgs {
     int64_t max_rows;
     int ks;                    // k-splits of the shrink
     int mfma_ok;               // dense tiles may use MFMA (bf16, 64-aligned slices)
+    int lds_v_off;             // expand: dynamic LDS byte offsets of v and B staging
+    int lds_b_off;
+    int lds_bytes;             // expand: dynamic LDS bytes
     // batch
     const int32_t *counts;
     const ShrinkTile *tiles;

@@ -88,17 +88,9 @@ void free_segments(lora_segments *seg)
     delete seg;
 }
 
-// MFMA tiles need bf16, slices made of whole 64-column blocks, and the v of a
-// 64-row tile for the slices one 256-column chunk touches must fit the
-// expand's LDS; otherwise the dense tiles of a batch are served by the vector
-// code.
-bool stack_has_mfma_path(const lora_stack *st)
+// Most slices one 256-column expand chunk touches.
+int expand_nq_max(const lora_stack *st)
 {
-    if (st->dtype != LORA_BF16)
-        return false;
-    for (int q = 0; q < st->n_slices; ++q)
-        if (st->slice_d[q] % 64 != 0)
-            return false;
     int nq_max = 1;
     for (int64_t c0 = 0; c0 < st->D; c0 += kExpandCols) {
         const int64_t c1 = std::min<int64_t>(c0 + kExpandCols, st->D) - 1;
@@ -109,7 +101,41 @@ bool stack_has_mfma_path(const lora_stack *st)
             ++q1;
         nq_max = std::max(nq_max, q1 - q0 + 1);
     }
-    return (int64_t)kSgmvTileRows * nq_max * st->r_max <= kExpandVsFloats;
+    return nq_max;
+}
+
+// Dynamic LDS of the expand: row indices, the slot table (few slots), v of a
+// tile for the slices of one chunk, and B (a whole [256][rp] chunk for MFMA
+// tiles, one 8 KB pass for vector tiles).
+struct ExpandLds {
+    int v_off, b_off, bytes;
+};
+
+ExpandLds expand_lds(const lora_stack *st, bool mfma)
+{
+    const int64_t table = st->n_slots <= kExpandTableSlots ? 8 * kExpandTableSlots : 0;
+    const int64_t rows = mfma ? kSgmvTileRows : kBgmvTileRows;
+    const int64_t v_bytes = round_up(rows * expand_nq_max(st) * st->r_max * 4, 16);
+    const int64_t b_bytes = std::max<int64_t>(8 * kExpandCols * 4,
+                                              mfma ? (int64_t)kExpandCols * st->rp_max * 2 : 0);
+    ExpandLds l;
+    l.v_off = (int)(kExpandLdsTable + table);
+    l.b_off = (int)(l.v_off + v_bytes);
+    l.bytes = (int)(l.b_off + b_bytes);
+    return l;
+}
+
+// MFMA tiles need bf16, slices made of whole 64-column blocks, and the v of a
+// 64-row tile plus a [256][rp] chunk of B within the expand's LDS budget;
+// otherwise the dense tiles of a batch are served by the vector code.
+bool stack_has_mfma_path(const lora_stack *st)
+{
+    if (st->dtype != LORA_BF16)
+        return false;
+    for (int q = 0; q < st->n_slices; ++q)
+        if (st->slice_d[q] % 64 != 0)
+            return false;
+    return expand_lds(st, true).bytes <= kExpandLdsMax;
 }
 
 lora_status check_apply_common(const lora_stack *st, const lora_segments *seg)
@@ -144,6 +170,10 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     a.max_rows = st->max_rows;
     a.ks = choose_ks(st->k, seg->n_rows);
     a.mfma_ok = stack_has_mfma_path(st) ? 1 : 0;
+    const ExpandLds l = expand_lds(st, a.mfma_ok != 0);
+    a.lds_v_off = l.v_off;
+    a.lds_b_off = l.b_off;
+    a.lds_bytes = l.bytes;
     a.counts = seg->counts;
     a.tiles = seg->tiles;
     return a;
