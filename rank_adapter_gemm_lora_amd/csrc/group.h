@@ -33,7 +33,7 @@ struct GroupLds {
     int bbg[kGroupBuckets];    // first BGMV tile of each slot, not counting the SGMV tiles
     int apos[kGroupBuckets];   // position of each slot in the active list
     int rank[kGroupBuckets];   // slot ranks (0: no adapter)
-    int2 tmp[kGroupWaves];
+    int4 tmp[kGroupWaves];
     int n_sg, n_bg, n_act, n_bad;
 };
 
@@ -114,82 +114,76 @@ __device__ __forceinline__ int wave_scan_dpp(int x)
 }
 
 // Scan of the buckets: group offsets, the SGMV and BGMV tile bases of every
-// slot and the positions in the active list, all into LDS.  Four counts per
-// bucket travel as two words of two 16-bit halves (rows | active slots, SGMV |
-// BGMV tiles): every prefix is at most 1024 + 1025, so halves never carry.
+// slot and the positions in the active list, all into LDS, from g.hist.
 __device__ __forceinline__ void group_scan(GroupLds &g, int N, int dense_min, int sg_shift)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int NB = N + 1;
-    int2 carry = make_int2(0, 0);
+    int4 carry = make_int4(0, 0, 0, 0);
     // one pass covers 4 buckets per thread; with few slots wavefront 0 alone
     // scans them and no barrier is needed inside the pass
     const bool one_wave = NB <= 256;
     const int per_pass = one_wave ? 256 : 4 * kGroupThreads;
     for (int e0 = 0; e0 < NB; e0 += per_pass) {
         const bool part = !one_wave || wave == 0;
-        int2 v[4];
-        int2 sum = make_int2(0, 0);
+        int4 v[4];   // (rows, active, SGMV tiles, BGMV tiles) per bucket
+        int4 sum = make_int4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int e = e0 + 4 * tid + u;
-            v[u] = make_int2(0, 0);
+            v[u] = make_int4(0, 0, 0, 0);
             if (part && e < NB) {
                 const int c = g.hist[e];
-                int act = 0, sg = 0, bg = 0;
+                v[u].x = c;
                 if (e < N && c > 0) {
                     const bool dn = c >= dense_min;
-                    sg = dn ? (c + (1 << sg_shift) - 1) >> sg_shift : 0;
-                    bg = dn ? 0 : (c + kBgmvTileRows - 1) >> 4;
-                    act = 1;
+                    v[u].y = 1;
+                    v[u].z = dn ? (c + (1 << sg_shift) - 1) >> sg_shift : 0;
+                    v[u].w = dn ? 0 : (c + kBgmvTileRows - 1) >> 4;
                 }
-                v[u] = make_int2(c | (act << 16), sg | (bg << 16));
             }
-            sum.x += v[u].x;
-            sum.y += v[u].y;
+            sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w;
         }
-        const int2 inc = make_int2(wave_scan_dpp(sum.x), wave_scan_dpp(sum.y));
-        int2 base = make_int2(0, 0), tot;
+        const int4 inc = make_int4(wave_scan_dpp(sum.x), wave_scan_dpp(sum.y), wave_scan_dpp(sum.z),
+                                   wave_scan_dpp(sum.w));
+        int4 base = make_int4(0, 0, 0, 0), tot;
         if (!one_wave) {
             if (lane == 63)
                 g.tmp[wave] = inc;
             __syncthreads();
-            tot = make_int2(0, 0);
+            tot = make_int4(0, 0, 0, 0);
 #pragma unroll
             for (int u = 0; u < kGroupWaves; ++u) {
-                const int2 t = g.tmp[u];
+                const int4 t = g.tmp[u];
                 if (u < wave) {
-                    base.x += t.x;
-                    base.y += t.y;
+                    base.x += t.x; base.y += t.y; base.z += t.z; base.w += t.w;
                 }
-                tot.x += t.x;
-                tot.y += t.y;
+                tot.x += t.x; tot.y += t.y; tot.z += t.z; tot.w += t.w;
             }
             __syncthreads();
         } else {
-            tot = make_int2(__builtin_amdgcn_readlane(inc.x, 63),
-                            __builtin_amdgcn_readlane(inc.y, 63));
+            tot = make_int4(__builtin_amdgcn_readlane(inc.x, 63), __builtin_amdgcn_readlane(inc.y, 63),
+                            __builtin_amdgcn_readlane(inc.z, 63), __builtin_amdgcn_readlane(inc.w, 63));
         }
-        int2 ex = make_int2(carry.x + base.x + inc.x - sum.x, carry.y + base.y + inc.y - sum.y);
+        int4 ex = make_int4(carry.x + base.x + inc.x - sum.x, carry.y + base.y + inc.y - sum.y,
+                            carry.z + base.z + inc.z - sum.z, carry.w + base.w + inc.w - sum.w);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int e = e0 + 4 * tid + u;
             if (part && e < NB) {
-                g.seg[e] = ex.x & 0xffff;
-                g.apos[e] = ex.x >> 16;
-                g.bsg[e] = ex.y & 0xffff;
-                g.bbg[e] = ex.y >> 16;
+                g.seg[e] = ex.x;
+                g.apos[e] = ex.y;
+                g.bsg[e] = ex.z;
+                g.bbg[e] = ex.w;
             }
-            ex.x += v[u].x;
-            ex.y += v[u].y;
+            ex.x += v[u].x; ex.y += v[u].y; ex.z += v[u].z; ex.w += v[u].w;
         }
-        carry.x += tot.x;
-        carry.y += tot.y;
+        carry.x += tot.x; carry.y += tot.y; carry.z += tot.z; carry.w += tot.w;
     }
     if (tid == 0) {
-        g.n_sg = carry.y & 0xffff;
-        g.n_bg = carry.y >> 16;
-        g.n_act = carry.x >> 16;
+        g.n_act = carry.y;
+        g.n_sg = carry.z;
+        g.n_bg = carry.w;
     }
     __syncthreads();
 }

@@ -23,6 +23,7 @@ constexpr int kTileBgmv = 0;
 constexpr int kTileSgmv = 1;
 constexpr int kMaxKSplit = 16;      // most k-splits of one shrink
 constexpr int kMaxSliceRank = 256;  // n_slices * r_max bound (LDS staging of v)
+constexpr int kChunkRows = 256;     // rows per chunk of the large-batch grouping
 
 // Device counts written by the segment builder.
 enum : int {
@@ -54,6 +55,11 @@ struct SegBuildArgs {
     int32_t *active;
     int32_t *counts;
     lora::ShrinkTile *tiles;
+    // scratch of the chunked grouping (batches above 1024 rows)
+    int32_t *keys;        // [max_rows] bucket of each row
+    int32_t *chunk;       // [chunks][n_slots + 1] histograms, then their prefixes
+    int32_t *chunk_bad;   // [chunks] bad ids per chunk
+    int4 *binfo;          // [n_slots + 1] group offset, first tile, tile shift, path
 };
 
 // Everything a shrink or expand kernel reads about the stack and the batch.
@@ -133,6 +139,10 @@ struct lora_segments {
     int32_t *active;
     int32_t *counts;
     lora::ShrinkTile *tiles;
+    int32_t *keys;
+    int32_t *chunk;
+    int32_t *chunk_bad;
+    int4 *binfo;
     // state of the last build
     int built;
     int64_t n_rows;

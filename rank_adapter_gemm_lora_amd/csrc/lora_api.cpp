@@ -85,6 +85,10 @@ void free_segments(lora_segments *seg)
     (void)hipFree(seg->active);
     (void)hipFree(seg->counts);
     (void)hipFree(seg->tiles);
+    (void)hipFree(seg->keys);
+    (void)hipFree(seg->chunk);
+    (void)hipFree(seg->chunk_bad);
+    (void)hipFree(seg->binfo);
     delete seg;
 }
 
@@ -367,6 +371,8 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
         return LORA_E_NOMEM;
     seg->perm = seg->seg_off = seg->active = seg->counts = nullptr;
     seg->tiles = nullptr;
+    seg->keys = seg->chunk = seg->chunk_bad = nullptr;
+    seg->binfo = nullptr;
     if (hipGetDevice(&seg->device) != hipSuccess) {
         delete seg;
         return LORA_E_HIP;
@@ -384,6 +390,11 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->active), sizeof(int32_t) * n_slots);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->counts), sizeof(int32_t) * kCntSlots);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->tiles), sizeof(ShrinkTile) * seg->max_tiles);
+    const int64_t n_chunks = (max_rows + kChunkRows - 1) / kChunkRows;
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->keys), sizeof(int32_t) * max_rows);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->chunk), sizeof(int32_t) * n_chunks * (n_slots + 1));
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->chunk_bad), sizeof(int32_t) * n_chunks);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->binfo), sizeof(int4) * (n_slots + 1));
     if (e == hipSuccess) e = hipMemset(seg->counts, 0, sizeof(int32_t) * kCntSlots);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -442,6 +453,10 @@ SegBuildArgs make_seg_args(const lora_stack *st, const int32_t *ids, int64_t n_r
     a.active = seg->active;
     a.counts = seg->counts;
     a.tiles = seg->tiles;
+    a.keys = seg->keys;
+    a.chunk = seg->chunk;
+    a.chunk_bad = seg->chunk_bad;
+    a.binfo = seg->binfo;
     return a;
 }
 

@@ -7,9 +7,10 @@
 // grouping the rows by their adapter id comes before add_shrink / add_expand.
 //
 // The grouping is a stable counting sort with n_slots + 1 buckets (bucket
-// n_slots collects the rows without a valid adapter); the kernel below says
-// how it is laid out on the GPU.  The launch shape depends only on the slot
-// count, never on the ids.
+// n_slots collects the rows without a valid adapter).  Two layouts: one
+// workgroup per bucket for batches of at most 1024 rows (group.h), and a
+// chunked count / scan / place for larger ones.  Launch shapes depend only on
+// n and the slot count, never on the ids.
 #include "device_common.h"
 #include "group.h"
 #include "internal.h"
@@ -18,254 +19,182 @@ namespace lora {
 
 namespace {
 
-// Last index s in [0, n) with base[s] <= v (base nondecreasing, base[0] <= v).
-__device__ __forceinline__ int upper_slot(const int *base, int n, int v)
-{
-    int lo = 0, hi = n;   // answer in [lo, hi)
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (base[mid] <= v)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    return lo;
-}
-
 // ---------------------------------------------------------------------------
-// One workgroup per bucket.  Every workgroup reads all ids and the slot table,
-// builds the bucket histogram and its scan in LDS (cheap at these sizes), then
-// writes only the rows of its own bucket.  Rows are taken in chunks of
-// kParRows, thread t owning rows [kParPer t, kParPer (t + 1)) of a chunk, so a
-// block scan of per-thread match counts (plus the count carried from earlier
-// chunks) gives every row its rank in index order: the sort is stable.
-// Workgroup 0 also writes seg_off, active, counts and the tile headers.  All
-// workgroups run at once and none waits on another.
+// Larger batches: a chunked counting sort in three launches over chunks of 256
+// rows (one row per thread).
+//   count: each chunk's histogram over the buckets (and its bad ids); the row
+//          keys are kept for the placement.
+//   scan:  one workgroup turns the chunk histograms into, per bucket, the
+//          exclusive prefix over chunks (in place), the group offsets, the tile
+//          plan, the active list and the counts, and writes every tile header.
+//   place: each chunk puts its rows at group offset + chunk prefix + rank among
+//          the chunk's earlier rows of the same bucket, so the order inside a
+//          group is the row order: the sort is stable.
+// Every launch's shape depends only on n and the slot count.
 
-constexpr int kParThreads = 256;
-constexpr int kParPer = 16;                           // rows per thread per chunk
-constexpr int kParRows = kParThreads * kParPer;       // 4096 rows per chunk
-constexpr int kParBuckets = LORA_MAX_SLOTS + 1;
+constexpr int kChunk = kChunkRows;
 
-// Exclusive scan of one int4 per thread (component-wise) over 256 threads.
-__device__ int4 scan256x4(int4 v, int4 *tmp, int4 *total)
+__device__ __forceinline__ int chunk_key(const SegBuildArgs &a, int64_t i, int N, int &bad)
 {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int4 x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int4 y = make_int4(__shfl_up(x.x, o), __shfl_up(x.y, o), __shfl_up(x.z, o),
-                                 __shfl_up(x.w, o));
-        if (lane >= o) {
-            x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
-        }
-    }
-    if (lane == 63)
-        tmp[w] = x;
-    __syncthreads();
-    int4 base = make_int4(0, 0, 0, 0), tot = make_int4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int4 t = tmp[u];
-        if (u < w) {
-            base.x += t.x; base.y += t.y; base.z += t.z; base.w += t.w;
-        }
-        tot.x += t.x; tot.y += t.y; tot.z += t.z; tot.w += t.w;
-    }
-    *total = tot;
-    __syncthreads();
-    return make_int4(base.x + x.x - v.x, base.y + x.y - v.y, base.z + x.z - v.z, base.w + x.w - v.w);
-}
-
-// ids of rows [r0, r0 + kParPer) (-1 past the batch end).
-__device__ __forceinline__ void load_ids(const SegBuildArgs &a, int64_t r0, int32_t (&id)[kParPer])
-{
-#pragma unroll
-    for (int j = 0; j < kParPer; ++j)
-        id[j] = r0 + j < a.n ? a.ids[r0 + j] : -1;
-}
-
-// Bucket key of row i with id `id`: the slot when it holds an adapter, n_slots
-// otherwise, -1 past the batch end.  Branch-free: the table lookup is always
-// made, at a clamped (in-bounds) index.
-__device__ __forceinline__ int row_key(int64_t i, int64_t n, int32_t id, int N, const uint8_t *ok,
-                                       int &bad)
-{
-    const bool in = i < n;
+    if (i >= a.n)
+        return -1;
+    const int32_t id = a.ids[i];
     const bool in_range = (uint32_t)id < (uint32_t)N;
-    const int look = ok[in_range ? id : 0];
-    const bool valid = in_range && look != 0;
-    bad += (in && !valid && id != -1) ? 1 : 0;
-    return in ? (valid ? id : N) : -1;
+    const bool valid = in_range && a.slot_rank[in_range ? id : 0] > 0;
+    bad = (!valid && id != -1) ? 1 : 0;
+    return valid ? id : N;
 }
 
-__global__ __launch_bounds__(kParThreads) void seg_build_kernel(SegBuildArgs a)
+__global__ __launch_bounds__(kChunk) void seg_count_kernel(SegBuildArgs a)
 {
-    __shared__ int hist[kParBuckets];    // rows per bucket
-    __shared__ int seg[kParBuckets];     // seg_off
-    __shared__ int bsg[kParBuckets];     // first SGMV tile of each slot
-    __shared__ int bbg[kParBuckets];     // first BGMV tile (without the SGMV count)
-    __shared__ uint8_t ok[kParBuckets];
-    __shared__ int4 tmp[4];
-
-    const int b = blockIdx.x;            // the bucket this workgroup places
-    const int N = a.n_slots, NB = N + 1;
-    const int tid = threadIdx.x;
-    const int64_t n = a.n;
-    const int sg_shift = a.sgmv_rows == 64 ? 6 : 4;   // dense tiles: 16 or 64 rows
-
-    // the first chunk's ids in flight while the slot table is copied to LDS;
-    // a one-chunk batch keeps them in registers for both passes
-    int32_t id0[kParPer];
-    load_ids(a, (int64_t)tid * kParPer, id0);
-    for (int e = tid; e < NB; e += kParThreads) {
-        hist[e] = 0;
-        ok[e] = (e < N && a.slot_rank[e] > 0) ? 1 : 0;
-    }
-    __syncthreads();
-
-    // histogram; runs of equal keys are merged inside the thread; the next
-    // chunk's ids are in flight while this one is counted
+    __shared__ int hist[kGroupBuckets];
+    __shared__ int nbad;
+    const int N = a.n_slots, NB = N + 1, c = blockIdx.x, tid = threadIdx.x;
+    const int64_t i = (int64_t)c * kChunk + tid;
     int bad = 0;
-    int32_t idn[kParPer];
-#pragma unroll
-    for (int j = 0; j < kParPer; ++j)
-        idn[j] = id0[j];
-    for (int64_t c0 = 0; c0 < n; c0 += kParRows) {
-        const int64_t r0 = c0 + (int64_t)tid * kParPer;
-        int32_t id[kParPer];
-#pragma unroll
-        for (int j = 0; j < kParPer; ++j)
-            id[j] = idn[j];
-        if (c0 + kParRows < n)
-            load_ids(a, r0 + kParRows, idn);
-        int run_key = -1, run_len = 0;
-#pragma unroll
-        for (int j = 0; j < kParPer; ++j) {
-            const int key = row_key(r0 + j, n, id[j], N, ok, bad);
-            if (key != run_key) {
-                if (run_len > 0)
-                    atomicAdd(&hist[run_key], run_len);
-                run_key = key;
-                run_len = 0;
-            }
-            run_len += key >= 0 ? 1 : 0;
-        }
-        if (run_len > 0)
-            atomicAdd(&hist[run_key], run_len);
-    }
+    const int key = chunk_key(a, i, N, bad);
+    for (int e = tid; e < NB; e += kChunk)
+        hist[e] = 0;
+    if (tid == 0)
+        nbad = 0;
     __syncthreads();
+    if (key >= 0) {
+        atomicAdd(&hist[key], 1);
+        a.keys[i] = key;
+    }
+    if (bad)
+        atomicAdd(&nbad, 1);
+    __syncthreads();
+    for (int e = tid; e < NB; e += kChunk)
+        a.chunk[(int64_t)c * NB + e] = hist[e];
+    if (tid == 0)
+        a.chunk_bad[c] = nbad;
+}
 
-    // scan of the buckets, 4 per thread per pass: (rows, SGMV tiles, BGMV tiles, active)
-    int4 carry = make_int4(0, 0, 0, 0);
-    for (int e0 = 0; e0 < NB; e0 += 4 * kParThreads) {
-        int4 v4[4];
-        int4 sum = make_int4(0, 0, 0, 0);
+__global__ __launch_bounds__(kGroupThreads) void seg_scan_kernel(SegBuildArgs a, int n_chunks)
+{
+    __shared__ GroupLds g;
+    const int N = a.n_slots, NB = N + 1, tid = threadIdx.x;
+    const int sg_shift = a.sgmv_rows == 64 ? 6 : 4;
+    // per bucket: exclusive prefix over the chunks (written back) and the
+    // total.  tpb threads (a power of two inside one wavefront) share a bucket,
+    // each taking a run of consecutive chunks; their sums are scanned across
+    // the group with shuffles.  Loads go out in batches of kBat.
+    constexpr int kBat = 16;
+    int tpb = 1;
+    while (tpb < 64 && 2 * tpb * NB <= kGroupThreads)
+        tpb *= 2;
+    const int per = (n_chunks + tpb - 1) / tpb;
+    for (int b0 = 0; b0 < NB; b0 += kGroupThreads / tpb) {
+        const int b = b0 + tid / tpb, sub = tid % tpb;
+        const bool act = b < NB;
+        const int c_begin = min(sub * per, n_chunks), c_end = min(c_begin + per, n_chunks);
+        int32_t *col = a.chunk + (act ? b : 0);
+        int v[kBat];
+        int local = 0;
+        for (int c0 = c_begin; c0 < c_end; c0 += kBat) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = e0 + 4 * tid + u;
-            v4[u] = make_int4(0, 0, 0, 0);
-            if (e < NB) {
-                const int c = hist[e];
-                v4[u].x = c;
-                if (e < N && c > 0) {
-                    const bool dn = c >= a.dense_min;
-                    v4[u].y = dn ? (c + (1 << sg_shift) - 1) >> sg_shift : 0;
-                    v4[u].z = dn ? 0 : (c + kBgmvTileRows - 1) >> 4;
-                    v4[u].w = 1;
+            for (int j = 0; j < kBat; ++j)
+                v[j] = (act && c0 + j < c_end) ? col[(int64_t)(c0 + j) * NB] : 0;
+#pragma unroll
+            for (int j = 0; j < kBat; ++j)
+                local += v[j];
+        }
+        int incl = local;
+        for (int o = 1; o < tpb; o <<= 1) {
+            const int y = __shfl_up(incl, o, tpb);
+            if (sub >= o)
+                incl += y;
+        }
+        int run = incl - local;
+        for (int c0 = c_begin; c0 < c_end; c0 += kBat) {
+            if (c_end - c_begin > kBat) {   // values of this batch no longer in registers
+#pragma unroll
+                for (int j = 0; j < kBat; ++j)
+                    v[j] = (act && c0 + j < c_end) ? col[(int64_t)(c0 + j) * NB] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < kBat; ++j) {
+                if (act && c0 + j < c_end) {
+                    col[(int64_t)(c0 + j) * NB] = run;
+                    run += v[j];
                 }
             }
-            sum.x += v4[u].x; sum.y += v4[u].y; sum.z += v4[u].z; sum.w += v4[u].w;
         }
-        int4 tot;
-        int4 ex = scan256x4(sum, tmp, &tot);
-        ex.x += carry.x; ex.y += carry.y; ex.z += carry.z; ex.w += carry.w;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = e0 + 4 * tid + u;
-            if (e < NB) {
-                seg[e] = ex.x;
-                bsg[e] = ex.y;
-                bbg[e] = ex.z;
-                if (b == 0) {
-                    a.seg_off[e] = ex.x;
-                    if (v4[u].w)
-                        a.active[ex.w] = e;
-                }
-            }
-            ex.x += v4[u].x; ex.y += v4[u].y; ex.z += v4[u].z; ex.w += v4[u].w;
-        }
-        carry.x += tot.x; carry.y += tot.y; carry.z += tot.z; carry.w += tot.w;
+        if (act && sub == tpb - 1)
+            g.hist[b] = incl;
     }
+    if (tid == 0)
+        g.n_bad = 0;
     __syncthreads();
-    const int n_sg = carry.y, n_bg = carry.z;
-
-    // this bucket's rows, in index order
-    const bool dense = b < N && hist[b] >= a.dense_min;
-    const int tile0 = dense ? bsg[b] : n_sg + bbg[b];
-    const int shift = dense ? sg_shift : 4;
-    const int mask = (1 << shift) - 1;
-    int placed = 0, bad_w = 0;
-    if (n > kParRows)
-        load_ids(a, (int64_t)tid * kParPer, idn);       // second pass from chunk 0 again
-    for (int64_t c0 = 0; c0 < n; c0 += kParRows) {
-        const int64_t r0 = c0 + (int64_t)tid * kParPer;
-        int32_t id[kParPer];
-#pragma unroll
-        for (int j = 0; j < kParPer; ++j)
-            id[j] = n > kParRows ? idn[j] : id0[j];
-        if (c0 + kParRows < n)
-            load_ids(a, r0 + kParRows, idn);
-        int key[kParPer];
-        int mine = 0;
-#pragma unroll
-        for (int j = 0; j < kParPer; ++j) {
-            key[j] = row_key(r0 + j, n, id[j], N, ok, bad_w);
-            mine += key[j] == b ? 1 : 0;
-        }
-        int4 tot;
-        int rk = placed + scan256x4(make_int4(mine, 0, 0, 0), tmp, &tot).x;
-        placed += tot.x;
-#pragma unroll
-        for (int j = 0; j < kParPer; ++j) {
-            if (key[j] == b) {
-                a.perm[seg[b] + rk] = (int32_t)(r0 + j);
-                if (b < N)
-                    a.tiles[tile0 + (rk >> shift)].rows[rk & mask] = (int32_t)(r0 + j);
-                ++rk;
-            }
-        }
+    int bad = 0;
+    for (int c = tid; c < n_chunks; c += kGroupThreads)
+        bad += a.chunk_bad[c];
+    if (bad)
+        atomicAdd(&g.n_bad, bad);
+    group_scan(g, N, a.dense_min, sg_shift);   // ends with a barrier
+    group_store(g, N, a.seg_off, a.active, a.counts);
+    // per bucket: group offset, first tile, tile shift, path
+    for (int b = tid; b < NB; b += kGroupThreads) {
+        const BucketPlan p = bucket_plan(g, b, N, a.dense_min, sg_shift);
+        a.binfo[b] = make_int4(p.first, p.tile0, p.shift, p.path);
     }
-
-    if (b != 0)
-        return;
-    // workgroup 0: the rest of the active list, counts, tile headers
-    int4 bt;
-    (void)scan256x4(make_int4(bad, 0, 0, 0), tmp, &bt);
-    for (int e = carry.w + tid; e < N; e += kParThreads)
-        a.active[e] = -1;
-    if (tid == 0) {
-        a.counts[kCntValid] = seg[N];
-        a.counts[kCntActive] = carry.w;
-        a.counts[kCntBad] = bt.x;
-        a.counts[kCntSgmv] = n_sg;
-        a.counts[kCntBgmv] = n_bg;
-    }
-    for (int t = tid; t < n_sg + n_bg; t += kParThreads) {
-        int s, m, sh;
-        if (t < n_sg) {
-            s = upper_slot(bsg, N, t);
-            m = t - bsg[s];
-            sh = sg_shift;
-        } else {
-            s = upper_slot(bbg, N, t - n_sg);
-            m = t - n_sg - bbg[s];
-            sh = 4;
-        }
-        const int c = hist[s];
+    for (int t = tid; t < g.n_sg + g.n_bg; t += kGroupThreads) {
+        int s, m;
+        locate_tile(g, N, t, s, m);
+        const BucketPlan p = bucket_plan(g, s, N, a.dense_min, sg_shift);
+        const int lo = m << p.shift;
         *reinterpret_cast<int4 *>(&a.tiles[t]) =
-            make_int4(s, seg[s] + (m << sh), min(1 << sh, c - (m << sh)),
-                      t < n_sg ? kTileSgmv : kTileBgmv);
+            make_int4(s, p.first + lo, min(1 << p.shift, p.count - lo), p.path);
+    }
+}
+
+__global__ __launch_bounds__(kChunk) void seg_place_kernel(SegBuildArgs a)
+{
+    __shared__ int run[kGroupBuckets];
+    __shared__ int4 info[kGroupBuckets];
+    const int N = a.n_slots, NB = N + 1, c = blockIdx.x, tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int64_t i = (int64_t)c * kChunk + tid;
+    const int key = i < a.n ? a.keys[i] : -1;
+    for (int e = tid; e < NB; e += kChunk) {
+        const int4 bi = a.binfo[e];
+        info[e] = bi;
+        run[e] = bi.x + a.chunk[(int64_t)c * NB + e];
+    }
+    // rank among the wavefront's lanes with the same key, one distinct key at
+    // a time (the lowest lane still unplaced names the next key)
+    int rank = 0, count = 0;
+    uint64_t left = __ballot(key >= 0);
+    while (left) {
+        const int k0 = __builtin_amdgcn_readlane(key, (int)__builtin_ctzll(left));
+        const uint64_t m = __ballot(key == k0);
+        if (key == k0) {
+            rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+            count = __popcll(m);
+        }
+        left &= ~m;
+    }
+    __syncthreads();   // run and info ready
+    // wavefronts in row order: read the running position, then the key's first
+    // lane advances it (inside a wavefront every read precedes the write)
+    int pos = -1;
+    for (int w = 0; w < kChunk / 64; ++w) {
+        if (wave == w && key >= 0) {
+            pos = run[key] + rank;
+            if (rank == 0)
+                run[key] += count;
+        }
+        __syncthreads();
+    }
+    if (key >= 0) {
+        a.perm[pos] = (int32_t)i;
+        if (key < N) {
+            const int4 bi = info[key];
+            const int p = pos - bi.x;
+            a.tiles[bi.y + (p >> bi.z)].rows[p & ((1 << bi.z) - 1)] = (int32_t)i;
+        }
     }
 }
 
@@ -311,11 +240,15 @@ __global__ __launch_bounds__(kGroupThreads) void seg_build_small_kernel(SegBuild
 
 hipError_t launch_seg_build(const SegBuildArgs &a, hipStream_t stream)
 {
-    if (a.n <= kGroupRows)
+    if (a.n <= kGroupRows) {
         hipLaunchKernelGGL(seg_build_small_kernel, dim3(a.n_slots + 1), dim3(kGroupThreads), 0,
                            stream, a);
-    else
-        hipLaunchKernelGGL(seg_build_kernel, dim3(a.n_slots + 1), dim3(kParThreads), 0, stream, a);
+        return hipGetLastError();
+    }
+    const int n_chunks = (int)((a.n + kChunk - 1) / kChunk);
+    hipLaunchKernelGGL(seg_count_kernel, dim3(n_chunks), dim3(kChunk), 0, stream, a);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(kGroupThreads), 0, stream, a, n_chunks);
+    hipLaunchKernelGGL(seg_place_kernel, dim3(n_chunks), dim3(kChunk), 0, stream, a);
     return hipGetLastError();
 }
 

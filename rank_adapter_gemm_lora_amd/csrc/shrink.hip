@@ -33,7 +33,7 @@ namespace lora {
 namespace {
 
 constexpr int kNT = 4;    // N-tiles (slice, 16-rank chunk) accumulated at once (SGMV)
-constexpr int kSt = 4;    // 8-element k groups per lane per SGMV step
+constexpr int kSt = 2;    // 8-element k groups per lane per SGMV step (two steps in flight)
 
 // Destination of one split's v for grouping position pos.
 __device__ __forceinline__ float *v_out(const ApplyArgs &a, int ks, int pos)
@@ -134,11 +134,12 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
             for (int tt = 0; tt < kNT; ++tt)
                 acc[mt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        for (int64_t u0 = wb; u0 < we; u0 += 4 * kSt) {
-            uint4 xs[4][kSt], as[kNT][kSt];
+        // steps of 4 * kSt units (8 k each), two register buffers: the loads of
+        // step i + 1 are in flight while the MFMAs of step i run
+        auto load_step = [&](int64_t u0, uint4 (&xs)[4][kSt], uint4 (&as)[kNT][kSt]) {
 #pragma unroll
             for (int st = 0; st < kSt; ++st) {
-                const int64_t unit = u0 + kSt * g + st;
+                const int64_t unit = u0 + 4 * st + g;   // lanes g = 0..3: 64 contiguous bytes of a row
                 const bool ok = unit < we;
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
@@ -149,6 +150,8 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
                     as[tt][st] = (ok && aok[tt]) ? load16(a.A, arow[tt] + unit * 8)
                                                  : make_uint4(0, 0, 0, 0);
             }
+        };
+        auto mma_step = [&](const uint4 (&xs)[4][kSt], const uint4 (&as)[kNT][kSt]) {
 #pragma unroll
             for (int st = 0; st < kSt; ++st)
 #pragma unroll
@@ -158,6 +161,20 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
                         for (int tt = 0; tt < kNT; ++tt)
                             acc[mt][tt] = mfma_bf16_16x16x32(xs[mt][st], as[tt][st], acc[mt][tt]);
                     }
+        };
+        const int64_t n_steps = (we - wb + 4 * kSt - 1) / (4 * kSt);
+        uint4 xa[4][kSt], aa[kNT][kSt], xb[4][kSt], ab[kNT][kSt];
+        if (n_steps > 0)
+            load_step(wb, xa, aa);
+        for (int64_t i = 0; i < n_steps; i += 2) {
+            if (i + 1 < n_steps)
+                load_step(wb + (i + 1) * 4 * kSt, xb, ab);
+            mma_step(xa, aa);
+            if (i + 1 >= n_steps)
+                break;
+            if (i + 2 < n_steps)
+                load_step(wb + (i + 2) * 4 * kSt, xa, aa);
+            mma_step(xb, ab);
         }
 
         // fixed-order sum of the four k-quarters, one M-tile at a time
