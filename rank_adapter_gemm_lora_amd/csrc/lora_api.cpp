@@ -174,6 +174,7 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     a.max_rows = st->max_rows;
     a.ks = choose_ks(st->k, seg->n_rows);
     a.mfma_ok = stack_has_mfma_path(st) ? 1 : 0;
+    a.sgmv_rows = sgmv_rows_for(seg->n_rows);
     const ExpandLds l = expand_lds(st, a.mfma_ok != 0);
     a.lds_v_off = l.v_off;
     a.lds_b_off = l.b_off;
@@ -445,9 +446,7 @@ SegBuildArgs make_seg_args(const lora_stack *st, const int32_t *ids, int64_t n_r
     a.n_slots = st->n_slots;
     a.slot_rank = st->d_rank;
     a.dense_min = seg->dense_min;
-    // dense groups of small batches are cut into 16-row tiles (more workgroups
-    // for few rows), of large batches into 64-row tiles (B reused by 64 rows)
-    a.sgmv_rows = n_rows <= 4096 ? kBgmvTileRows : kSgmvTileRows;
+    a.sgmv_rows = sgmv_rows_for(n_rows);
     a.perm = seg->perm;
     a.seg_off = seg->seg_off;
     a.active = seg->active;

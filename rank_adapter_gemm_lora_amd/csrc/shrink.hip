@@ -33,7 +33,6 @@ namespace lora {
 namespace {
 
 constexpr int kNT = 4;    // N-tiles (slice, 16-rank chunk) accumulated at once (SGMV)
-constexpr int kSt = 2;    // 8-element k groups per lane per SGMV step (two steps in flight)
 
 // Destination of one split's v for grouping position pos.
 __device__ __forceinline__ float *v_out(const ApplyArgs &a, int ks, int pos)
@@ -99,15 +98,22 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
     }
 }
 
+// MT: M-tiles (16 rows each) of the tile shape this launch serves -- 1 for
+// the 16-row tiles of batches up to 4096 rows, 4 for 64-row tiles -- so each
+// instantiation holds only the registers its shape needs.  kSt: 8-element k
+// groups per lane per step; steps run with two register buffers (the loads of
+// step i + 1 in flight during the MFMAs of step i).
+template <int MT>
 __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, int p0,
                                  int cnt, int ks)
 {
+    constexpr int kSt = MT == 1 ? 4 : 2;
     __shared__ f32x4_t red[4][kNT * 64];   // [wave][tt * 64 + lane]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
-    int64_t xrow[4];
+    int64_t xrow[MT];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
         xrow[mt] = (int64_t)rows[min(16 * mt + m, cnt - 1)] * a.ldx;   // clamp: dropped later
     const int nj = (r + 15) >> 4;
     const int NT = a.n_slices * nj;
@@ -127,22 +133,22 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
             aok[tt] = t < NT && j < r;
             arow[tt] = aok[tt] ? (((int64_t)s * a.n_slices + q) * a.r_max + j) * a.k : 0;
         }
-        f32x4_t acc[4][kNT];
+        f32x4_t acc[MT][kNT];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int tt = 0; tt < kNT; ++tt)
                 acc[mt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         // steps of 4 * kSt units (8 k each), two register buffers: the loads of
         // step i + 1 are in flight while the MFMAs of step i run
-        auto load_step = [&](int64_t u0, uint4 (&xs)[4][kSt], uint4 (&as)[kNT][kSt]) {
+        auto load_step = [&](int64_t u0, uint4 (&xs)[MT][kSt], uint4 (&as)[kNT][kSt]) {
 #pragma unroll
             for (int st = 0; st < kSt; ++st) {
                 const int64_t unit = u0 + 4 * st + g;   // lanes g = 0..3: 64 contiguous bytes of a row
                 const bool ok = unit < we;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
                     xs[mt][st] = (ok && mt < n_mt) ? load16(a.x, xrow[mt] + unit * 8)
                                                   : make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -151,11 +157,11 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
                                                  : make_uint4(0, 0, 0, 0);
             }
         };
-        auto mma_step = [&](const uint4 (&xs)[4][kSt], const uint4 (&as)[kNT][kSt]) {
+        auto mma_step = [&](const uint4 (&xs)[MT][kSt], const uint4 (&as)[kNT][kSt]) {
 #pragma unroll
             for (int st = 0; st < kSt; ++st)
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
                     if (mt < n_mt) {
 #pragma unroll
                         for (int tt = 0; tt < kNT; ++tt)
@@ -163,7 +169,7 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
                     }
         };
         const int64_t n_steps = (we - wb + 4 * kSt - 1) / (4 * kSt);
-        uint4 xa[4][kSt], aa[kNT][kSt], xb[4][kSt], ab[kNT][kSt];
+        uint4 xa[MT][kSt], aa[kNT][kSt], xb[MT][kSt], ab[kNT][kSt];
         if (n_steps > 0)
             load_step(wb, xa, aa);
         for (int64_t i = 0; i < n_steps; i += 2) {
@@ -179,7 +185,7 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 
         // fixed-order sum of the four k-quarters, one M-tile at a time
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
             if (mt >= n_mt)
                 break;
 #pragma unroll
@@ -209,13 +215,13 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 static_assert(kNT * 64 == 256, "one reduction entry per thread");
 
 // One tile, its rows already in LDS; r is the slot's rank.
-template <int DT>
+template <int DT, int MT>
 __device__ __forceinline__ void shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r,
                                             int p0, int cnt, int path, int ks)
 {
     if constexpr (DT == DT_BF16) {
         if (path == kTileSgmv && a.mfma_ok) {
-            sgmv_shrink_tile(a, rows, s, r, p0, cnt, ks);
+            sgmv_shrink_tile<MT>(a, rows, s, r, p0, cnt, ks);
             return;
         }
     }
@@ -224,7 +230,7 @@ __device__ __forceinline__ void shrink_tile(const ApplyArgs &a, const int32_t *r
         bgmv_shrink_tile<DT>(a, rows + sub, s, r, p0 + sub, min(kBgmvTileRows, cnt - sub), ks);
 }
 
-template <int DT>
+template <int DT, int MT>
 __global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
 {
     __shared__ int32_t rows[kSgmvTileRows];
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
     const int r = rank[h.x];
     if (r == 0)
         return;   // slot emptied since the grouping was built: nothing to compute
-    shrink_tile<DT>(a, rows, h.x, r, h.y, h.z, h.w, ks);
+    shrink_tile<DT, MT>(a, rows, h.x, r, h.y, h.z, h.w, ks);
 }
 
 // Grouping and shrink in one launch, for small batches.  Every workgroup
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(256) void build_shrink_kernel(ApplyArgs a, SegBuild
                 rows[u] = j * kGroupThreads + tid;
         }
         __syncthreads();
-        shrink_tile<DT>(a, rows, s, g.rank[s], p0, cnt, p.path, ks);
+        shrink_tile<DT, 1>(a, rows, s, g.rank[s], p0, cnt, p.path, ks);   // 16-row tiles
         if (ks == 0) {
 #pragma unroll
             for (int j = 0; j < kGroupPer; ++j) {
@@ -315,17 +321,22 @@ hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream
     if (max_tiles <= 0)
         return hipSuccess;
     const dim3 grid(a.ks, max_tiles);
-    if (dtype == DT_BF16)
-        hipLaunchKernelGGL(shrink_kernel<DT_BF16>, grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(shrink_kernel<DT_F32>, grid, dim3(256), 0, stream, a);
+    const bool tall = a.sgmv_rows > kBgmvTileRows;   // 64-row dense tiles
+    if (dtype == DT_BF16) {
+        if (tall)
+            hipLaunchKernelGGL((shrink_kernel<DT_BF16, 4>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((shrink_kernel<DT_BF16, 1>), grid, dim3(256), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((shrink_kernel<DT_F32, 1>), grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_build_shrink(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
                                hipStream_t stream)
 {
-    if (max_tiles <= 0 || sb.n > kGroupRows)
+    if (max_tiles <= 0 || sb.n > kGroupRows || sb.sgmv_rows != kBgmvTileRows)
         return hipErrorInvalidValue;
     const dim3 grid(a.ks, max_tiles);
     if (dtype == DT_BF16)
