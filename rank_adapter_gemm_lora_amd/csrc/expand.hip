@@ -146,6 +146,9 @@ __device__ __forceinline__ void merge16(const ApplyArgs &a, int64_t yi, bool h0,
 
 // ---------------------------------------------------------------- SGMV (MFMA)
 
+// MT: row tiles (16 rows each) of the dense tile height this launch serves (1
+// for batches up to 4096 rows, 4 above), so the y registers match the shape.
+template <int MT>
 __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
                                  int p0, int cnt, int64_t c0, float *vs, uint16_t *bs)
 {
@@ -157,9 +160,9 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     const int rp = (r + 7) & ~7, nj = (r + 15) >> 4;
 
     // y of this lane's rows
-    Vec8<DT_BF16> y0[4], y1[4];
+    Vec8<DT_BF16> y0[MT], y1[MT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < MT; ++nt) {
         const int u = 16 * nt + m;
         if (nt < n_nt && u < cnt && in_d) {
             const int64_t yi = (int64_t)rows[u] * a.ldy + cb;
@@ -201,7 +204,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
         bcol[mt] = (64 * wave + 16 * (m >> 2) + 4 * mt + (m & 3)) * rp;
 
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < MT; ++nt) {
         if (nt >= n_nt)
             continue;   // (uniform) fully unrolled: y0[nt] / y1[nt] stay in registers
         const int u = 16 * nt + m;
@@ -360,7 +363,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
 
 // Dynamic LDS: [rows: 64 int][slot table: rank, scale (when n_slots <= 256)]
 // [v staging at lds_v_off][B staging at lds_b_off]; the host sizes it.
-template <int DT>
+template <int DT, int MT>
 __global__ __launch_bounds__(256) void expand_kernel(ApplyArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -397,8 +400,8 @@ __global__ __launch_bounds__(256) void expand_kernel(ApplyArgs a)
         return;   // slot emptied since the grouping was built: rows stay untouched
     if constexpr (DT == DT_BF16) {
         if (h.w == kTileSgmv && a.mfma_ok) {
-            sgmv_expand_tile(a, rows, s, r, scale, p0, cnt, c0, vs,
-                             reinterpret_cast<uint16_t *>(bst));
+            sgmv_expand_tile<MT>(a, rows, s, r, scale, p0, cnt, c0, vs,
+                                 reinterpret_cast<uint16_t *>(bst));
             return;
         }
     }
@@ -417,10 +420,15 @@ hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream
     if (max_tiles <= 0)
         return hipSuccess;
     const dim3 grid((unsigned)((a.D + kCols - 1) / kCols), max_tiles);
-    if (dtype == DT_BF16)
-        hipLaunchKernelGGL(expand_kernel<DT_BF16>, grid, dim3(256), a.lds_bytes, stream, a);
-    else
-        hipLaunchKernelGGL(expand_kernel<DT_F32>, grid, dim3(256), a.lds_bytes, stream, a);
+    const bool tall = a.sgmv_rows > kBgmvTileRows;   // 64-row dense tiles
+    if (dtype == DT_BF16) {
+        if (tall)
+            hipLaunchKernelGGL((expand_kernel<DT_BF16, 4>), grid, dim3(256), a.lds_bytes, stream, a);
+        else
+            hipLaunchKernelGGL((expand_kernel<DT_BF16, 1>), grid, dim3(256), a.lds_bytes, stream, a);
+    } else {
+        hipLaunchKernelGGL((expand_kernel<DT_F32, 1>), grid, dim3(256), a.lds_bytes, stream, a);
+    }
     return hipGetLastError();
 }
 

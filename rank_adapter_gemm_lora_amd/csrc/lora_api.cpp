@@ -115,10 +115,10 @@ struct ExpandLds {
     int v_off, b_off, bytes;
 };
 
-ExpandLds expand_lds(const lora_stack *st, bool mfma)
+ExpandLds expand_lds(const lora_stack *st, bool mfma, int tile_rows)
 {
     const int64_t table = st->n_slots <= kExpandTableSlots ? 8 * kExpandTableSlots : 0;
-    const int64_t rows = mfma ? kSgmvTileRows : kBgmvTileRows;
+    const int64_t rows = mfma ? tile_rows : kBgmvTileRows;
     const int64_t v_bytes = round_up(rows * expand_nq_max(st) * st->r_max * 4, 16);
     const int64_t b_bytes = std::max<int64_t>(8 * kExpandCols * 4,
                                               mfma ? (int64_t)kExpandCols * st->rp_max * 2 : 0);
@@ -139,7 +139,7 @@ bool stack_has_mfma_path(const lora_stack *st)
     for (int q = 0; q < st->n_slices; ++q)
         if (st->slice_d[q] % 64 != 0)
             return false;
-    return expand_lds(st, true).bytes <= kExpandLdsMax;
+    return expand_lds(st, true, kSgmvTileRows).bytes <= kExpandLdsMax;
 }
 
 lora_status check_apply_common(const lora_stack *st, const lora_segments *seg)
@@ -175,7 +175,9 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     a.ks = choose_ks(st->k, seg->n_rows);
     a.mfma_ok = stack_has_mfma_path(st) ? 1 : 0;
     a.sgmv_rows = sgmv_rows_for(seg->n_rows);
-    const ExpandLds l = expand_lds(st, a.mfma_ok != 0);
+    // v staging sized for this batch's dense tile height (16 rows up to 4096
+    // rows): a smaller footprint lets more expand workgroups share a CU
+    const ExpandLds l = expand_lds(st, a.mfma_ok != 0, sgmv_rows_for(seg->n_rows));
     a.lds_v_off = l.v_off;
     a.lds_b_off = l.b_off;
     a.lds_bytes = l.bytes;
