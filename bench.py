@@ -386,7 +386,7 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, copy_mb, wor
     # and a chunked variant)
     names = {"seg_build": ("seg_build_kernel", "seg_build_small_kernel"),
              "shrink": ("shrink_kernel",), "build_shrink": ("build_shrink_kernel",),
-             "expand": ("expand_kernel",)}
+             "expand": ("expand_kernel", "expand_kernel_bf16_short")}
 
     def bare(kname):
         head = kname.replace("(anonymous namespace)", "").split("(")[0].split("<")[0]
