@@ -153,7 +153,8 @@ def set_bytes(p) -> int:
     return pool + p.x.nbytes + p.y.nbytes + p.ids.nbytes
 
 
-def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None) -> dict:
+def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
+            graph: bool = True) -> dict:
     import torch
     from rank_adapter_gemm_lora_amd import binding as lb
 
@@ -230,12 +231,36 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None) -> 
         e1.record(stream)
         torch.cuda.synchronize()
         per[name] = e0.elapsed_time(e1) * 1e3 / steps
+    # the same step replayed from HIP graphs (one captured per buffer set): the
+    # launch shapes depend only on the batch shape, so a graph serves any mix
+    graph_ms = None
+    if graph:
+        graphs = []
+        for bs in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(bs)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for i in range(min(warmup, n_sets)):
+                graphs[i % n_sets].replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                graphs[(warmup + i) % n_sets].replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / steps
+        del graphs
     n_bgmv, n_sgmv = lb.lora_segments_tile_counts(sets[0].seg, sh)
     for bs in sets:
         bs.close(lb)
     torch.cuda.synchronize()
     return dict(wall_s=wall, gpu_ms=gpu_ms, n_sets=n_sets, set_bytes=set_bytes(p),
-                kernel_us=per, tiles=dict(bgmv=n_bgmv, sgmv=n_sgmv))
+                kernel_us=per, tiles=dict(bgmv=n_bgmv, sgmv=n_sgmv), graph_ms=graph_ms)
 
 
 # ----------------------------------------------------------------- CPU oracle
@@ -303,6 +328,9 @@ def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -
         "tiles": g["tiles"],
         "roofline": roof,
         "host_wall_ms_per_step": round(g["wall_s"] * 1e3 / steps, 4),
+        "graph_ms_per_step": (round(g["graph_ms"], 5) if g["graph_ms"] is not None else None),
+        "graph_tokens_per_s": (round(acct["n_valid"] / (g["graph_ms"] * 1e-3), 1)
+                               if g["graph_ms"] is not None else None),
     }
     if cpu:
         line["cpu_baseline"] = run_cpu_baseline(p, acct)

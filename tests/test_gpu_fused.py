@@ -129,3 +129,42 @@ def test_build_apply_repeated_layers():
             check_against_oracle(p, run.y_host(), what=f"layer {layer}")
     finally:
         run.close()
+
+
+def test_build_apply_graph_replay_any_mix():
+    """The launch shapes depend only on the batch shape, so one captured HIP
+    graph of lora_build_apply serves every adapter mix: replays with new ids
+    (and a fresh base y) each match the oracle, segments included.  The new
+    inputs are copied in eagerly between replays, with synchronisations."""
+    base = synth.make_random(41, n_rows=256, k=512, slice_d=[512], n_slots=8, ranks=[16] * 8,
+                             r_max=16, p_none=1 / 9)
+    run = GpuRun(base)
+    try:
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        note("graph capture of lora_build_apply")
+        with torch.cuda.graph(graph):
+            lb.lora_build_apply(run.stack, run.y.data_ptr(), base.ldy, run.x.data_ptr(), base.ldx,
+                                run.ids.data_ptr(), base.n_rows, run.seg,
+                                torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(7)
+        for rep in range(4):
+            ids = rng.integers(-1, base.n_slots, size=base.n_rows).astype(np.int32)
+            if rep == 3:
+                ids[:] = 2   # one dense group
+            p = synth.make_random(41, n_rows=256, k=512, slice_d=[512], n_slots=8, ranks=[16] * 8,
+                                  r_max=16, ids=ids)
+            p.A, p.B, p.alphas, p.x, p.y = base.A, base.B, base.alphas, base.x, base.y
+            run.ids.copy_(torch.from_numpy(ids).to(run.device))
+            run.y.copy_(torch.from_numpy(base.y.view(np.int16)).to(run.device))
+            torch.cuda.synchronize()
+            note(f"graph replay {rep}")
+            graph.replay()
+            torch.cuda.synchronize()
+            check_against_oracle(p, run.y_host(), what=f"replay {rep}")
+            _seg_equal(lb.lora_segments_download(run.seg, p.n_rows, p.n_slots, run.stream), p,
+                       f"replay {rep}")
+        del graph
+    finally:
+        run.close()
