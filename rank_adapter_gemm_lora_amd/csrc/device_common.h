@@ -40,6 +40,18 @@ __device__ __forceinline__ int div_small(int n, uint32_t m)
     return (int)(((uint64_t)(uint32_t)n * m) >> 24);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wavefront's LDS
+// stores (lgkmcnt), not for its global loads, so loads issued ahead of the
+// barrier stay in flight across it.  __syncthreads() is a full release fence
+// and would drain them.  Not for LDS written by global-to-LDS copies (those
+// complete on the vector-memory counter).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Eight consecutive elements of a row, held in their storage format.
 template <int DT> struct Vec8;
 

@@ -65,6 +65,11 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj)
                     acc0[jj] = acc1[jj] = 0.f;
+                // A rows j0 .. j0 + 15 of the slot: rows at or past the rank are
+                // zero in the pool (load_slot zero-fills), so they are read
+                // without a branch and add nothing; rows past r_max repeat the
+                // last row (their results are never stored).  Row bases are
+                // uniform, so only the lane's k offset lives in a vector register.
 #pragma nounroll
                 for (int64_t g = gb + lane; g < ge; g += 64) {
                     Vec8<DT> xa, xb;
@@ -75,11 +80,9 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
                         xb.zero();
 #pragma unroll
                     for (int jj = 0; jj < 16; ++jj) {
+                        const int64_t arow = abase + (int64_t)min(jj, a.r_max - 1 - j0) * a.k;
                         Vec8<DT> av;
-                        if (j0 + jj < r)
-                            av.load(a.A, abase + (int64_t)jj * a.k + g * 8);
-                        else
-                            av.zero();
+                        av.load(a.A, arow + g * 8);
                         acc0[jj] = av.dot(xa, acc0[jj]);
                         acc1[jj] = av.dot(xb, acc1[jj]);
                     }
@@ -214,6 +217,143 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 }
 static_assert(kNT * 64 == 256, "one reduction entry per thread");
 
+// 64-row tiles (batches above 4096 rows).  Each wavefront owns 16 rows of the
+// tile over the split's whole k-range, so no cross-wavefront reduction is
+// needed.  Blocks of 128 k; per block each thread loads
+//   x: 4 granules of its wavefront's 16 rows in row-run order -- instruction
+//      i covers rows 4 i .. 4 i + 3 with 16 lanes (256 contiguous bytes) per
+//      row, which reads HBM at ~5.3 TB/s on this part where the MFMA operand
+//      order (16 rows x 64 B per instruction) reads at ~4.2;
+//   A: 4 granules of the block's rank rows, shared by the four wavefronts;
+// into a ring of kTallRing register slots three blocks ahead, then stores them
+// into LDS (x: the wavefront's own buffer, A: one of two shared buffers) and
+// reads the MFMA operands back.  Both layouts XOR the unit index with the row,
+// so the operand reads of 16 rows x 4 units hit 64 distinct banks.  The one
+// barrier per block orders LDS only (lds_barrier), so the loads of the next
+// three blocks stay in flight across it.
+constexpr int kTallRing = 4;
+constexpr int kBlkUnits = 16;   // 8-element k units per block
+
+__device__ void sgmv_shrink_tile_tall(const ApplyArgs &a, const int32_t *rows, int s, int r,
+                                      int p0, int cnt, int ks)
+{
+    __shared__ uint4 ablk[2][kNT * 16 * kBlkUnits];   // [buffer][rank row * 16 + swizzled unit]
+    __shared__ uint4 xblk[4 * 16 * kBlkUnits];        // [wavefront][row][swizzled unit]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int nj = (r + 15) >> 4;
+    const int NT = a.n_slices * nj;
+    const int64_t g8 = a.k >> 3;
+    const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
+    const int nb = (int)((ge - gb + kBlkUnits - 1) / kBlkUnits);
+    // the x granules this lane loads: rows 4 i + lane / 16 of the wavefront's
+    // 16, unit lane % 16 of the block
+    int64_t xsrc[4];
+    bool xval[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int u = 16 * wave + 4 * i + g;
+        xval[i] = u < cnt;
+        xsrc[i] = (int64_t)rows[min(u, cnt - 1)] * a.ldx;
+    }
+    uint4 *xw = xblk + 16 * kBlkUnits * wave;
+
+    for (int t0 = 0; t0 < NT; t0 += kNT) {
+        const int ntv = min(kNT, NT - t0);            // valid N-tiles in this pass
+        // the four A granules this thread stages per block: rank row jm of
+        // N-tiles 0..3, unit au; consecutive threads read consecutive 16 B of
+        // one rank row
+        const int jm = threadIdx.x >> 4, au = threadIdx.x & 15;
+        const int adst = jm * kBlkUnits + (au ^ jm);   // + 256 tt: N-tile tt's rows
+        int64_t asrc[4];
+        bool aval[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int t = t0 + tt;
+            const int q = t / nj, jc = t - q * nj;
+            const int j = 16 * jc + jm;
+            aval[tt] = tt < ntv && j < r;
+            asrc[tt] = aval[tt] ? (((int64_t)s * a.n_slices + q) * a.r_max + j) * a.k : 0;
+        }
+        auto issue = [&](int b, uint4 (&xs)[4], uint4 (&as)[4]) {
+            const int64_t u0 = gb + (int64_t)b * kBlkUnits;
+            const int64_t xunit = u0 + m;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xs[i] = (xval[i] && xunit < ge) ? load16(a.x, xsrc[i] + xunit * 8)
+                                                : make_uint4(0, 0, 0, 0);
+            const int64_t aunit = u0 + au;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                as[tt] = (aval[tt] && aunit < ge) ? load16(a.A, asrc[tt] + aunit * 8)
+                                                  : make_uint4(0, 0, 0, 0);
+        };
+        f32x4_t acc[kNT];
+#pragma unroll
+        for (int tt = 0; tt < kNT; ++tt)
+            acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        uint4 xr[kTallRing][4], ar[kTallRing][4];
+        auto step = [&](int b, uint4 (&xs)[4], uint4 (&as)[4], uint4 (&xn)[4], uint4 (&an)[4]) {
+            if (b + kTallRing - 1 < nb)
+                issue(b + kTallRing - 1, xn, an);
+            uint4 *buf = ablk[b & 1];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                buf[256 * tt + adst] = as[tt];
+            // x row 4 i + g, unit m -> LDS row 4 i + g, unit m ^ (4 i + g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xw[(4 * i + g) * kBlkUnits + (m ^ (4 * i + g))] = xs[i];
+            // block b of A and x in LDS; the loads issued above stay in flight
+            lds_barrier();
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int unit = 4 * st + g;
+                const uint4 xop = xw[m * kBlkUnits + (unit ^ m)];
+#pragma unroll
+                for (int tt = 0; tt < kNT; ++tt) {
+                    if (tt < ntv) {
+                        const uint4 aop = buf[(16 * tt + m) * kBlkUnits + (unit ^ m)];
+                        acc[tt] = mfma_bf16_16x16x32(xop, aop, acc[tt]);
+                    }
+                }
+            }
+            // the x buffer is rewritten next block: every lane of this
+            // wavefront must have read it first (LDS ops of a wavefront run in
+            // order, and the next writes follow these reads in program order)
+        };
+#pragma unroll
+        for (int b = 0; b < kTallRing - 1; ++b)
+            if (b < nb)
+                issue(b, xr[b], ar[b]);
+        for (int b = 0; b < nb; b += kTallRing) {
+            step(b, xr[0], ar[0], xr[3], ar[3]);
+            if (b + 1 < nb)
+                step(b + 1, xr[1], ar[1], xr[0], ar[0]);
+            if (b + 2 < nb)
+                step(b + 2, xr[2], ar[2], xr[1], ar[1]);
+            if (b + 3 < nb)
+                step(b + 3, xr[3], ar[3], xr[2], ar[2]);
+        }
+        // accumulator lane (g, m): rows 16 wave + 4 g + i, rank row m of each N-tile
+#pragma unroll
+        for (int tt = 0; tt < kNT; ++tt) {
+            const int t = t0 + tt;
+            const int q = t / nj, jc = t - q * nj;
+            const int j = 16 * jc + m;
+            if (tt < ntv && j < r) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int u = 16 * wave + 4 * g + i;
+                    if (u < cnt)
+                        v_out(a, ks, p0 + u)[q * a.r_max + j] = acc[tt][i];
+                }
+            }
+        }
+        __syncthreads();   // the next pass restages every buffer
+    }
+}
+
 // One tile, its rows already in LDS; r is the slot's rank.
 template <int DT, int MT>
 __device__ __forceinline__ void shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r,
@@ -221,7 +361,10 @@ __device__ __forceinline__ void shrink_tile(const ApplyArgs &a, const int32_t *r
 {
     if constexpr (DT == DT_BF16) {
         if (path == kTileSgmv && a.mfma_ok) {
-            sgmv_shrink_tile<MT>(a, rows, s, r, p0, cnt, ks);
+            if constexpr (MT == 4)
+                sgmv_shrink_tile_tall(a, rows, s, r, p0, cnt, ks);
+            else
+                sgmv_shrink_tile<MT>(a, rows, s, r, p0, cnt, ks);
             return;
         }
     }
