@@ -50,6 +50,9 @@ def _bind(lib):
     lib.oracle_apply_rows.restype = ctypes.c_int
     lib.oracle_apply_rows.argtypes = [ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, P, P,
                                       P, P, P, P, P, P, i64, P, i64, P, i64, P, ctypes.c_int]
+    lib.oracle_merge.restype = ctypes.c_int
+    lib.oracle_merge.argtypes = [ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, ctypes.c_double,
+                                 P, P, P, i64, ctypes.c_int, P, ctypes.c_int]
     lib.oracle_param_count.restype = ctypes.c_int64
     lib.oracle_param_count.argtypes = [ctypes.c_int, i64, ctypes.c_int, P]
     return lib
@@ -151,3 +154,30 @@ def apply_rows(dtype: str, k: int, slice_d, slot_rank, slot_alpha, A, B, ids, x,
     if rc != 0:
         raise ValueError("oracle_apply_rows: bad argument")
     return out[:n_sel]
+
+
+def merge(dtype: str, k: int, slice_d, rank: int, alpha: float, A, B, W, sign: int = 1,
+          n_threads: int = 1, lib=None) -> np.ndarray:
+    """fp64 merged (sign +1) or unmerged (sign -1) weight, shape [D, k].
+
+    ``A`` is the slot's shrink factor [n_slices, rank, k], ``B`` its expand
+    factor [D, rank], ``W`` the base weight [D, ldw]; float32 values, or bf16
+    bit patterns as uint16 when ``dtype == "bf16"``.
+    """
+    lib = lib or load()
+    code = {"f32": F32, "bf16": BF16}[dtype]
+    npdt = np.float32 if code == F32 else np.uint16
+    slice_d = np.ascontiguousarray(slice_d, dtype=np.int64)
+    D = int(slice_d.sum())
+    A = np.ascontiguousarray(A, dtype=npdt)
+    B = np.ascontiguousarray(B, dtype=npdt)
+    W = np.ascontiguousarray(W, dtype=npdt)
+    assert A.shape == (len(slice_d), rank, k), A.shape
+    assert B.shape == (D, rank), B.shape
+    assert W.shape[0] == D and W.shape[1] >= k, W.shape
+    out = np.empty((D, k), np.float64)
+    rc = lib.oracle_merge(code, k, len(slice_d), _ptr(slice_d), int(rank), float(alpha), _ptr(A),
+                          _ptr(B), _ptr(W), W.shape[1], int(sign), _ptr(out), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_merge: bad argument")
+    return out

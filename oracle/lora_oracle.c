@@ -246,3 +246,60 @@ int64_t oracle_param_count(int rank, int64_t k, int n_slices, const int64_t *sli
         total += (int64_t)rank * k + slice_d[q] * (int64_t)rank;
     return total;
 }
+
+/*
+ * Merged weight of one adapter, in double, unrounded.
+ *
+ * Page "LoRA serving: multi-adapter dynamic loading", section 1 (merge versus
+ * keeping the adapter separate): folding one adapter into the base weight,
+ * W' = W + (alpha / r) B A, serves that adapter at the base model's cost, and
+ * unmerging subtracts the same product.  Page "Multi-LoRA Serving", section
+ * 3.1 gives the shapes: B is d x r, A is r x k.  With output slices (fused
+ * q/k/v, gate/up) the rows of slice q use that slice's A_q.
+ *
+ *   dtype            ORACLE_F32 or ORACLE_BF16 (W, A, B share it)
+ *   k                input width (columns of W)
+ *   n_slices, slice_d[n_slices]   output slices; D = sum, the rows of W
+ *   rank, alpha      the slot's true rank and alpha; scale = alpha / rank
+ *   A [n_slices][rank][k], B [D][rank]   the slot's factors, dense at true rank
+ *   W, ldw           base weight, row o (output feature) starts at element o * ldw
+ *   sign             +1 merge, -1 unmerge
+ *   Wout [D][k]      doubles, written:
+ *                    W[o][i] + sign * scale * sum_j B[o][j] A[q(o)][j][i]
+ *   n_threads        OpenMP threads over rows (<= 1: serial)
+ *
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_merge(int dtype, int64_t k, int n_slices, const int64_t *slice_d, int rank,
+                 double alpha, const void *A, const void *B, const void *W, int64_t ldw,
+                 int sign, double *Wout, int n_threads)
+{
+    if ((dtype != ORACLE_F32 && dtype != ORACLE_BF16) || k < 1 || n_slices < 1 || !slice_d ||
+        rank < 1 || !A || !B || !W || ldw < k || (sign != 1 && sign != -1) || !Wout)
+        return -1;
+    int64_t D = 0;
+    for (int q = 0; q < n_slices; ++q)
+        D += slice_d[q];
+    const double scale = alpha / (double)rank;
+
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(n_threads > 1 ? n_threads : 1)
+#endif
+    for (int64_t o = 0; o < D; ++o) {
+        /* the slice this output row belongs to */
+        int q = 0;
+        int64_t off = 0;
+        while (q + 1 < n_slices && o >= off + slice_d[q]) {
+            off += slice_d[q];
+            ++q;
+        }
+        for (int64_t i = 0; i < k; ++i) {
+            double delta = 0.0;
+            for (int j = 0; j < rank; ++j)
+                delta += load_elem(dtype, B, o * rank + j) *
+                         load_elem(dtype, A, ((int64_t)q * rank + j) * k + i);
+            Wout[o * k + i] = load_elem(dtype, W, o * ldw + i) + (double)sign * scale * delta;
+        }
+    }
+    return 0;
+}

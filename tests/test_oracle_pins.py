@@ -14,7 +14,10 @@ re-types its loops: each one evaluates the same quantity another way.
 * invariants: row permutation, slot relabelling, linearity in alpha, B = 0,
   untouched none / bad rows;
 * segments: numpy's stable argsort of the routing key;
-* parameter count: r(d + k) with the values the pages print.
+* parameter count: r(d + k) with the values the pages print;
+* merge / unmerge: the merged weight equals numpy's W + (alpha/r) B A per
+  slice, merge + unmerge cancel, and serving the merged weight reproduces
+  the per-row apply (page "LoRA serving", section 1, merge vs adapter).
 
 ``test_planted_mistake_is_caught`` compiles copies of the oracle with one
 plausible mistake each (dropped term, wrong sign, transposed operand, wrong
@@ -217,8 +220,64 @@ def pin_param_count(lib):
     assert oracle.param_count(128, 4096, [4096], lib=lib) == 8 * got
 
 
+def _merge_case(dtype, seed, slice_d=(48, 16, 24), k=40, rank=5, pad=8):
+    rng = np.random.default_rng(seed)
+    D = int(sum(slice_d))
+    A = rng.standard_normal((len(slice_d), rank, k)).astype(np.float32)
+    B = rng.standard_normal((D, rank)).astype(np.float32)
+    W = rng.standard_normal((D, k + pad)).astype(np.float32)
+    if dtype == "bf16":
+        A, B, W = (synth.f32_to_bf16_bits(t) for t in (A, B, W))
+    return A, B, W
+
+
+def pin_merge_dense(lib):
+    """Merged weight = W + sign (alpha/r) B_q A_q, materialised with numpy, per slice."""
+    slice_d = (48, 16, 24)
+    for dtype in ("f32", "bf16"):
+        A, B, W = _merge_case(dtype, 5, slice_d)
+        k, rank, alpha = A.shape[2], A.shape[1], 7.0
+        Af, Bf, Wf = _f64(A, dtype), _f64(B, dtype), _f64(W, dtype)
+        for sign in (1, -1):
+            got = oracle.merge(dtype, k, slice_d, rank, alpha, A, B, W, sign, lib=lib)
+            off = 0
+            for q, d in enumerate(slice_d):
+                want = Wf[off:off + d, :k] + sign * (alpha / rank) * (Bf[off:off + d] @ Af[q])
+                np.testing.assert_allclose(got[off:off + d], want, rtol=1e-12, atol=1e-12)
+                off += d
+
+
+def pin_merge_unmerge_cancel(lib):
+    """Merge and unmerge are negatives around W: their sum is 2 W (to fp64 rounding)."""
+    A, B, W = _merge_case("f32", 9)
+    k, rank = A.shape[2], A.shape[1]
+    plus = oracle.merge("f32", k, (48, 16, 24), rank, 3.0, A, B, W, 1, lib=lib)
+    minus = oracle.merge("f32", k, (48, 16, 24), rank, 3.0, A, B, W, -1, lib=lib)
+    np.testing.assert_allclose(plus + minus, 2.0 * W[:, :k].astype(np.float64), rtol=0, atol=1e-12)
+    assert np.abs(plus - W[:, :k]).max() > 0.1   # the adapter does change the weight
+
+
+def pin_merge_serves_apply(lib):
+    """Serving the merged weight reproduces the per-row apply of that adapter,
+    exactly on small integers: (W + (alpha/r) B A) x = W x + (alpha/r) B (A x)."""
+    rng = np.random.default_rng(11)
+    slice_d, k, rank, n = (8, 4), 6, 2, 5
+    D = sum(slice_d)
+    A = rng.integers(-3, 4, (len(slice_d), rank, k)).astype(np.float32)
+    B = rng.integers(-3, 4, (D, rank)).astype(np.float32)
+    W = rng.integers(-3, 4, (D, k)).astype(np.float32)
+    x = rng.integers(-3, 4, (n, k)).astype(np.float32)
+    y = (x.astype(np.float64) @ W.T.astype(np.float64)).astype(np.float32)   # exact
+    merged = oracle.merge("f32", k, slice_d, rank, 4.0, A, B, W, 1, lib=lib)
+    served = x.astype(np.float64) @ merged.T
+    applied = oracle.apply_rows("f32", k, slice_d, [rank], [4.0], [A], [B],
+                                np.zeros(n, np.int32), x, y, lib=lib)
+    np.testing.assert_array_equal(served, applied)
+
+
 PINS = [pin_golden_worked, pin_dense_delta, pin_merged_weight, pin_rank1_closed_form,
-        pin_invariants, pin_segments_stable_sort, pin_param_count]
+        pin_invariants, pin_segments_stable_sort, pin_param_count, pin_merge_dense,
+        pin_merge_unmerge_cancel, pin_merge_serves_apply]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f.__name__ for f in PINS])
@@ -234,7 +293,9 @@ MUTATIONS = [
     ("A_rank_slice_swapped", "((int64_t)q * r + j) * k + t", "((int64_t)j * n_slices + q) * k + t"),
     ("scale_uses_pool_rank", "double scale = slot_alpha[s] / (double)r;",
      "double scale = slot_alpha[s] / (double)max_rank;"),
-    ("slice_offset_dropped", "off += slice_d[q];", "off += 0;"),
+    ("slice_offset_dropped", "            off += slice_d[q];\n        }\n        free(v);",
+     "            off += 0;\n        }\n        free(v);"),
+    ("merge_slice_never_advances", "            off += slice_d[q];\n            ++q;", "            ++q;"),
     ("ignores_ldx", "i * ldx + t", "i * k + t"),
     ("ignores_ldy", "i * ldy + c", "i * D + c"),
     ("unstable_group_order", "perm[seg_off[s] + fill[s]] = (int32_t)i;",
@@ -244,6 +305,12 @@ MUTATIONS = [
     ("none_counted_bad", "else if (ids[i] != -1)", "else"),
     ("param_count_one_slice", "total += (int64_t)rank * k + slice_d[q] * (int64_t)rank;",
      "total += (q == 0 ? (int64_t)rank * k : 0) + slice_d[q] * (int64_t)rank;"),
+    ("merge_B_transposed", "load_elem(dtype, B, o * rank + j)", "load_elem(dtype, B, (int64_t)j * D + o)"),
+    ("merge_slice_A_ignored", "load_elem(dtype, A, ((int64_t)q * rank + j) * k + i)",
+     "load_elem(dtype, A, ((int64_t)0 * rank + j) * k + i)"),
+    ("merge_sign_dropped", "(double)sign * scale * delta", "scale * delta"),
+    ("merge_ignores_ldw", "load_elem(dtype, W, o * ldw + i)", "load_elem(dtype, W, o * k + i)"),
+    ("merge_pool_scale", "const double scale = alpha / (double)rank;", "const double scale = alpha;"),
 ]
 
 
