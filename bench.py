@@ -20,7 +20,8 @@ One JSON line goes to stdout:
              committed measurement matches the current kernel sources, else null
   cpu_baseline  the CPU oracle on the host cores on a bounded sample
 
-Other modes: --all (every workload, lines to --out); --copy-probe (plain copy
+Other modes: --all (every workload, lines to --out); --merge (lora_merge_slot
+on named projections, one line each); --copy-probe (plain copy
 kernel at the decode size and at 1 GB: the achievable HBM ceiling);
 --copy-calib MB (a plain copy of known size, the calibration run for the PMC
 byte counters); --pmc-summary (fold two rocprofv3 --pmc runs and their
@@ -265,23 +266,31 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
 
 # ----------------------------------------------------------------- CPU oracle
 
-def run_cpu_baseline(p, acct, budget_s: float = 10.0) -> dict:
+def run_cpu_baseline(p, acct, budget_s: float = 10.0, budget_1t_s: float = 3.0) -> dict:
+    """The oracle as it stands: OpenMP over rows on up to 16 host threads for
+    ~budget_s, then one thread for ~budget_1t_s; full passes of the batch."""
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     ranks = p.ranks
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.build_segments(p.ids, p.n_slots, ranks)
-        oracle.apply_rows(p.dtype, p.k, p.slice_d, ranks, p.alphas, p.A, p.B, p.ids, p.x, p.y,
-                          n_threads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+
+    def passes(n_threads, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.build_segments(p.ids, p.n_slots, ranks)
+            oracle.apply_rows(p.dtype, p.k, p.slice_d, ranks, p.alphas, p.A, p.B, p.ids, p.x, p.y,
+                              n_threads=n_threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    reps, el = passes(threads, budget_s)
+    reps1, el1 = passes(1, budget_1t_s)
     return dict(value=acct["n_valid"] * reps / el, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{reps} full passes of the {p.name} batch ({p.n_rows} rows, "
                        f"{acct['n_valid']} with an adapter): segments + fp64 apply, "
-                       f"{el:.1f} s, OpenMP over rows")
+                       f"{el:.1f} s, OpenMP over rows",
+                value_1_thread=acct["n_valid"] * reps1 / el1)
 
 
 # ----------------------------------------------------------------- modes
@@ -293,6 +302,8 @@ def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -
     log(f"[bench] {name}: {p.note}; valid rows {acct['n_valid']}, "
         f"algorithmic bytes {acct['bytes']['total'] / 1e6:.2f} MB/step")
     g = run_gpu(p, steps, warmup, rotate=rotate, dense_min=dense_min)
+    # the same step on one buffer set, cache-resident (MALL / L2 served, not HBM)
+    warm = run_gpu(p, steps, warmup, rotate=False, dense_min=dense_min, graph=False) if rotate else g
     ms = g["gpu_ms"] / steps
     ku = g["kernel_us"]
     dom = max(step_kernels(p), key=lambda k: ku[k])
@@ -328,12 +339,102 @@ def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -
         "tiles": g["tiles"],
         "roofline": roof,
         "host_wall_ms_per_step": round(g["wall_s"] * 1e3 / steps, 4),
+        "warm_ms_per_step": round(warm["gpu_ms"] / steps, 5),
+        "warm_note": "one buffer set, cache-served (not HBM)",
         "graph_ms_per_step": (round(g["graph_ms"], 5) if g["graph_ms"] is not None else None),
         "graph_tokens_per_s": (round(acct["n_valid"] / (g["graph_ms"] * 1e-3), 1)
                                if g["graph_ms"] is not None else None),
     }
     if cpu:
         line["cpu_baseline"] = run_cpu_baseline(p, acct)
+    return line
+
+
+MERGE_CASES = {
+    # name: (k, slice widths, rank)
+    "merge_q_proj_r16": (4096, [4096], 16),
+    "merge_q_proj_r64": (4096, [4096], 64),
+    "merge_q_proj_r128": (4096, [4096], 128),
+    "merge_fused_qkv_r16": (4096, [4096, 1024, 1024], 16),
+    "merge_gate_up_r64": (4096, [14336, 14336], 64),
+}
+
+
+def bench_merge(name, steps, warmup, cpu=True) -> dict:
+    """lora_merge_slot on bf16 weights of a named projection: each call reads
+    and writes the whole weight once (plus the slot's factors).  Calls alternate
+    merge and unmerge over weight copies totalling >= 512 MB (HBM-cold)."""
+    import torch
+    from rank_adapter_gemm_lora_amd import binding as lb
+    from rank_adapter_gemm_lora_amd import synth
+
+    k, slice_d, rank = MERGE_CASES[name]
+    D = sum(slice_d)
+    p = synth.make_random(0, n_rows=1, k=k, slice_d=slice_d, n_slots=1, ranks=[rank],
+                          r_max=rank, dtype="bf16")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)
+    sh = stream.cuda_stream
+    w_bytes = D * k * 2
+    n_w = max(2, math.ceil(ROTATE_BYTES / w_bytes))
+    W0 = torch.from_numpy(synth.make_base_weight(1, D, k, "bf16").view(np.int16)).to(dev)
+    Ws = [W0.clone() for _ in range(n_w)]
+    del W0
+    dA = torch.from_numpy(np.ascontiguousarray(p.A[0]).view(np.int16)).to(dev)
+    dB = torch.from_numpy(np.ascontiguousarray(p.B[0]).view(np.int16)).to(dev)
+    torch.cuda.synchronize()
+    st = lb.lora_stack_create(lb.LORA_BF16, 1, rank, k, slice_d, 1)
+    lb.lora_load_slot(st, 0, rank, 32.0, dA.data_ptr(), dB.data_ptr(), False, sh)
+
+    def call(i):
+        lb.lora_merge_slot(st, 0, Ws[i % n_w].data_ptr(), k, 1 if (i // n_w) % 2 == 0 else -1, sh)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        call(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    lb.lora_stack_destroy(st)
+    rp = (rank + 7) // 8 * 8
+    byts = 2 * w_bytes + (len(slice_d) * rank * k + D * rp) * 2
+    flops = 2 * D * k * rank
+    gbs = byts / (us * 1e-6) / 1e9
+    line = {
+        "metric": "merge: weight bytes moved per second (read + write) by lora_merge_slot",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "us_per_merge": round(us, 3), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (seeded, HBM-cold rotation)",
+        "config": {"workload": name, "k": k, "slices": slice_d, "rank": rank,
+                   "weight_copies": n_w},
+        "roofline": {"kernel": "merge_bf16_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": byts,
+                     "mean_launch_us": round(us, 3)},
+        "mfma_util": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+    }
+    if cpu:
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        n_rows = min(D, 256)
+        Wh = synth.make_base_weight(1, D, k, "bf16")
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 5.0:
+            oracle.merge("bf16", k, [n_rows], rank, 32.0, p.A[0][:1], p.B[0][:n_rows], Wh[:n_rows],
+                         1, n_threads=threads)
+            reps += 1
+        el = time.perf_counter() - t0
+        cpu_bytes = (2 * n_rows * k + rank * k + n_rows * rp) * 2
+        line["cpu_baseline"] = {"value": round(cpu_bytes * reps / el / 1e9, 3), "unit": "GB/s",
+                                "cores": threads, "kind": "oracle",
+                                "sample": f"{reps} oracle merges of the first {n_rows} rows "
+                                          f"of slice 0 in {el:.1f} s"}
     return line
 
 
@@ -447,6 +548,8 @@ def main(argv=None):
     ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-served)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--dense-min", type=int, default=None, help="SGMV threshold (rows per group)")
+    ap.add_argument("--merge", action="store_true",
+                    help="bench lora_merge_slot on the named projections instead")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=None, metavar="MB",
                     help="only run a plain device copy of MB megabytes (PMC calibration)")
@@ -475,18 +578,37 @@ def main(argv=None):
         print(json.dumps({"copy_probe": res}))
         return 0
 
+    if args.merge:
+        for i, name in enumerate(MERGE_CASES):
+            emit(bench_merge(name, args.steps, args.warmup, cpu=not args.no_cpu and i == 0),
+                 args.out)
+        return 0
     names = ["tiny_ref", "decode_bgmv", "prefill_sgmv", "mlp_gate_up", "mlp_down",
              "many_adapter"] if args.all else [args.workload]
+    lines = {}
     for name in names:
         line = bench_workload(name, args.steps, args.warmup, rotate=not args.warm,
                               cpu=not args.no_cpu and (not args.all or name == DEFAULT_WORKLOAD),
                               dense_min=args.dense_min)
-        s = json.dumps(line)
-        print(s, flush=True)
-        if args.out:
-            with open(args.out, "a") as f:
-                f.write(s + "\n")
+        lines[name] = line
+        emit(line, args.out)
+    if "mlp_gate_up" in lines and "mlp_down" in lines:
+        # one MLP layer: the gate/up stack then the down stack on the same batch
+        gu, dn = lines["mlp_gate_up"], lines["mlp_down"]
+        ms = gu["ms_per_step"] + dn["ms_per_step"]
+        rows = gu["config"]["valid_rows"]
+        emit({"metric": gu["metric"], "value": round(rows / (ms * 1e-3), 1), "unit": "tokens/s",
+              "ms_per_step": round(ms, 5), "config": {"workload": "mlp_layer (gate/up + down)",
+                                                      "valid_rows": rows}}, args.out)
     return 0
+
+
+def emit(line, out):
+    s = json.dumps(line)
+    print(s, flush=True)
+    if out:
+        with open(out, "a") as f:
+            f.write(s + "\n")
 
 
 if __name__ == "__main__":

@@ -143,6 +143,33 @@ lora_status lora_evict_slot(lora_stack *st, int slot, void *stream);
 lora_status lora_slot_info(const lora_stack *st, int slot, int *rank, float *alpha,
                            int64_t *live_params);
 
+/*
+ * Fold the adapter of one slot into a dense weight, or take it out again
+ * (page "LoRA serving: multi-adapter dynamic loading", section 1: merging an
+ * adapter into the base weight, W' = W + (alpha/r) B A, serves that one
+ * adapter at the base model's cost, and subtracting the same product unmerges;
+ * page "Multi-LoRA Serving", section 3.1: B is d x r, A is r x k).  For every
+ * row o of slice q (rows [off_q, off_q + slice_d[q])) and column i < k:
+ *
+ *      W[o][i] = round(fp32(W[o][i]) + sign * scale * sum_j B[o][j] A_q[j][i]),
+ *
+ * scale = alpha / rank (the same fp32 value the apply path uses), the sum in
+ * fp32, one rounding to the stack's dtype per element.
+ *
+ *   W      DEVICE [D][ldw] in the stack's dtype (row o = output feature, the
+ *          layout of a linear layer's weight), updated in place; columns
+ *          >= k are not touched.  16-byte aligned.
+ *   ldw    >= k, multiple of 8
+ *   sign   +1 merge, -1 unmerge
+ *
+ * Merge followed by unmerge returns W up to the two roundings.  Reads the pool
+ * in stream order (after a load on the same stream).  Errors: LORA_E_SLOT,
+ * LORA_E_EMPTY (the slot holds no adapter), LORA_E_ARG, LORA_E_UNSUPPORTED
+ * (more than 65535 * 64 rows), LORA_E_HIP.
+ */
+lora_status lora_merge_slot(const lora_stack *st, int slot, void *W, int64_t ldw, int sign,
+                            void *stream);
+
 /* ---------------------------------------------------------------- segments */
 
 /*

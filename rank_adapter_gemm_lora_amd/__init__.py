@@ -11,5 +11,5 @@ from .binding import (EXPORTS, LORA_BF16, LORA_F32, LoraError, lora_add_expand, 
                       lora_evict_slot,
                       lora_get_device_status, lora_load_slot, lora_segments_create,
                       lora_segments_destroy, lora_segments_download, lora_segments_set_dense_min,
-                      lora_segments_tile_counts, lora_slot_info, lora_stack_create,
+                      lora_segments_tile_counts, lora_slot_info, lora_merge_slot, lora_stack_create,
                       lora_stack_destroy, lora_status_string)

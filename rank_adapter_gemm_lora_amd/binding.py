@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "LORA_OK", 1: "LORA_E_ARG", 2: "LORA_E_RANK", 3: "LORA_E_SLOT
 
 # Every symbol include/lora.h declares, in header order.
 EXPORTS = ("lora_stack_create", "lora_stack_destroy", "lora_load_slot", "lora_evict_slot",
-           "lora_slot_info", "lora_segments_create", "lora_segments_destroy",
+           "lora_slot_info", "lora_merge_slot", "lora_segments_create", "lora_segments_destroy",
            "lora_segments_set_dense_min", "lora_build_segments", "lora_add_shrink",
            "lora_add_expand", "lora_apply", "lora_build_shrink", "lora_build_apply",
            "lora_segments_download",
@@ -68,6 +68,7 @@ def load(path: str | None = None):
             "lora_load_slot": [P, I, I, F, P, P, I, P],
             "lora_evict_slot": [P, I, P],
             "lora_slot_info": [P, I, P, P, P],
+            "lora_merge_slot": [P, I, P, I64, I, P],
             "lora_segments_create": [PP, I64, I],
             "lora_segments_destroy": [P],
             "lora_segments_set_dense_min": [P, I],
@@ -131,6 +132,11 @@ def lora_slot_info(stack, slot: int):
     _check(load().lora_slot_info(stack, int(slot), ctypes.byref(r), ctypes.byref(a),
                                  ctypes.byref(p)), "lora_slot_info")
     return r.value, a.value, p.value
+
+
+def lora_merge_slot(stack, slot: int, W: int, ldw: int, sign: int = 1, stream=None):
+    _check(load().lora_merge_slot(stack, int(slot), ctypes.c_void_p(W), int(ldw), int(sign),
+                                  _stream(stream)), "lora_merge_slot")
 
 
 def lora_segments_create(max_rows: int, n_slots: int):

@@ -105,6 +105,23 @@ constexpr int kFusedMaxRows = 1024;
 hipError_t launch_build_shrink(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
                                hipStream_t stream);
 hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream);
+// Merge of one slot into a dense weight (rows tiled per slice, 64 rows a tile).
+struct MergeArgs {
+    const void *A;             // the slot's A: [n_slices][r_max][k]
+    const void *B;             // the slot's B: [D][rp]
+    void *W;                   // [D][ldw], updated in place
+    int64_t ldw;
+    int64_t k;
+    int rank;                  // the slot's true rank
+    int rp;                    // its B row pitch (rank rounded up to 8)
+    int r_max;
+    float s;                   // sign * alpha / rank
+    int n_slices;
+    int64_t slice_off[LORA_MAX_SLICES + 1];
+    int tile0[LORA_MAX_SLICES + 1];   // first row tile of each slice; [n_slices] = total
+};
+int merge_row_tiles(int64_t d);
+hipError_t launch_merge(int dtype, const MergeArgs &a, hipStream_t stream);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_set_slot(int32_t *rank, float *scale, int slot, int r, float s,
                            hipStream_t stream);

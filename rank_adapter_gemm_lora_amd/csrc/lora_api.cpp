@@ -360,6 +360,47 @@ lora_status lora_slot_info(const lora_stack *st, int slot, int *rank, float *alp
     return LORA_OK;
 }
 
+lora_status lora_merge_slot(const lora_stack *st, int slot, void *W, int64_t ldw, int sign,
+                            void *stream)
+{
+    if (!st)
+        return LORA_E_ARG;
+    if (slot < 0 || slot >= st->n_slots)
+        return LORA_E_SLOT;
+    const int rank = st->h_rank[slot];
+    if (rank == 0)
+        return LORA_E_EMPTY;
+    if (!W || (reinterpret_cast<uintptr_t>(W) & 15) != 0 || ldw < st->k || ldw % 8 != 0 ||
+        (sign != 1 && sign != -1) || !current_device_is(st->device))
+        return LORA_E_ARG;
+    MergeArgs a{};
+    const size_t es = st->esize;
+    a.A = static_cast<const char *>(st->A_pool) + (size_t)slot * st->n_slices * st->r_max * st->k * es;
+    a.B = static_cast<const char *>(st->B_pool) + (size_t)slot * st->D * st->rp_max * es;
+    a.W = W;
+    a.ldw = ldw;
+    a.k = st->k;
+    a.rank = rank;
+    a.rp = (int)round_up(rank, 8);
+    a.r_max = st->r_max;
+    // the same fp32 scale the apply path reads from the slot table
+    const float scale = st->h_alpha[slot] / (float)rank;
+    a.s = sign > 0 ? scale : -scale;
+    a.n_slices = st->n_slices;
+    int64_t tiles = 0;
+    for (int q = 0; q <= st->n_slices; ++q) {
+        a.slice_off[q] = st->slice_off[q];
+        a.tile0[q] = (int)tiles;
+        if (q < st->n_slices)
+            tiles += merge_row_tiles(st->slice_d[q]);
+    }
+    if (tiles > 65535)
+        return LORA_E_UNSUPPORTED;
+    LORA_TRY(launch_merge(st->dtype == LORA_F32 ? DT_F32 : DT_BF16, a,
+                          reinterpret_cast<hipStream_t>(stream)));
+    return LORA_OK;
+}
+
 lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_slots)
 {
     if (!out)

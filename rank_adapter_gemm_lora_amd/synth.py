@@ -257,6 +257,14 @@ def with_strides(p: Problem, pad_x: int, pad_y: int, seed: int = 1) -> Problem:
     return replace(p, x=x, y=y, name=p.name + f"+ld({pad_x},{pad_y})")
 
 
+def make_base_weight(seed: int, D: int, k: int, dtype: str = "bf16", std: float = 0.02,
+                     pad: int = 0) -> np.ndarray:
+    """A seeded dense base weight [D, k + pad] (row = output feature), N(0, std),
+    for the merge path; the pad columns must come back untouched."""
+    rng = np.random.default_rng(seed)
+    return _normal(rng, (D, k + pad), std, dtype)
+
+
 def subset_rows(p: Problem, n: int) -> Problem:
     """The first n rows of ``p`` (same adapters)."""
     return replace(p, ids=p.ids[:n].copy(), x=p.x[:n].copy(), y=p.y[:n].copy(),
