@@ -21,7 +21,8 @@ One JSON line goes to stdout:
   cpu_baseline  the CPU oracle on the host cores on a bounded sample
 
 Other modes: --all (every workload, lines to --out); --merge (lora_merge_slot
-on named projections, one line each); --copy-probe (plain copy
+on named projections, one line each); --sweep (adapter count x rank against the
+base GEMM of the same layer); --copy-probe (plain copy
 kernel at the decode size and at 1 GB: the achievable HBM ceiling);
 --copy-calib MB (a plain copy of known size, the calibration run for the PMC
 byte counters); --pmc-summary (fold two rocprofv3 --pmc runs and their
@@ -438,6 +439,100 @@ def bench_merge(name, steps, warmup, cpu=True) -> dict:
     return line
 
 
+SWEEP_ADAPTERS = (1, 4, 16, 100)
+SWEEP_RANKS = (8, 16, 32, 64, 128)
+SWEEP_ROWS = (256, 4096)
+SWEEP_K = 4096
+
+
+def sweep_problem(n_rows, n_adapters, rank, seed=0):
+    """q-proj 4096 -> 4096, bf16, every row routed, ids uniform over the adapters."""
+    from rank_adapter_gemm_lora_amd import synth
+    return synth.make_random(seed, n_rows=n_rows, k=SWEEP_K, slice_d=[SWEEP_K], n_slots=n_adapters,
+                             ranks=[rank] * n_adapters, r_max=rank, dtype="bf16", alpha=32.0,
+                             name=f"sweep_n{n_rows}_a{n_adapters}_r{rank}")
+
+
+def time_base_gemm(n_rows, steps, warmup) -> float:
+    """Mean time (us) of the shared base projection y = x W^T (torch's GEMM,
+    bf16, 4096 x 4096) over W and x copies totalling >= 512 MB."""
+    import torch
+    from rank_adapter_gemm_lora_amd import synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(dev)
+    w = torch.from_numpy(synth.make_base_weight(3, SWEEP_K, SWEEP_K, "bf16").view(np.int16))
+    w = w.to(dev).view(torch.bfloat16)
+    x = torch.randn((n_rows, SWEEP_K), generator=torch.Generator().manual_seed(5)).to(dev)
+    x = x.to(torch.bfloat16)
+    per = w.numel() * 2 + x.numel() * 2 + n_rows * SWEEP_K * 2
+    n = max(2, math.ceil(ROTATE_BYTES / per))
+    ws = [w.clone() for _ in range(n)]
+    xs = [x.clone() for _ in range(n)]
+    ys = [torch.empty((n_rows, SWEEP_K), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            torch.matmul(xs[i % n], ws[i % n].t(), out=ys[i % n])
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            torch.matmul(xs[i % n], ws[i % n].t(), out=ys[i % n])
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def bench_sweep(steps, warmup, out=None, md=None) -> list:
+    """Adapter count x rank sweep of one q-proj LoRA layer (lora_build_apply,
+    HBM-cold rotation) against the base GEMM of the same layer on the same GPU."""
+    lines = []
+    for n_rows in SWEEP_ROWS:
+        base_us = time_base_gemm(n_rows, steps, warmup)
+        log(f"[sweep] base GEMM n={n_rows}: {base_us:.2f} us")
+        for n_ad in SWEEP_ADAPTERS:
+            for rank in SWEEP_RANKS:
+                p = sweep_problem(n_rows, n_ad, rank)
+                acct = accounting(p)
+                g = run_gpu(p, steps, warmup, rotate=True, graph=False)
+                us = g["gpu_ms"] * 1e3 / steps
+                line = {"metric": "sweep: one LoRA q-proj layer vs its base GEMM",
+                        "config": {"workload": p.name, "rows": n_rows, "adapters": n_ad,
+                                   "rank": rank, "k": SWEEP_K, "d": SWEEP_K},
+                        "lora_us": round(us, 3), "base_gemm_us": round(base_us, 3),
+                        "relative_throughput": round(base_us / (base_us + us), 4),
+                        "lora_hbm_gbs": round(acct["bytes"]["total"] / (us * 1e-6) / 1e9, 1),
+                        "distinct_slots": acct["distinct_slots"],
+                        "kernel_us": {k: round(v, 3) for k, v in g["kernel_us"].items()},
+                        "tiles": g["tiles"]}
+                lines.append(line)
+                emit(line, out)
+    if md:
+        with open(md, "w") as f:
+            f.write(sweep_markdown(lines))
+    return lines
+
+
+def sweep_markdown(lines) -> str:
+    rows = sorted({l["config"]["rows"] for l in lines})
+    out = []
+    for n in rows:
+        sel = [l for l in lines if l["config"]["rows"] == n]
+        base = sel[0]["base_gemm_us"]
+        out.append(f"\n### {n} rows, q-proj 4096 -> 4096 bf16; base GEMM {base:.2f} us\n")
+        out.append("LoRA step time in us (relative throughput base / (base + LoRA)):\n")
+        ranks = sorted({l["config"]["rank"] for l in sel})
+        out.append("| adapters | " + " | ".join(f"r={r}" for r in ranks) + " |")
+        out.append("|---|" + "---|" * len(ranks))
+        for a in sorted({l["config"]["adapters"] for l in sel}):
+            cells = []
+            for r in ranks:
+                l = next(l for l in sel if l["config"]["adapters"] == a and l["config"]["rank"] == r)
+                cells.append(f"{l['lora_us']:.1f} ({l['relative_throughput'] * 100:.0f}%)")
+            out.append(f"| {a} | " + " | ".join(cells) + " |")
+    return "\n".join(out) + "\n"
+
+
 def copy_probe(reps: int = 50) -> list:
     """A plain device copy at the decode step's size and at 1 GB (rotated past
     the MALL): the achievable HBM ceiling, and the calibration kernel for the
@@ -550,6 +645,9 @@ def main(argv=None):
     ap.add_argument("--dense-min", type=int, default=None, help="SGMV threshold (rows per group)")
     ap.add_argument("--merge", action="store_true",
                     help="bench lora_merge_slot on the named projections instead")
+    ap.add_argument("--sweep", action="store_true",
+                    help="adapter count x rank sweep against the base GEMM")
+    ap.add_argument("--sweep-md", default=None, help="also write the sweep as a markdown table")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=None, metavar="MB",
                     help="only run a plain device copy of MB megabytes (PMC calibration)")
@@ -578,6 +676,9 @@ def main(argv=None):
         print(json.dumps({"copy_probe": res}))
         return 0
 
+    if args.sweep:
+        bench_sweep(args.steps, args.warmup, args.out, args.sweep_md)
+        return 0
     if args.merge:
         for i, name in enumerate(MERGE_CASES):
             emit(bench_merge(name, args.steps, args.warmup, cpu=not args.no_cpu and i == 0),

@@ -52,6 +52,19 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// v, or zeros, selected per component.  Used after a load from a clamped,
+// in-bounds address: the load needs no branch around it, and a select of the
+// whole vector would be compiled as a select of addresses through scratch.
+__device__ __forceinline__ float4 keep_if(bool ok, float4 v)
+{
+    return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
+}
+
+__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v)
+{
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
 // Eight consecutive elements of a row, held in their storage format.
 template <int DT> struct Vec8;
 

@@ -29,7 +29,8 @@
 //     other with four accumulators, which keeps the register count -- and so
 //     the number of workgroups resident per CU -- where a streaming kernel
 //     needs it.  B sits in LDS as the chunk's contiguous [256 columns][rp]
-//     block, copied with 16-byte loads.
+//     block, copied with 16-byte loads; when that block would not fit beside
+//     v, the ranks go through in windows of b_win, one LDS block each.
 //   BGMV tile (<= 16 rows), vector ALU: the tile's B columns are staged in LDS
 //     in passes (bf16: 8 rank pairs, fp32: 8 ranks); each lane forms the bf16
 //     hi/lo pairs of its row's v and accumulates packed bf16 dot products
@@ -170,38 +171,47 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
             y1[nt].load(a.y, yi + 8);
         }
     }
-    // the B chunk: columns [c0, c0 + 256) of the slot are one contiguous
-    // [256][rp] block; 16-byte granules, consecutive threads on consecutive
-    // granules
-    // (granules go global -> LDS directly, 16 bytes per lane, with no register
-    // staging; thread t takes granules t, t + 256, ...  They are in flight with
-    // y while v is staged, so B, v and y share one round trip.  Granules of
-    // columns past D are not loaded: those columns are whole 64-column blocks
-    // (D % 64 == 0 on this path) whose wavefronts never read B.)
+    // the B chunk: columns [c0, c0 + 256) of the slot, ranks [w0, w0 + wl) of
+    // each column, as LDS [256][wl] (the whole [256][rp] block when the rank
+    // fits one window).  16-byte granules go global -> LDS directly, 16 bytes
+    // per lane, no register staging; thread t takes granules t, t + 256, ...
+    // The first window is in flight with y while v is staged, so B, v and y
+    // share one round trip.  Granules of columns past D are not loaded: those
+    // columns are whole 64-column blocks (D % 64 == 0 on this path) whose
+    // wavefronts never read B.
     const int64_t bchunk = (int64_t)s * a.b_slot_stride + c0 * rp;
-    const int gpc = rp >> 3;                         // granules per column
-    const int n_gran = (int)min((int64_t)kCols, a.D - c0) * gpc;
-    for (int i = 0; i < gpc; ++i) {
-        const int e = i * kCols + threadIdx.x;
-        if (e < n_gran)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(
-                    reinterpret_cast<const uint16_t *>(a.B) + bchunk + 8 * (int64_t)e),
-                (__attribute__((address_space(3))) void *)(bs + 8 * (i * kCols + 64 * wave)), 16, 0,
-                0);
-    }
+    const int ncol = (int)min((int64_t)kCols, a.D - c0);
+    const int n_win = (rp + a.b_win - 1) / a.b_win;
+    auto stage_b = [&](int w0) {
+        const int gpw = min(a.b_win, rp - w0) >> 3;   // granules per column in the window
+        const int n_gran = ncol * gpw;
+        const uint32_t m_gpw = div_magic(gpw);
+        for (int i = 0; i < gpw; ++i) {
+            const int e = i * kCols + threadIdx.x;
+            if (e < n_gran) {
+                // one window: the chunk is contiguous and granule e sits at 8 e
+                const int col = div_small(e, m_gpw), gi = e - col * gpw;
+                const int64_t off = n_win == 1 ? 8 * (int64_t)e : (int64_t)col * rp + w0 + 8 * gi;
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(
+                        reinterpret_cast<const uint16_t *>(a.B) + bchunk + off),
+                    (__attribute__((address_space(3))) void *)(bs + 8 * (i * kCols + 64 * wave)), 16, 0,
+                    0);
+            }
+        }
+    };
+    stage_b(0);
     const int q_lo = slice_of(a, c0);
     const int nq = slice_of(a, min(c0 + kCols, a.D) - 1) - q_lo + 1;
     const int pitch = nq * r;
     stage_v(a, p0, cnt, r, q_lo, nq, vs);
-    __syncthreads();   // B and v staged
-    if (!in_d)
-        return;
+    __syncthreads();   // B (first window) and v staged
     const int qq = slice_of(a, c0 + 64 * wave) - q_lo;
-    int bcol[4];                                     // LDS offset of M-tile mt's column for row m
+    // LDS column of M-tile mt for row m, in units of the window's rank pitch
+    int bcolumn[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
-        bcol[mt] = (64 * wave + 16 * (m >> 2) + 4 * mt + (m & 3)) * rp;
+        bcolumn[mt] = 64 * wave + 16 * (m >> 2) + 4 * mt + (m & 3);
 
 #pragma unroll
     for (int nt = 0; nt < MT; ++nt) {
@@ -212,28 +222,39 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
             acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int jc = 0; jc < nj; ++jc) {
-            const int jo = jc * 16 + 8 * (g & 1);
-            float f[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int j = jo + i;
-                const float v = (u < cnt && j < r) ? vs[u * pitch + qq * r + j] : 0.f;
-                f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
+        for (int w = 0; w < n_win; ++w) {
+            const int w0 = w * a.b_win, wl = min(a.b_win, rp - w0);
+            if (n_win > 1 && (nt > 0 || w > 0)) {   // (uniform) restage this window
+                __syncthreads();                    // every wavefront is done with the last one
+                stage_b(w0);
+                __syncthreads();
             }
-            uint4 vop;
-            vop.x = pack_bf16x2(f[0], f[1]);
-            vop.y = pack_bf16x2(f[2], f[3]);
-            vop.z = pack_bf16x2(f[4], f[5]);
-            vop.w = pack_bf16x2(f[6], f[7]);
+            if (!in_d)
+                continue;
+            for (int jc = w0 >> 4; jc < min(nj, (w0 + wl + 15) >> 4); ++jc) {
+                const int jo = jc * 16 + 8 * (g & 1);
+                float f[8];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const uint4 bop = jo < rp ? *reinterpret_cast<const uint4 *>(bs + bcol[mt] + jo)
+                for (int i = 0; i < 8; ++i) {
+                    const int j = jo + i;
+                    const float v = (u < cnt && j < r) ? vs[u * pitch + qq * r + j] : 0.f;
+                    f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
+                }
+                uint4 vop;
+                vop.x = pack_bf16x2(f[0], f[1]);
+                vop.y = pack_bf16x2(f[2], f[3]);
+                vop.z = pack_bf16x2(f[4], f[5]);
+                vop.w = pack_bf16x2(f[6], f[7]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const uint4 bop = jo < w0 + wl
+                                          ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + (jo - w0))
                                           : make_uint4(0, 0, 0, 0);
-                acc[mt] = mfma_bf16_16x16x32(bop, vop, acc[mt]);
+                    acc[mt] = mfma_bf16_16x16x32(bop, vop, acc[mt]);
+                }
             }
         }
-        if (u < cnt) {
+        if (in_d && u < cnt) {
             float f[16];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -309,11 +330,6 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
         acc[c] = 0.f;
 
     for (int j0 = 0; j0 < rp; j0 += kPassElems) {
-        if (j0 > 0) {
-#pragma unroll
-            for (int q4 = 0; q4 < kWords; ++q4)
-                w[q4] = b_word<DT>(a, bslot, gcol, rp, j0 + kElemsPerWord * q4);
-        }
 #pragma unroll
         for (int q4 = 0; q4 < kWords; ++q4) {
             bsh[(4 * q4 + 0) * kCols + threadIdx.x] = w[q4].x;
@@ -321,7 +337,15 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
             bsh[(4 * q4 + 2) * kCols + threadIdx.x] = w[q4].z;
             bsh[(4 * q4 + 3) * kCols + threadIdx.x] = w[q4].w;
         }
-        __syncthreads();   // v and this pass of B staged
+        // v and this pass of B staged.  The barriers order LDS only, so the
+        // next pass's B, issued before this pass's arithmetic, stays in flight
+        // across them.
+        lds_barrier();
+        if (j0 + kPassElems < rp) {
+#pragma unroll
+            for (int q4 = 0; q4 < kWords; ++q4)
+                w[q4] = b_word<DT>(a, bslot, gcol, rp, j0 + kPassElems + kElemsPerWord * q4);
+        }
         if constexpr (DT == DT_BF16) {
             const int np = min(kPassElems, rp - j0) / 2;
             for (int pp = 0; pp < np; ++pp) {
@@ -356,7 +380,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                 }
             }
         }
-        __syncthreads();   // bsh is restaged by the next pass
+        lds_barrier();   // bsh is restaged by the next pass
     }
     merge16<DT>(a, yi, h0, h1, y0, y1, scale, acc);
 }

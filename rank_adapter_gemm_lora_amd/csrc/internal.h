@@ -24,10 +24,6 @@ constexpr int kTileSgmv = 1;
 constexpr int kMaxKSplit = 16;      // most k-splits of one shrink
 constexpr int kMaxSliceRank = 256;  // n_slices * r_max bound (LDS staging of v)
 constexpr int kChunkRows = 256;     // rows per chunk of the large-batch grouping
-// Dense groups of batches up to 4096 rows are cut into 16-row tiles (more
-// workgroups for few rows), of larger batches into 64-row tiles (each B chunk
-// and A row then serves 64 rows).
-inline int sgmv_rows_for(int64_t n_rows) { return n_rows <= 4096 ? kBgmvTileRows : kSgmvTileRows; }
 
 // Device counts written by the segment builder.
 enum : int {
@@ -86,6 +82,7 @@ struct ApplyArgs {
     int ks;                    // k-splits of the shrink
     int mfma_ok;               // dense tiles may use MFMA (bf16, 64-aligned slices)
     int sgmv_rows;             // rows per dense tile of this batch (16 or 64)
+    int b_win;                 // expand (MFMA): ranks of B staged in LDS at once (multiple of 16)
     int lds_v_off;             // expand: dynamic LDS byte offsets of v and B staging
     int lds_b_off;
     int lds_bytes;             // expand: dynamic LDS bytes

@@ -38,10 +38,27 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 // split's partials once per column chunk, so the split count also shrinks as
 // the batch grows (at most 4096 / rows).  Depends only on the shape, never on
 // the ids.
-int choose_ks(int64_t k, int64_t n_rows)
+// Rows per dense tile.  Dense groups of batches up to 4096 rows are cut into
+// 16-row tiles (more workgroups for few rows), of larger batches into 64-row
+// tiles (each B chunk and A row then serves 64 rows).  Stacks of rank 32 and
+// up take 64-row tiles from 1024 rows on when the batch still gives 512 or
+// more expand workgroups: a 16-row tile would reread more of B and A than it
+// moves of y and x.
+int sgmv_rows_for(const lora_stack *st, int64_t n_rows)
+{
+    if (n_rows > 4096)
+        return kSgmvTileRows;
+    if (n_rows > kFusedMaxRows && st->r_max >= 32 && n_rows * st->D >= ((int64_t)1 << 23))
+        return kSgmvTileRows;
+    return kBgmvTileRows;
+}
+
+// k-splits of the shrink: about 256 tile workgroups in all (tile_rows-row
+// tiles), at least 512 k per split, at most kMaxKSplit, a power of two.
+int choose_ks(int64_t k, int64_t n_rows, int tile_rows)
 {
     int64_t ks = std::max<int64_t>(1, k / 512);
-    ks = std::min<int64_t>(ks, std::max<int64_t>(1, 4096 / std::max<int64_t>(1, n_rows)));
+    ks = std::min<int64_t>(ks, std::max<int64_t>(1, 256 * tile_rows / std::max<int64_t>(1, n_rows)));
     ks = std::min<int64_t>(ks, kMaxKSplit);
     // powers of two keep blocks of one split on one XCD
     int64_t p = 1;
@@ -109,10 +126,12 @@ int expand_nq_max(const lora_stack *st)
 }
 
 // Dynamic LDS of the expand: row indices, the slot table (few slots), v of a
-// tile for the slices of one chunk, and B (a whole [256][rp] chunk for MFMA
-// tiles, one 8 KB pass for vector tiles).
+// tile for the slices of one chunk, and B (for MFMA tiles a [256][b_win] block
+// of the chunk, b_win ranks at a time: the whole rank when it fits, else the
+// widest multiple of 16 that does; one 8 KB pass for vector tiles).  b_win 0:
+// no window fits.
 struct ExpandLds {
-    int v_off, b_off, bytes;
+    int v_off, b_off, bytes, b_win;
 };
 
 ExpandLds expand_lds(const lora_stack *st, bool mfma, int tile_rows)
@@ -120,18 +139,29 @@ ExpandLds expand_lds(const lora_stack *st, bool mfma, int tile_rows)
     const int64_t table = st->n_slots <= kExpandTableSlots ? 8 * kExpandTableSlots : 0;
     const int64_t rows = mfma ? tile_rows : kBgmvTileRows;
     const int64_t v_bytes = round_up(rows * expand_nq_max(st) * st->r_max * 4, 16);
-    const int64_t b_bytes = std::max<int64_t>(8 * kExpandCols * 4,
-                                              mfma ? (int64_t)kExpandCols * st->rp_max * 2 : 0);
     ExpandLds l;
     l.v_off = (int)(kExpandLdsTable + table);
     l.b_off = (int)(l.v_off + v_bytes);
+    l.b_win = 0;
+    int64_t b_bytes = 8 * kExpandCols * 4;
+    if (mfma) {
+        const int64_t room = kExpandLdsMax - l.b_off;
+        for (int64_t w = round_up(st->rp_max, 16); w >= 16; w -= 16) {
+            const int64_t need = (int64_t)kExpandCols * std::min<int64_t>(w, st->rp_max) * 2;
+            if (std::max(need, b_bytes) <= room) {
+                l.b_win = (int)w;
+                b_bytes = std::max(need, b_bytes);
+                break;
+            }
+        }
+    }
     l.bytes = (int)(l.b_off + b_bytes);
     return l;
 }
 
 // MFMA tiles need bf16, slices made of whole 64-column blocks, and the v of a
-// 64-row tile plus a [256][rp] chunk of B within the expand's LDS budget;
-// otherwise the dense tiles of a batch are served by the vector code.
+// 64-row tile plus at least a 16-rank window of B within the expand's LDS
+// budget; otherwise the dense tiles of a batch are served by the vector code.
 bool stack_has_mfma_path(const lora_stack *st)
 {
     if (st->dtype != LORA_BF16)
@@ -139,7 +169,7 @@ bool stack_has_mfma_path(const lora_stack *st)
     for (int q = 0; q < st->n_slices; ++q)
         if (st->slice_d[q] % 64 != 0)
             return false;
-    return expand_lds(st, true, kSgmvTileRows).bytes <= kExpandLdsMax;
+    return expand_lds(st, true, kSgmvTileRows).b_win > 0;
 }
 
 lora_status check_apply_common(const lora_stack *st, const lora_segments *seg)
@@ -172,12 +202,13 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     a.b_slot_stride = st->D * st->rp_max;
     a.vpart = st->vpart;
     a.max_rows = st->max_rows;
-    a.ks = choose_ks(st->k, seg->n_rows);
+    a.sgmv_rows = sgmv_rows_for(st, seg->n_rows);
+    a.ks = choose_ks(st->k, seg->n_rows, a.sgmv_rows);
     a.mfma_ok = stack_has_mfma_path(st) ? 1 : 0;
-    a.sgmv_rows = sgmv_rows_for(seg->n_rows);
     // v staging sized for this batch's dense tile height (16 rows up to 4096
     // rows): a smaller footprint lets more expand workgroups share a CU
-    const ExpandLds l = expand_lds(st, a.mfma_ok != 0, sgmv_rows_for(seg->n_rows));
+    const ExpandLds l = expand_lds(st, a.mfma_ok != 0, a.sgmv_rows);
+    a.b_win = l.b_win > 0 ? l.b_win : 16;   // (unused by the vector code)
     a.lds_v_off = l.v_off;
     a.lds_b_off = l.b_off;
     a.lds_bytes = l.bytes;
@@ -489,7 +520,7 @@ SegBuildArgs make_seg_args(const lora_stack *st, const int32_t *ids, int64_t n_r
     a.n_slots = st->n_slots;
     a.slot_rank = st->d_rank;
     a.dense_min = seg->dense_min;
-    a.sgmv_rows = sgmv_rows_for(n_rows);
+    a.sgmv_rows = sgmv_rows_for(st, n_rows);
     a.perm = seg->perm;
     a.seg_off = seg->seg_off;
     a.active = seg->active;
@@ -518,7 +549,8 @@ bool fused_build_pays(const lora_stack *st, int64_t n_rows)
 {
     if (n_rows <= 0 || n_rows > kFusedMaxRows)
         return false;
-    return (int64_t)choose_ks(st->k, n_rows) * max_tiles_for(n_rows, st->n_slots) <=
+    return (int64_t)choose_ks(st->k, n_rows, sgmv_rows_for(st, n_rows)) *
+               max_tiles_for(n_rows, st->n_slots) <=
            kFusedMaxBlocks;
 }
 

@@ -47,18 +47,6 @@ __device__ __forceinline__ int a_unit(int j, int u) { return j * 16 + (u ^ (2 * 
 // LDS index (in 16-byte units) of unit u (4 fp32 columns) of product row m.
 __device__ __forceinline__ int c_unit(int m, int u) { return m * 32 + (u ^ (4 * ((m >> 2) & 3))); }
 
-// v, or zeros: selected per component (a select of the whole vector is
-// compiled as a select of addresses through scratch memory).
-__device__ __forceinline__ float4 keep_if(bool ok, float4 v)
-{
-    return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
-}
-
-__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v)
-{
-    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
-}
-
 // bf16: NKC chunks of 32 rank values (rank <= 32 * NKC).
 template <int NKC>
 __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(MergeArgs a)

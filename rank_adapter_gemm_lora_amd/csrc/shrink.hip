@@ -101,78 +101,72 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
     }
 }
 
-// MT: M-tiles (16 rows each) of the tile shape this launch serves -- 1 for
-// the 16-row tiles of batches up to 4096 rows, 4 for 64-row tiles -- so each
-// instantiation holds only the registers its shape needs.  kSt: 8-element k
-// groups per lane per step; steps run with two register buffers (the loads of
-// step i + 1 in flight during the MFMAs of step i).
-template <int MT>
+// 16-row SGMV tile (batches up to 4096 rows): M = the tile's rows, N = up to
+// kNT N-tiles (slice, 16-rank chunk) per pass over the k-range, K = k; the
+// four wavefronts split the workgroup's k-range and their partial tiles are
+// summed in LDS in wavefront order.  A pass handles NTV N-tiles, a template
+// parameter: 1 when the whole rank is one N-tile (rank <= 16, one slice: the
+// common decode shape loads nothing it drops), else kNT.  kSt 8-element k
+// groups per lane per step (4 for one N-tile, 2 for kNT: the two register
+// buffers, loads of step i + 1 in flight during the MFMAs of step i, then fit
+// without spilling).  Every load reads an in-bounds address (clamped unit;
+// rank rows past r read from the pool's start) and its value is selected
+// afterwards, so no branch surrounds a load.  (Measured: branches around the
+// loads, or a select of "load or zero" on a runtime tile count, made the
+// compiler drain the loads in flight at every step.)
 __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, int p0,
                                  int cnt, int ks)
 {
-    constexpr int kSt = MT == 1 ? 4 : 2;
     __shared__ f32x4_t red[4][kNT * 64];   // [wave][tt * 64 + lane]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
-    int64_t xrow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        xrow[mt] = (int64_t)rows[min(16 * mt + m, cnt - 1)] * a.ldx;   // clamp: dropped later
+    const int64_t xrow = (int64_t)rows[min(m, cnt - 1)] * a.ldx;   // clamp: dropped later
     const int nj = (r + 15) >> 4;
     const int NT = a.n_slices * nj;
     const int64_t g8 = a.k >> 3;
     const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
     const int64_t wb = gb + (ge - gb) * wave / 4, we = gb + (ge - gb) * (wave + 1) / 4;
-    const int n_mt = (cnt + 15) >> 4;
 
-    for (int t0 = 0; t0 < NT; t0 += kNT) {
-        int64_t arow[kNT];
-        bool aok[kNT];
+    auto pass = [&](int t0, auto ntv_tag) {
+        constexpr int NTV = decltype(ntv_tag)::value;
+        constexpr int kSt = NTV == 1 ? 4 : 2;   // register buffers: 2 x kSt x (1 + NTV) granules
+        int64_t arow[NTV];
+        bool aok[NTV];
 #pragma unroll
-        for (int tt = 0; tt < kNT; ++tt) {
-            const int t = t0 + tt;
+        for (int tt = 0; tt < NTV; ++tt) {
+            const int t = min(t0 + tt, NT - 1);   // N-tiles past the last repeat it
             const int q = t / nj, jc = t - q * nj;
             const int j = jc * 16 + m;
-            aok[tt] = t < NT && j < r;
+            aok[tt] = t0 + tt < NT && j < r;
+            // rank rows past r (and N-tiles past the last) read the pool's start, dropped
             arow[tt] = aok[tt] ? (((int64_t)s * a.n_slices + q) * a.r_max + j) * a.k : 0;
         }
-        f32x4_t acc[MT][kNT];
+        f32x4_t acc[NTV];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int tt = 0; tt < kNT; ++tt)
-                acc[mt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < NTV; ++tt)
+            acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // steps of 4 * kSt units (8 k each), two register buffers: the loads of
-        // step i + 1 are in flight while the MFMAs of step i run
-        auto load_step = [&](int64_t u0, uint4 (&xs)[MT][kSt], uint4 (&as)[kNT][kSt]) {
+        auto load_step = [&](int64_t u0, uint4 (&xs)[kSt], uint4 (&as)[NTV][kSt]) {
 #pragma unroll
             for (int st = 0; st < kSt; ++st) {
                 const int64_t unit = u0 + 4 * st + g;   // lanes g = 0..3: 64 contiguous bytes of a row
                 const bool ok = unit < we;
+                const int64_t cu = min(unit, g8 - 1);
+                xs[st] = keep_if(ok, load16(a.x, xrow + cu * 8));
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    xs[mt][st] = (ok && mt < n_mt) ? load16(a.x, xrow[mt] + unit * 8)
-                                                  : make_uint4(0, 0, 0, 0);
-#pragma unroll
-                for (int tt = 0; tt < kNT; ++tt)
-                    as[tt][st] = (ok && aok[tt]) ? load16(a.A, arow[tt] + unit * 8)
-                                                 : make_uint4(0, 0, 0, 0);
+                for (int tt = 0; tt < NTV; ++tt)
+                    as[tt][st] = keep_if(ok && aok[tt], load16(a.A, arow[tt] + cu * 8));
             }
         };
-        auto mma_step = [&](const uint4 (&xs)[MT][kSt], const uint4 (&as)[kNT][kSt]) {
+        auto mma_step = [&](const uint4 (&xs)[kSt], const uint4 (&as)[NTV][kSt]) {
 #pragma unroll
             for (int st = 0; st < kSt; ++st)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    if (mt < n_mt) {
-#pragma unroll
-                        for (int tt = 0; tt < kNT; ++tt)
-                            acc[mt][tt] = mfma_bf16_16x16x32(xs[mt][st], as[tt][st], acc[mt][tt]);
-                    }
+                for (int tt = 0; tt < NTV; ++tt)
+                    acc[tt] = mfma_bf16_16x16x32(xs[st], as[tt][st], acc[tt]);
         };
         const int64_t n_steps = (we - wb + 4 * kSt - 1) / (4 * kSt);
-        uint4 xa[MT][kSt], aa[kNT][kSt], xb[MT][kSt], ab[kNT][kSt];
+        uint4 xa[kSt], aa[NTV][kSt], xb[kSt], ab[NTV][kSt];
         if (n_steps > 0)
             load_step(wb, xa, aa);
         for (int64_t i = 0; i < n_steps; i += 2) {
@@ -186,35 +180,42 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
             mma_step(xb, ab);
         }
 
-        // fixed-order sum of the four k-quarters, one M-tile at a time
+        // fixed-order sum of the four k-quarters
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            if (mt >= n_mt)
-                break;
-#pragma unroll
-            for (int tt = 0; tt < kNT; ++tt)
-                red[wave][tt * 64 + lane] = acc[mt][tt];
-            __syncthreads();
-            {
-                const int e = threadIdx.x;            // kNT * 64 == 256 entries
+        for (int tt = 0; tt < NTV; ++tt)
+            red[wave][tt * 64 + lane] = acc[tt];
+        __syncthreads();
+        {
+            const int e = threadIdx.x;            // kNT * 64 == 256 entries
+            const int ln = e & 63, tt = e >> 6;
+            if (tt < NTV && t0 + tt < NT) {
                 const f32x4_t v = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
-                const int ln = e & 63, tt = e >> 6;
                 const int t = t0 + tt;
                 const int q = t / nj, jc = t - q * nj;
                 const int j = jc * 16 + (ln & 15);
-                if (t < NT && j < r) {
+                if (j < r) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int u = 16 * mt + 4 * (ln >> 4) + i;
+                        const int u = 4 * (ln >> 4) + i;
                         if (u < cnt)
                             v_out(a, ks, p0 + u)[q * a.r_max + j] = v[i];
                     }
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();
+    };
+    for (int t0 = 0; t0 < NT; t0 += kNT) {
+        // (uniform) one N-tile (rank <= 16, one slice: the common decode
+        // shape) or a full pass; a partial last pass loads its empty N-tiles
+        // from row r - 1 and drops them
+        if (NT - t0 == 1)
+            pass(t0, std::integral_constant<int, 1>());
+        else
+            pass(t0, std::integral_constant<int, kNT>());
     }
 }
+
 static_assert(kNT * 64 == 256, "one reduction entry per thread");
 
 // 64-row tiles (batches above 4096 rows).  Each wavefront owns 16 rows of the
@@ -364,7 +365,7 @@ __device__ __forceinline__ void shrink_tile(const ApplyArgs &a, const int32_t *r
             if constexpr (MT == 4)
                 sgmv_shrink_tile_tall(a, rows, s, r, p0, cnt, ks);
             else
-                sgmv_shrink_tile<MT>(a, rows, s, r, p0, cnt, ks);
+                sgmv_shrink_tile(a, rows, s, r, p0, cnt, ks);
             return;
         }
     }

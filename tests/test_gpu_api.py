@@ -46,6 +46,12 @@ EDGE_CASES = {
     "max_slots": dict(n_rows=3000, k=64, slice_d=[64], n_slots=1024, ranks=[8] * 1024,
                       r_max=8, p_none=0.1),
     "single_row": dict(n_rows=1, k=128, slice_d=[64], n_slots=1, ranks=[16], r_max=16),
+    # rank windows of the MFMA expand: B of a 256-column chunk does not fit
+    # LDS beside v in one piece (64-row tiles above 4096 rows: 48-rank windows)
+    "rank128_tall": dict(n_rows=4500, k=256, slice_d=[256], n_slots=2, ranks=[128, 100],
+                         r_max=128, p_none=0.05),
+    "rank128_slices": dict(n_rows=300, k=128, slice_d=[192, 64], n_slots=2, ranks=[128, 72],
+                           r_max=128),
 }
 
 
