@@ -22,7 +22,8 @@ One JSON line goes to stdout:
 
 Other modes: --all (every workload, lines to --out); --merge (lora_merge_slot
 on named projections, one line each); --sweep (adapter count x rank against the
-base GEMM of the same layer); --copy-probe (plain copy
+base GEMM of the same layer); --residency (adapter load bandwidth from the
+pinned host tier, decode steps under Zipf adapter churn); --copy-probe (plain copy
 kernel at the decode size and at 1 GB: the achievable HBM ceiling);
 --copy-calib MB (a plain copy of known size, the calibration run for the PMC
 byte counters); --pmc-summary (fold two rocprofv3 --pmc runs and their
@@ -533,6 +534,120 @@ def sweep_markdown(lines) -> str:
     return "\n".join(out) + "\n"
 
 
+def bench_residency(steps, warmup, out=None) -> list:
+    """Adapter residency on the decode projection (4096 -> 4096, bf16, rank 16,
+    16 GPU slots, 200 registered adapters in the pinned host tier):
+    (1) host -> HBM load bandwidth: batches of 16 adapters none of which is
+        resident, so every map_batch call loads 16 adapters (GPU time of the
+        copies, HIP events on the stream);
+    (2) decode steps under Zipf(1.1) adapter churn: each step maps a batch of
+        256 rows over 16 adapters drawn Zipf without replacement, then runs
+        lora_build_apply; mean step time, hit rate and loads per step against
+        the same steps with every adapter already resident."""
+    import torch
+    from rank_adapter_gemm_lora_amd import binding as lb
+    from rank_adapter_gemm_lora_amd import synth
+
+    k, D, rank, n_slots, n_ad, n_rows = 4096, 4096, 16, 16, 200, 256
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)
+    sh = stream.cuda_stream
+    rng = np.random.default_rng(0)
+    st = lb.lora_stack_create(lb.LORA_BF16, n_slots, rank, k, [D], n_rows)
+    seg = lb.lora_segments_create(n_rows, n_slots)
+    m = lb.lora_residency_create(st, n_ad)
+    ad_bytes = rank * (k + D) * 2
+    for aid in range(n_ad):
+        A = synth.f32_to_bf16_bits(rng.standard_normal((1, rank, k), dtype=np.float32) * 0.02)
+        B = synth.f32_to_bf16_bits(rng.standard_normal((D, rank), dtype=np.float32) * 0.02)
+        lb.lora_residency_register(m, aid, rank, 32.0, A.ctypes.data, B.ctypes.data)
+    lines = []
+
+    # (1) cold loads: 16 fresh adapters per call
+    groups = [list(range(i, i + n_slots)) for i in range(0, n_ad - n_slots + 1, n_slots)]
+    for g in groups[:2]:
+        lb.lora_residency_map_batch(m, g, sh)
+    torch.cuda.synchronize()
+    s0 = lb.lora_residency_stats(m)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    calls = 0
+    for rep in range(max(1, steps // len(groups))):
+        for g in groups[2:] + groups[:2]:
+            lb.lora_residency_map_batch(m, g, sh)
+            calls += 1
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s1 = lb.lora_residency_stats(m)
+    loads = s1["loads"] - s0["loads"]
+    byts = s1["bytes_loaded"] - s0["bytes_loaded"]
+    gpu_s = e0.elapsed_time(e1) * 1e-3
+    line = {"metric": "residency: adapter load bandwidth, pinned host tier -> HBM",
+            "value": round(byts / gpu_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+            "loads": loads, "bytes_per_load": ad_bytes, "us_per_load": round(gpu_s * 1e6 / loads, 2),
+            "host_wall_us_per_load": round(wall * 1e6 / loads, 2), "map_calls": calls,
+            "config": {"workload": "residency_cold_loads", "k": k, "d": D, "rank": rank,
+                       "slots": n_slots, "registered": n_ad}}
+    lines.append(line)
+    emit(line, out)
+
+    # (2) Zipf churn vs all-resident steps
+    x = torch.from_numpy(synth._normal(rng, (n_rows, k), 1.0, "bf16").view(np.int16)).to(dev)
+    y = torch.from_numpy(synth._normal(rng, (n_rows, D), 1.0, "bf16").view(np.int16)).to(dev)
+    p = synth.zipf_probs(n_ad, 1.1)
+    batches = []
+    for _ in range(steps):
+        use = rng.choice(n_ad, size=n_slots, replace=False, p=p)
+        batches.append(rng.choice(use, size=n_rows).astype(np.int64))
+    ids_dev = torch.empty(n_rows, dtype=torch.int32, device=dev)
+    pinned = torch.empty(n_rows, dtype=torch.int32, pin_memory=True)
+
+    def step(rows):
+        ids = lb.lora_residency_map_batch(m, rows, sh)
+        pinned.numpy()[:] = ids
+        with torch.cuda.stream(stream):
+            ids_dev.copy_(pinned, non_blocking=True)
+        lb.lora_build_apply(st, y.data_ptr(), D, x.data_ptr(), k, ids_dev.data_ptr(), n_rows, seg, sh)
+        stream.synchronize()   # the pinned staging buffer is reused by the next step
+
+    for rows in batches[:warmup]:
+        step(rows)
+    s0 = lb.lora_residency_stats(m)
+    t0 = time.perf_counter()
+    for rows in batches:
+        step(rows)
+    churn = (time.perf_counter() - t0) / len(batches)
+    s1 = lb.lora_residency_stats(m)
+    # the same loop with one fixed resident set: no loads
+    hot = batches[0]
+    step(hot)
+    t0 = time.perf_counter()
+    for _ in batches:
+        step(hot)
+    resident = (time.perf_counter() - t0) / len(batches)
+    uses = (s1["hits"] - s0["hits"]) + (s1["loads"] - s0["loads"])
+    line = {"metric": "residency: decode step under Zipf(1.1) adapter churn (host wall, map + upload + apply)",
+            "value": round(churn * 1e6, 2), "unit": "us/step", "higher_is_better": False,
+            "n_gpus": 1, "steps": len(batches),
+            "all_resident_us_per_step": round(resident * 1e6, 2),
+            "hit_rate": round((s1["hits"] - s0["hits"]) / max(1, uses), 4),
+            "loads_per_step": round((s1["loads"] - s0["loads"]) / len(batches), 3),
+            "config": {"workload": "residency_zipf_churn", "rows": n_rows, "k": k, "d": D,
+                       "rank": rank, "slots": n_slots, "registered": n_ad,
+                       "adapters_per_batch": n_slots}}
+    lines.append(line)
+    emit(line, out)
+    torch.cuda.synchronize()
+    lb.lora_residency_destroy(m)
+    lb.lora_segments_destroy(seg)
+    lb.lora_stack_destroy(st)
+    return lines
+
+
 def copy_probe(reps: int = 50) -> list:
     """A plain device copy at the decode step's size and at 1 GB (rotated past
     the MALL): the achievable HBM ceiling, and the calibration kernel for the
@@ -648,6 +763,8 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="adapter count x rank sweep against the base GEMM")
     ap.add_argument("--sweep-md", default=None, help="also write the sweep as a markdown table")
+    ap.add_argument("--residency", action="store_true",
+                    help="adapter load bandwidth and Zipf churn through the residency manager")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=None, metavar="MB",
                     help="only run a plain device copy of MB megabytes (PMC calibration)")
@@ -676,6 +793,9 @@ def main(argv=None):
         print(json.dumps({"copy_probe": res}))
         return 0
 
+    if args.residency:
+        bench_residency(args.steps, args.warmup, args.out)
+        return 0
     if args.sweep:
         bench_sweep(args.steps, args.warmup, args.out, args.sweep_md)
         return 0

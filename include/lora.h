@@ -61,7 +61,9 @@ typedef enum lora_status {
     LORA_E_NOMEM = 6,     /* device allocation failed                        */
     LORA_E_HIP = 7,       /* a HIP runtime call failed                       */
     LORA_E_BAD_IDS = 8,   /* (reported by lora_get_device_status)            */
-    LORA_E_UNSUPPORTED = 9 /* shape or option outside this build's limits    */
+    LORA_E_UNSUPPORTED = 9, /* shape or option outside this build's limits   */
+    LORA_E_CAPACITY = 10, /* more adapters than the slots or host tier hold  */
+    LORA_E_NOT_FOUND = 11 /* adapter id not registered                       */
 } lora_status;
 
 /* Path of the row tiles of one segment (see lora_segments_set_dense_min). */
@@ -274,6 +276,102 @@ lora_status lora_build_shrink(const lora_stack *st, const void *x, int64_t ldx,
 lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const void *x,
                              int64_t ldx, const int32_t *ids, int64_t n_rows, lora_segments *seg,
                              void *stream);
+
+/* --------------------------------------------------------------- residency */
+
+/*
+ * Adapter residency around one stack: a host tier of registered adapters in
+ * pinned memory (max_cpu_adapters of them), GPU residency of up to n_slots
+ * (the stack's slots) with least-recently-used eviction, and the mapping of a
+ * batch's per-row adapter ids to slot ids.  Page "LoRA hot-loading and adapter
+ * routing", adapter-lifecycle section (load on first use after a rank check;
+ * past the limit the least recently used adapter is unloaded and reloaded on
+ * its next use); page "Multi-LoRA Serving: one base, many adapters", section
+ * 3.2 (adapters resident on the GPU with an optional CPU-side cache: max_loras
+ * and max_cpu_loras) and section 6 (a batch with more distinct adapters than
+ * max_loras cannot run in one step); page "LoRA serving: multi-adapter dynamic
+ * loading", section 4 (loading copies A and B to the GPU; unloading is
+ * immediate).
+ *
+ * Not thread-safe.  All GPU work goes on the stream passed to each call; the
+ * caller runs the batch's lora_build_segments / lora_apply on that stream
+ * too (or orders the streams), so loads and evictions land between batches.
+ */
+typedef struct lora_residency lora_residency;
+
+/* Counters of lora_residency_stats, by index. */
+enum {
+    LORA_RES_HITS = 0,          /* adapter uses served by a resident slot        */
+    LORA_RES_LOADS = 1,         /* host -> GPU loads (misses)                    */
+    LORA_RES_EVICTIONS = 2,     /* slots freed for another adapter or unregister */
+    LORA_RES_HOST_DROPS = 3,    /* host-tier entries dropped to admit a new one  */
+    LORA_RES_BYTES_LOADED = 4,  /* adapter bytes copied host -> GPU (true rank)  */
+    LORA_RES_HOST_ENTRIES = 5,  /* registered adapters now in the host tier      */
+    LORA_RES_RESIDENT = 6,      /* adapters now resident on the GPU              */
+    LORA_RES_NSTATS = 7
+};
+
+/*
+ * Create a manager.  With a stack (st != NULL) the manager owns the stack's
+ * slots that are empty now (slots the caller already loaded are never used)
+ * and the shape arguments are ignored.  With st == NULL it only plans: same
+ * decisions and slot ids, no data moved, no GPU call (n_slots, r_max, k,
+ * n_slices, slice_d, dtype give the shape, as in lora_stack_create).
+ * max_cpu_adapters >= 1 bounds the host tier.  The stack must outlive the
+ * manager.  Errors: LORA_E_ARG, LORA_E_NOMEM.
+ */
+lora_status lora_residency_create(lora_residency **out, lora_stack *st, int n_slots, int r_max,
+                                  int64_t k, int n_slices, const int64_t *slice_d,
+                                  lora_dtype dtype, int max_cpu_adapters);
+
+/* Free the manager and its pinned host tier (waits for copies still reading
+ * it).  The slots it loaded stay loaded in the stack.  NULL is accepted. */
+lora_status lora_residency_destroy(lora_residency *m);
+
+/*
+ * Register an adapter under a caller-chosen id >= 0: A [n_slices][rank][k]
+ * and B [D][rank] (HOST pointers, dense, true rank, the stack's dtype) are
+ * copied into the pinned host tier; the call returns once they are copied.
+ * The rank is checked here (page "Multi-LoRA Serving", section 6: an adapter
+ * above the rank cap is refused at load).  When the host tier is full the
+ * least recently used adapter that is not resident on the GPU is dropped
+ * (LORA_E_CAPACITY when every entry is resident); the registration itself
+ * counts as a use.  A host tier of at least n_slots plus the distinct adapters
+ * of one batch never drops an adapter the next batch needs while the caller
+ * registers it.  Errors: LORA_E_ARG,
+ * LORA_E_RANK, LORA_E_OCCUPIED (id already registered), LORA_E_CAPACITY,
+ * LORA_E_NOMEM, LORA_E_HIP.
+ */
+lora_status lora_residency_register(lora_residency *m, int64_t adapter_id, int rank, float alpha,
+                                    const void *A, const void *B);
+
+/* Drop an adapter: its slot (if resident) is evicted in stream order and its
+ * host copy freed once no copy reads it.  Errors: LORA_E_ARG,
+ * LORA_E_NOT_FOUND, LORA_E_HIP. */
+lora_status lora_residency_unregister(lora_residency *m, int64_t adapter_id, void *stream);
+
+/*
+ * Map one batch: row_adapter (HOST int64 [n_rows], -1 = no adapter) ->
+ * ids_out (HOST int32 [n_rows], the slot of each row's adapter, -1 for none),
+ * the ids lora_build_segments takes.  Every adapter the batch uses is made
+ * resident first: already resident is a hit; otherwise it goes to an empty
+ * slot (lowest index) or replaces the least recently used resident adapter
+ * this batch does not use (ties: lowest slot), copied from the host tier in
+ * stream order.  "Used" advances once per batch (and per registration).
+ * Checked before anything
+ * changes: LORA_E_NOT_FOUND (an id not registered), LORA_E_CAPACITY (more
+ * distinct adapters than usable slots: split the batch), LORA_E_ARG.  Also
+ * LORA_E_HIP.
+ */
+lora_status lora_residency_map_batch(lora_residency *m, const int64_t *row_adapter, int64_t n_rows,
+                                     int32_t *ids_out, void *stream);
+
+/* Slot holding an adapter (-1 when registered but not resident).  Errors:
+ * LORA_E_ARG, LORA_E_NOT_FOUND. */
+lora_status lora_residency_slot_of(const lora_residency *m, int64_t adapter_id, int *slot);
+
+/* Counters (HOST int64 [LORA_RES_NSTATS], indices above).  Errors: LORA_E_ARG. */
+lora_status lora_residency_stats(const lora_residency *m, int64_t *stats);
 
 /* --------------------------------------------------------------- inspection */
 

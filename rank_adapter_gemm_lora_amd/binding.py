@@ -17,15 +17,22 @@ from .build import LIB_PATH
 LORA_F32, LORA_BF16 = 0, 1
 LORA_OK, LORA_E_ARG, LORA_E_RANK, LORA_E_SLOT, LORA_E_OCCUPIED, LORA_E_EMPTY = 0, 1, 2, 3, 4, 5
 LORA_E_NOMEM, LORA_E_HIP, LORA_E_BAD_IDS, LORA_E_UNSUPPORTED = 6, 7, 8, 9
+LORA_E_CAPACITY, LORA_E_NOT_FOUND = 10, 11
+RES_STATS = ("hits", "loads", "evictions", "host_drops", "bytes_loaded", "host_entries",
+             "resident")
 STATUS_NAMES = {0: "LORA_OK", 1: "LORA_E_ARG", 2: "LORA_E_RANK", 3: "LORA_E_SLOT",
                 4: "LORA_E_OCCUPIED", 5: "LORA_E_EMPTY", 6: "LORA_E_NOMEM", 7: "LORA_E_HIP",
-                8: "LORA_E_BAD_IDS", 9: "LORA_E_UNSUPPORTED"}
+                8: "LORA_E_BAD_IDS", 9: "LORA_E_UNSUPPORTED", 10: "LORA_E_CAPACITY",
+                11: "LORA_E_NOT_FOUND"}
 
 # Every symbol include/lora.h declares, in header order.
 EXPORTS = ("lora_stack_create", "lora_stack_destroy", "lora_load_slot", "lora_evict_slot",
            "lora_slot_info", "lora_merge_slot", "lora_segments_create", "lora_segments_destroy",
            "lora_segments_set_dense_min", "lora_build_segments", "lora_add_shrink",
            "lora_add_expand", "lora_apply", "lora_build_shrink", "lora_build_apply",
+           "lora_residency_create", "lora_residency_destroy", "lora_residency_register",
+           "lora_residency_unregister", "lora_residency_map_batch", "lora_residency_slot_of",
+           "lora_residency_stats",
            "lora_segments_download",
            "lora_get_device_status",
            "lora_segments_tile_counts", "lora_status_string")
@@ -78,6 +85,13 @@ def load(path: str | None = None):
             "lora_apply": [P, P, I64, P, I64, P, P],
             "lora_build_shrink": [P, P, I64, P, I64, P, P],
             "lora_build_apply": [P, P, I64, P, I64, P, I64, P, P],
+            "lora_residency_create": [PP, P, I, I, I64, I, P, I, I],
+            "lora_residency_destroy": [P],
+            "lora_residency_register": [P, I64, I, F, P, P],
+            "lora_residency_unregister": [P, I64, P],
+            "lora_residency_map_batch": [P, P, I64, P, P],
+            "lora_residency_slot_of": [P, I64, P],
+            "lora_residency_stats": [P, P],
             "lora_segments_download": [P, P, P, P, P, P],
             "lora_get_device_status": [P, P, P],
             "lora_segments_tile_counts": [P, P, P, P],
@@ -214,6 +228,56 @@ def lora_segments_tile_counts(seg, stream=None):
     _check(load().lora_segments_tile_counts(seg, ctypes.byref(b), ctypes.byref(s),
                                             _stream(stream)), "lora_segments_tile_counts")
     return b.value, s.value
+
+
+def lora_residency_create(stack, max_cpu_adapters: int, n_slots: int = 0, r_max: int = 0,
+                          k: int = 0, slice_d=(), dtype: int = LORA_BF16):
+    """With a stack the shape arguments are ignored; stack=None plans only."""
+    sd = (ctypes.c_int64 * max(1, len(slice_d)))(*[int(d) for d in slice_d])
+    out = ctypes.c_void_p()
+    _check(load().lora_residency_create(ctypes.byref(out), stack, int(n_slots), int(r_max), int(k),
+                                        len(slice_d), ctypes.cast(sd, ctypes.c_void_p) if slice_d
+                                        else None, int(dtype), int(max_cpu_adapters)),
+           "lora_residency_create")
+    return out
+
+
+def lora_residency_destroy(m):
+    _check(load().lora_residency_destroy(m), "lora_residency_destroy")
+
+
+def lora_residency_register(m, adapter_id: int, rank: int, alpha: float, A: int, B: int):
+    _check(load().lora_residency_register(m, int(adapter_id), int(rank), float(alpha),
+                                          ctypes.c_void_p(A), ctypes.c_void_p(B)),
+           "lora_residency_register")
+
+
+def lora_residency_unregister(m, adapter_id: int, stream=None):
+    _check(load().lora_residency_unregister(m, int(adapter_id), _stream(stream)),
+           "lora_residency_unregister")
+
+
+def lora_residency_map_batch(m, row_adapter, stream=None):
+    """row_adapter: int64 sequence (-1 = none) -> numpy int32 slot ids."""
+    import numpy as np
+    ra = np.ascontiguousarray(row_adapter, dtype=np.int64)
+    ids = np.empty(ra.shape[0], np.int32)
+    _check(load().lora_residency_map_batch(m, ra.ctypes.data, ra.shape[0], ids.ctypes.data,
+                                           _stream(stream)), "lora_residency_map_batch")
+    return ids
+
+
+def lora_residency_slot_of(m, adapter_id: int) -> int:
+    v = ctypes.c_int(0)
+    _check(load().lora_residency_slot_of(m, int(adapter_id), ctypes.byref(v)),
+           "lora_residency_slot_of")
+    return v.value
+
+
+def lora_residency_stats(m) -> dict:
+    a = (ctypes.c_int64 * len(RES_STATS))()
+    _check(load().lora_residency_stats(m, ctypes.cast(a, ctypes.c_void_p)), "lora_residency_stats")
+    return dict(zip(RES_STATS, list(a)))
 
 
 def lora_status_string(status: int) -> str:

@@ -119,6 +119,37 @@ struct MergeArgs {
 };
 int merge_row_tiles(int64_t d);
 hipError_t launch_merge(int dtype, const MergeArgs &a, hipStream_t stream);
+lora_status load_slot(lora_stack *st, int slot, int rank, float alpha, const void *A, const void *B,
+                      hipMemcpyKind kind, bool sync, hipStream_t stream);
+
+// Loads of several adapters into free slots by one kernel that reads their A
+// and B straight from mapped pinned host memory (device-side pointers).
+constexpr int kGatherJobs = 16;
+struct GatherJob {
+    const void *A;   // [n_slices][rank][k], device-accessible
+    const void *B;   // [D][rank], device-accessible
+    int slot;
+    int rank;
+    float scale;     // alpha / rank
+    int pad;
+};
+struct GatherArgs {
+    void *A_pool;
+    void *B_pool;
+    int32_t *rank_tab;
+    float *scale_tab;
+    int64_t k;
+    int64_t D;
+    int n_slices;
+    int r_max;
+    int rp_max;
+    int esize;
+    int n_jobs;
+    GatherJob job[kGatherJobs];
+};
+hipError_t launch_gather_load(const GatherArgs &g, hipStream_t stream);
+// Record a host-gathered load in the stack's host state (after the launch).
+void note_loaded(lora_stack *st, int slot, int rank, float alpha);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_set_slot(int32_t *rank, float *scale, int slot, int r, float s,
                            hipStream_t stream);

@@ -219,6 +219,58 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
 
 }  // namespace
 
+// Load one adapter into an empty slot, in stream order.  kind: where A and B
+// are (host memory is pinned when the copy is to be asynchronous); sync: wait
+// for the copies before returning (the caller's buffers are then free).
+lora_status lora::load_slot(lora_stack *st, int slot, int rank, float alpha, const void *A,
+                            const void *B, hipMemcpyKind kind, bool sync, hipStream_t s)
+{
+    if (!st)
+        return LORA_E_ARG;
+    if (slot < 0 || slot >= st->n_slots)
+        return LORA_E_SLOT;
+    if (rank < 1 || rank > st->r_max)
+        return LORA_E_RANK;
+    if (st->h_rank[slot] != 0)
+        return LORA_E_OCCUPIED;
+    if (!A || !B || !std::isfinite(alpha) || !current_device_is(st->device))
+        return LORA_E_ARG;
+
+    const size_t es = st->esize;
+    char *a_dst = static_cast<char *>(st->A_pool) +
+                  (size_t)slot * st->n_slices * st->r_max * st->k * es;
+    char *b_dst = static_cast<char *>(st->B_pool) + (size_t)slot * st->D * st->rp_max * es;
+    const int rp = (int)round_up(rank, 8);
+
+    // the kernels read A rows up to r_max and B ranks up to rp: those past the
+    // rank must be zero (nothing to clear when the copies cover them)
+    if (rank < st->r_max)
+        LORA_TRY(launch_zero(a_dst, (size_t)st->n_slices * st->r_max * st->k * es, s));
+    if (rp != rank)
+        LORA_TRY(launch_zero(b_dst, (size_t)st->D * rp * es, s));
+    // A: [n_slices][rank][k] -> [n_slices][r_max][k]
+    LORA_TRY(hipMemcpy2DAsync(a_dst, (size_t)st->r_max * st->k * es, A, (size_t)rank * st->k * es,
+                              (size_t)rank * st->k * es, st->n_slices, kind, s));
+    // B: [D][rank] -> [D][rp], rp = rank rounded up to 8 (rank-contiguous rows)
+    if (rp == rank)
+        LORA_TRY(hipMemcpyAsync(b_dst, B, (size_t)st->D * rank * es, kind, s));
+    else
+        LORA_TRY(hipMemcpy2DAsync(b_dst, (size_t)rp * es, B, (size_t)rank * es, (size_t)rank * es,
+                                  st->D, kind, s));
+    LORA_TRY(launch_set_slot(st->d_rank, st->d_scale, slot, rank, alpha / (float)rank, s));
+    if (sync)
+        LORA_TRY(hipStreamSynchronize(s));
+    st->h_rank[slot] = rank;
+    st->h_alpha[slot] = alpha;
+    return LORA_OK;
+}
+
+void lora::note_loaded(lora_stack *st, int slot, int rank, float alpha)
+{
+    st->h_rank[slot] = rank;
+    st->h_alpha[slot] = alpha;
+}
+
 extern "C" {
 
 const char *lora_status_string(lora_status s)
@@ -234,6 +286,8 @@ const char *lora_status_string(lora_status s)
     case LORA_E_HIP: return "HIP runtime error";
     case LORA_E_BAD_IDS: return "batch contained ids naming no loaded slot";
     case LORA_E_UNSUPPORTED: return "shape outside the limits of this build";
+    case LORA_E_CAPACITY: return "more adapters than the slots or the host tier hold";
+    case LORA_E_NOT_FOUND: return "adapter id not registered";
     }
     return "unknown status";
 }
@@ -319,42 +373,9 @@ lora_status lora_stack_destroy(lora_stack *st)
 lora_status lora_load_slot(lora_stack *st, int slot, int rank, float alpha, const void *A,
                            const void *B, int src_is_host, void *stream)
 {
-    if (!st)
-        return LORA_E_ARG;
-    if (slot < 0 || slot >= st->n_slots)
-        return LORA_E_SLOT;
-    if (rank < 1 || rank > st->r_max)
-        return LORA_E_RANK;
-    if (st->h_rank[slot] != 0)
-        return LORA_E_OCCUPIED;
-    if (!A || !B || !std::isfinite(alpha) || !current_device_is(st->device))
-        return LORA_E_ARG;
-
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const hipMemcpyKind kind = src_is_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
-    const size_t es = st->esize;
-    char *a_dst = static_cast<char *>(st->A_pool) +
-                  (size_t)slot * st->n_slices * st->r_max * st->k * es;
-    char *b_dst = static_cast<char *>(st->B_pool) + (size_t)slot * st->D * st->rp_max * es;
-    const int rp = (int)round_up(rank, 8);
-
-    LORA_TRY(launch_zero(a_dst, (size_t)st->n_slices * st->r_max * st->k * es, s));
-    LORA_TRY(launch_zero(b_dst, (size_t)st->D * st->rp_max * es, s));
-    // A: [n_slices][rank][k] -> [n_slices][r_max][k]
-    LORA_TRY(hipMemcpy2DAsync(a_dst, (size_t)st->r_max * st->k * es, A, (size_t)rank * st->k * es,
-                              (size_t)rank * st->k * es, st->n_slices, kind, s));
-    // B: [D][rank] -> [D][rp], rp = rank rounded up to 8 (rank-contiguous rows)
-    if (rp == rank)
-        LORA_TRY(hipMemcpyAsync(b_dst, B, (size_t)st->D * rank * es, kind, s));
-    else
-        LORA_TRY(hipMemcpy2DAsync(b_dst, (size_t)rp * es, B, (size_t)rank * es, (size_t)rank * es,
-                                  st->D, kind, s));
-    LORA_TRY(launch_set_slot(st->d_rank, st->d_scale, slot, rank, alpha / (float)rank, s));
-    if (src_is_host)
-        LORA_TRY(hipStreamSynchronize(s));
-    st->h_rank[slot] = rank;
-    st->h_alpha[slot] = alpha;
-    return LORA_OK;
+    return lora::load_slot(st, slot, rank, alpha, A, B,
+                           src_is_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice,
+                           src_is_host != 0, reinterpret_cast<hipStream_t>(stream));
 }
 
 lora_status lora_evict_slot(lora_stack *st, int slot, void *stream)

@@ -1,6 +1,7 @@
 // pool.hip -- stream-ordered maintenance of the adapter pool: zero-filling a
-// slot's region before a load, and writing the device slot table (rank,
-// scale) so that load -> apply -> evict on one stream need no host sync.
+// slot's region before a load, writing the device slot table (rank, scale) so
+// that load -> apply -> evict on one stream need no host sync, and loading
+// several adapters at once straight from mapped pinned host memory.
 #include "internal.h"
 
 namespace lora {
@@ -22,7 +23,66 @@ __global__ void set_slot_kernel(int32_t *rank, float *scale, int slot, int r, fl
     }
 }
 
+// One slot per blockIdx.y.  A: the pool region [n_slices][r_max][k] in 16-byte
+// units, rows below the rank copied from the source, the rest zero (k % 8 == 0:
+// no unit straddles a row).  B: [D][rp], rp = rank rounded up to 8; with
+// rank == rp the region is the source itself, else element by element with
+// zeros in the ranks past the rank.  Block 0 of the slot writes the slot table.
+__global__ __launch_bounds__(256) void gather_load_kernel(GatherArgs g)
+{
+    const GatherJob &j = g.job[blockIdx.y];
+    const int es = g.esize;
+    const int rp = (j.rank + 7) & ~7;
+    const int64_t row_elems = g.k, slice_elems = (int64_t)g.r_max * g.k;
+    const int64_t a_units = (int64_t)g.n_slices * slice_elems * es / 16;
+    const int epu = 16 / es;   // elements per 16-byte unit
+    uint4 *adst = reinterpret_cast<uint4 *>(static_cast<char *>(g.A_pool) +
+                                            (size_t)j.slot * g.n_slices * slice_elems * es);
+    const char *asrc = static_cast<const char *>(j.A);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < a_units; u += stride) {
+        const int64_t e = u * epu;
+        const int64_t q = e / slice_elems, rem = e - q * slice_elems;
+        const int64_t row = rem / row_elems, col = rem - row * row_elems;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < j.rank)
+            v = *reinterpret_cast<const uint4 *>(asrc + (((q * j.rank + row) * g.k) + col) * es);
+        adst[u] = v;
+    }
+    char *bdst = static_cast<char *>(g.B_pool) + (size_t)j.slot * g.D * g.rp_max * es;
+    const char *bsrc = static_cast<const char *>(j.B);
+    if (rp == j.rank) {
+        const int64_t b_units = g.D * j.rank * es / 16;
+        for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < b_units; u += stride)
+            reinterpret_cast<uint4 *>(bdst)[u] = reinterpret_cast<const uint4 *>(bsrc)[u];
+    } else {
+        const int64_t n = g.D * rp;
+        for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+            const int64_t o = e / rp, c = e - o * rp;
+            if (es == 2) {
+                const uint16_t v = c < j.rank ? reinterpret_cast<const uint16_t *>(bsrc)[o * j.rank + c] : 0;
+                reinterpret_cast<uint16_t *>(bdst)[e] = v;
+            } else {
+                const uint32_t v = c < j.rank ? reinterpret_cast<const uint32_t *>(bsrc)[o * j.rank + c] : 0u;
+                reinterpret_cast<uint32_t *>(bdst)[e] = v;
+            }
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        g.rank_tab[j.slot] = j.rank;
+        g.scale_tab[j.slot] = j.scale;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gather_load(const GatherArgs &g, hipStream_t stream)
+{
+    if (g.n_jobs <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(gather_load_kernel, dim3(64, g.n_jobs), dim3(256), 0, stream, g);
+    return hipGetLastError();
+}
 
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream)
 {

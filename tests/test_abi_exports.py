@@ -30,7 +30,7 @@ def test_library_exports_every_symbol():
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(12):
         assert binding.lora_status_string(s) not in ("", "unknown status")
     assert binding.lora_status_string(99) == "unknown status"
 
