@@ -10,15 +10,18 @@
 // Serving", section 3.1: B is d x r, A is r x k.
 //
 // The pass reads and writes W once and the product has only r terms per
-// element, so it is bound by HBM.  One workgroup owns a 64 x 128 tile of W that
-// lies inside one slice.  Loads are issued adapter first, W last: a load
-// counter wait for the adapter data then does not also wait for W, whose
-// loads stay in flight while the product is formed.
-//   bf16: the 64 x 128 x r product runs on the matrix cores.  The rank rows of
-//   A are staged in LDS (XOR-swizzled 16-byte units) so that each lane can read
-//   its 8 rank values of one column; the fp32 result goes through LDS once more
-//   so that W is read and written in 16-byte runs along its rows.
-//   fp32: the same tile on the vector ALUs, in rank chunks of 16.
+// element, so it is bound by HBM.  W is cut into 64 x 128 tiles that each lie
+// inside one slice.  Loads are issued adapter first, W last: a load counter
+// wait for the adapter data then does not also wait for W, whose loads stay in
+// flight while the product is formed.
+//   bf16: the 64 x 128 x r product of a tile runs on the matrix cores, and the
+//   fp32 result goes through LDS once more so that W is read and written in
+//   16-byte units along its rows.  Weights of fewer than kMergeStreamTiles
+//   tiles take one tile per workgroup; larger ones a persistent grid whose
+//   workgroups walk runs of tiles with the next tile's loads in flight.
+//   fp32: one tile per workgroup on the vector ALUs, in rank chunks of 16.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -30,6 +33,12 @@ namespace {
 constexpr int kMergeRows = 64;
 constexpr int kMergeCols = 128;
 constexpr int kMergeThreads = 256;
+constexpr int kMergeCus = 256;       // compute units of the part
+constexpr int kMergeWgPerCu = 2;     // persistent bf16 workgroups per compute unit
+// Weights of at least this many 64 x 128 tiles take the persistent kernel
+// (measured: it wins on a 28672 x 4096 weight, 14336 tiles, and loses on a
+// 4096 x 4096 one, 2048 tiles, where a workgroup gets too few tiles to pipeline).
+constexpr int64_t kMergeStreamTiles = 4096;
 
 __device__ __forceinline__ void merge_tile_origin(const MergeArgs &a, int &q, int64_t &o0)
 {
@@ -45,9 +54,14 @@ __device__ __forceinline__ void merge_tile_origin(const MergeArgs &a, int &q, in
 __device__ __forceinline__ int a_unit(int j, int u) { return j * 16 + (u ^ (2 * ((j >> 3) & 3))); }
 
 // LDS index (in 16-byte units) of unit u (4 fp32 columns) of product row m.
+// The four row groups one accumulator store covers land on distinct banks.
 __device__ __forceinline__ int c_unit(int m, int u) { return m * 32 + (u ^ (4 * ((m >> 2) & 3))); }
 
-// bf16: NKC chunks of 32 rank values (rank <= 32 * NKC).
+// bf16, one tile per workgroup (weights of fewer than kMergeStreamTiles tiles):
+// NKC chunks of 32 rank values (rank <= 32 * NKC).  The slot's A rows for the
+// tile's 128 columns are staged row-major in LDS (XOR-swizzled 16-byte units)
+// and each lane gathers its 8 rank values of one column with 2-byte reads;
+// wavefront w owns columns 32 w .. + 31 and all 64 rows.
 template <int NKC>
 __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(MergeArgs a)
 {
@@ -162,6 +176,178 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(MergeArgs a)
     }
 }
 
+// Column slab, slice and first row of tile t.  Tiles run slab-major: the row
+// tiles of all slices for columns [0, 128), then for [128, 256), ...
+__device__ __forceinline__ void merge_tile(const MergeArgs &a, int64_t t, int64_t &c0, int &q, int64_t &o0)
+{
+    const int rt_total = a.tile0[a.n_slices];
+    const int64_t slab = t / rt_total;
+    const int rt = (int)(t - slab * rt_total);
+    c0 = slab * kMergeCols;
+    q = 0;
+    while (q + 1 < a.n_slices && rt >= a.tile0[q + 1])
+        ++q;
+    o0 = a.slice_off[q] + (int64_t)(rt - a.tile0[q]) * kMergeRows;
+}
+
+// bf16, large weights: NKC chunks of 32 rank values.  Persistent: each
+// workgroup walks a contiguous run of tiles, so consecutive tiles mostly share
+// the column slab and slice, and the slot's A for that slab is staged in LDS
+// once -- transposed, [128 columns][ranks], so each lane's matrix-core operand
+// (8 rank values of one column) is one 16-byte LDS read.  While a tile is
+// computed, the next tile's B rows and W are already loading.  Wavefront w owns rows
+// 16 w .. 16 w + 15 of a tile and all 128 columns (8 N-blocks), so each B row
+// is loaded once.  The fp32 product goes through LDS so W is read and written
+// in 256-byte row runs.
+template <int NKC>
+__global__ __launch_bounds__(kMergeThreads) void merge_bf16_stream_kernel(MergeArgs a)
+{
+    constexpr int kRp = 32 * NKC + 8;              // A^T row pitch in elements (16-byte pad)
+    __shared__ uint4 at_lds[kMergeCols * kRp / 8];  // A^T [128][kRp] bf16
+    __shared__ uint4 c_lds[kMergeRows * kMergeCols / 4];   // fp32 product [64][128], swizzled
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int su = tid & 15;                       // 16-byte unit of a tile row
+    const uint16_t *B = static_cast<const uint16_t *>(a.B);
+    uint16_t *W = static_cast<uint16_t *>(a.W);
+    uint16_t *at = reinterpret_cast<uint16_t *>(at_lds);
+    float *cs = reinterpret_cast<float *>(c_lds);
+
+    const int64_t n_slabs = (a.k + kMergeCols - 1) / kMergeCols;
+    const int64_t T = n_slabs * a.tile0[a.n_slices];
+    const int64_t t_begin = (int64_t)blockIdx.x * T / gridDim.x;
+    const int64_t t_end = ((int64_t)blockIdx.x + 1) * T / gridDim.x;
+    if (t_begin >= t_end)
+        return;
+
+    // this thread's four W units of a tile: rows o0 + tid / 16 + 16 p, columns
+    // c0 + 8 su .. + 7 (clamped in-bounds addresses; units past the tile unused)
+    auto load_w = [&](int64_t c0, int64_t o0, int64_t o_end, uint4 (&w)[4]) {
+        const int64_t scol = c0 + 8 * su, ccol = scol < a.k ? scol : a.k - 8;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int64_t o = o0 + (tid >> 4) + 16 * p;
+            w[p] = load16(W, min(o, o_end - 1) * a.ldw + ccol);
+        }
+    };
+
+    // matrix-core row operand of a tile: B rows o0 + 16 wave + lane % 16, rank
+    // values 32 c + 8 (lane / 16) .. + 7 (the pool pads each row to rp with zeros)
+    auto load_b = [&](int64_t o0, int64_t o_end, uint4 (&bop)[NKC]) {
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) {
+            const int64_t o = o0 + 16 * wave + (lane & 15);
+            const int g = 4 * c + (lane >> 4);
+            const uint4 v = load16(B, min(o, o_end - 1) * a.rp + 8 * min(g, a.rp / 8 - 1));
+            bop[c] = keep_if(o < o_end && 8 * g < a.rp, v);
+        }
+    };
+
+    int64_t c0, o0;
+    int q;
+    merge_tile(a, t_begin, c0, q, o0);
+    uint4 bop[NKC], w_cur[4];
+    load_b(o0, a.slice_off[q + 1], bop);
+    load_w(c0, o0, a.slice_off[q + 1], w_cur);
+    int64_t staged_c0 = -1;
+    int staged_q = -1;
+
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int64_t o_end = a.slice_off[q + 1];
+        // the next tile's B and W, in flight while this one is computed (issued
+        // after this tile's, so waiting for this tile's never waits for them)
+        int64_t nc0 = c0, no0 = o0;
+        int nq = q;
+        uint4 b_next[NKC], w_next[4];
+        if (t + 1 < t_end) {
+            merge_tile(a, t + 1, nc0, nq, no0);
+            load_b(no0, a.slice_off[nq + 1], b_next);
+            load_w(nc0, no0, a.slice_off[nq + 1], w_next);
+        }
+        // (uniform) new slab or slice: stage its A rows, transposed
+        if (c0 != staged_c0 || q != staged_q) {
+            if (staged_q >= 0)
+                lds_barrier();   // every wavefront is done with the previous A^T
+            const uint16_t *A = static_cast<const uint16_t *>(a.A) + (int64_t)q * a.r_max * a.k;
+            const int64_t scol = c0 + 8 * su;
+            const bool col_ok = scol < a.k;
+            const int64_t ccol = col_ok ? scol : a.k - 8;
+            uint4 v[2 * NKC];
+#pragma unroll
+            for (int p = 0; p < 2 * NKC; ++p) {
+                const int j = (tid >> 4) + 16 * p;
+                v[p] = keep_if(j < a.rank && col_ok, load16(A, (int64_t)min(j, a.rank - 1) * a.k + ccol));
+            }
+#pragma unroll
+            for (int p = 0; p < 2 * NKC; ++p) {
+                const int j = (tid >> 4) + 16 * p;
+                const uint32_t wd[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    at[(8 * su + e) * kRp + j] = (uint16_t)(e & 1 ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu);
+            }
+            lds_barrier();
+            staged_c0 = c0;
+            staged_q = q;
+        }
+
+        f32x4_t acc[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+            acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const uint4 col = *reinterpret_cast<const uint4 *>(
+                    at + (16 * nb + (lane & 15)) * kRp + 32 * c + 8 * (lane >> 4));
+                acc[nb] = mfma_bf16_16x16x32(bop[c], col, acc[nb]);
+            }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const int col = 16 * nb + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * wave + 4 * (lane >> 4) + i;
+                cs[c_unit(m, col >> 2) * 4 + (col & 3)] = acc[nb][i];
+            }
+        }
+        lds_barrier();
+
+        const int64_t scol = c0 + 8 * su;
+        const bool col_ok = scol < a.k;
+        const float4 *c4 = reinterpret_cast<const float4 *>(c_lds);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int m = (tid >> 4) + 16 * p;
+            const int64_t o = o0 + m;
+            if (o >= o_end || !col_ok)
+                continue;
+            const float4 lo = c4[c_unit(m, 2 * su)], hi = c4[c_unit(m, 2 * su + 1)];
+            const float d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const uint32_t ww[4] = {w_cur[p].x, w_cur[p].y, w_cur[p].z, w_cur[p].w};
+            float f[8];
+#pragma unroll
+            for (int m2 = 0; m2 < 4; ++m2) {
+                f[2 * m2] = fmaf(a.s, d[2 * m2], bf16_lo(ww[m2]));
+                f[2 * m2 + 1] = fmaf(a.s, d[2 * m2 + 1], bf16_hi(ww[m2]));
+            }
+            Vec8<DT_BF16>::store(W, o * a.ldw + scol, f);
+        }
+        lds_barrier();   // the product buffer is rewritten by the next tile
+
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            w_cur[p] = w_next[p];
+#pragma unroll
+        for (int c = 0; c < NKC; ++c)
+            bop[c] = b_next[c];
+        c0 = nc0;
+        o0 = no0;
+        q = nq;
+    }
+}
+
 // fp32: rank chunks of 16 staged in LDS, 4 rows x 8 columns per thread.
 __global__ __launch_bounds__(kMergeThreads) void merge_f32_kernel(MergeArgs a)
 {
@@ -244,13 +430,26 @@ hipError_t launch_merge(int dtype, const MergeArgs &a, hipStream_t stream)
         return hipSuccess;
     if (dtype == DT_F32) {
         hipLaunchKernelGGL(merge_f32_kernel, grid, block, 0, stream, a);
-    } else {
-        switch ((a.rank + 31) / 32) {
+        return hipGetLastError();
+    }
+    const int64_t tiles = (int64_t)grid.x * grid.y;
+    const int nkc = (a.rank + 31) / 32;
+    if (tiles < kMergeStreamTiles) {
+        switch (nkc) {
         case 1: hipLaunchKernelGGL(merge_bf16_kernel<1>, grid, block, 0, stream, a); break;
         case 2: hipLaunchKernelGGL(merge_bf16_kernel<2>, grid, block, 0, stream, a); break;
         case 3: hipLaunchKernelGGL(merge_bf16_kernel<3>, grid, block, 0, stream, a); break;
         default: hipLaunchKernelGGL(merge_bf16_kernel<4>, grid, block, 0, stream, a); break;
         }
+        return hipGetLastError();
+    }
+    // persistent grid: kMergeWgPerCu workgroups per compute unit, each a run of tiles
+    const dim3 pgrid((unsigned)std::min<int64_t>(tiles, (int64_t)kMergeWgPerCu * kMergeCus));
+    switch (nkc) {
+    case 1: hipLaunchKernelGGL(merge_bf16_stream_kernel<1>, pgrid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(merge_bf16_stream_kernel<2>, pgrid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(merge_bf16_stream_kernel<3>, pgrid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(merge_bf16_stream_kernel<4>, pgrid, block, 0, stream, a); break;
     }
     return hipGetLastError();
 }

@@ -114,6 +114,8 @@ WORKLOAD_MERGES = {
     "fused_qkv_r16": (4096, [4096, 1024, 1024], [16], 16, None),
     "gate_up_r64": (4096, [14336, 14336], [64, 8], 64, 600),
     "up_8192_28672_r16": (8192, [28672], [16], 16, 300),
+    # >= 4096 tiles (the persistent kernel) with ragged slabs, slices and rank
+    "ragged_stream_r40": (136, [131000, 72], [40], 40, 600),
 }
 
 
