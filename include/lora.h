@@ -293,9 +293,14 @@ lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const v
  * loading", section 4 (loading copies A and B to the GPU; unloading is
  * immediate).
  *
- * Not thread-safe.  All GPU work goes on the stream passed to each call; the
- * caller runs the batch's lora_build_segments / lora_apply on that stream
- * too (or orders the streams), so loads and evictions land between batches.
+ * Not thread-safe; one manager per stack.  All GPU work goes on the stream
+ * passed to each call; the caller runs the batch's lora_build_segments /
+ * lora_apply on that stream too (or orders the streams), so loads and
+ * evictions land between batches.  Direct lora_load_slot / lora_evict_slot
+ * calls on the stack are followed at the next map_batch: a slot the caller
+ * loaded is left to the caller, one the caller emptied becomes usable, and an
+ * adapter whose slot the caller evicted is loaded again when next used.
+ * After LORA_E_HIP the manager's view of the slots is undefined: destroy it.
  */
 typedef struct lora_residency lora_residency;
 

@@ -173,6 +173,30 @@ void displace(lora_residency *m, int slot)
     m->stats[LORA_RES_EVICTIONS] += 1;
 }
 
+// Follow direct calls on the stack made since the last batch: a slot the
+// caller loaded becomes the caller's; a slot the caller emptied (evicted, or
+// never the manager's) becomes usable; an adapter whose slot the caller
+// evicted is no longer resident.
+void follow_stack(lora_residency *m)
+{
+    if (!m->st)
+        return;
+    for (int sl = 0; sl < m->n_slots; ++sl) {
+        const bool loaded = m->st->h_rank[sl] != 0;
+        const int64_t a = m->slot_adapter[sl];
+        if (a == -1 && loaded) {
+            m->slot_adapter[sl] = -2;
+        } else if (a == -2 && !loaded) {
+            m->slot_adapter[sl] = -1;
+        } else if (a >= 0 && !loaded) {
+            auto it = m->host.find(a);
+            if (it != m->host.end())
+                it->second.slot = -1;
+            m->slot_adapter[sl] = -1;
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -319,6 +343,7 @@ lora_status lora_residency_map_batch(lora_residency *m, const int64_t *row_adapt
 {
     if (!m || n_rows < 0 || (n_rows > 0 && (!row_adapter || !ids_out)))
         return LORA_E_ARG;
+    follow_stack(m);
     // the batch's distinct adapters, in order of first use; checked before any change
     std::vector<int64_t> distinct;
     std::unordered_map<int64_t, int> seen;

@@ -122,3 +122,34 @@ def test_caller_slots_are_kept_and_unregister_evicts():
     finally:
         lb.lora_residency_destroy(m)
         lb.lora_stack_destroy(st)
+
+
+def test_direct_stack_calls_are_followed():
+    k, slice_d = 64, [64]
+    A, B, alphas = _adapters("bf16", 3, k, slice_d, [8, 8, 8], seed=6)
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    st = lb.lora_stack_create(lb.LORA_BF16, 3, 8, k, slice_d, 8)
+    m = lb.lora_residency_create(st, 8)
+    ptr = lambda a: np.ascontiguousarray(a).ctypes.data
+    try:
+        for aid in range(3):
+            lb.lora_residency_register(m, aid, 8, 32.0, ptr(A[aid]), ptr(B[aid]))
+        note("residency follows direct stack calls")
+        # the caller takes slot 0 after the manager was created
+        lb.lora_load_slot(st, 0, 8, 32.0, ptr(A[0]), ptr(B[0]), True, stream)
+        with pytest.raises(lb.LoraError) as e:
+            lb.lora_residency_map_batch(m, [0, 1, 2], stream)
+        assert e.value.status == lb.LORA_E_CAPACITY
+        ids = lb.lora_residency_map_batch(m, [1, 2], stream)
+        assert sorted(ids.tolist()) == [1, 2]
+        # the caller evicts one of the manager's slots: that adapter is reloaded on use
+        lb.lora_evict_slot(st, int(ids[0]), stream)
+        assert lb.lora_residency_map_batch(m, [1], stream).tolist() == [int(ids[0])]
+        assert lb.lora_slot_info(st, int(ids[0]))[0] == 8
+        # the caller frees slot 0: three distinct adapters fit again
+        lb.lora_evict_slot(st, 0, stream)
+        assert sorted(lb.lora_residency_map_batch(m, [0, 1, 2], stream).tolist()) == [0, 1, 2]
+        torch.cuda.synchronize(DEV)
+    finally:
+        lb.lora_residency_destroy(m)
+        lb.lora_stack_destroy(st)
