@@ -131,18 +131,21 @@ def test_build_apply_repeated_layers():
         run.close()
 
 
-def test_build_apply_graph_replay_any_mix():
+@pytest.mark.parametrize("n_rows", [256, 3000])
+def test_build_apply_graph_replay_any_mix(n_rows):
     """The launch shapes depend only on the batch shape, so one captured HIP
     graph of lora_build_apply serves every adapter mix: replays with new ids
     (and a fresh base y) each match the oracle, segments included.  The new
-    inputs are copied in eagerly between replays, with synchronisations."""
-    base = synth.make_random(41, n_rows=256, k=512, slice_d=[512], n_slots=8, ranks=[16] * 8,
+    inputs are copied in eagerly between replays, with synchronisations.
+    256 rows: grouping inside the shrink (two launches); 3000 rows: the chunked
+    grouping, shrink and expand (five launches)."""
+    base = synth.make_random(41, n_rows=n_rows, k=512, slice_d=[512], n_slots=8, ranks=[16] * 8,
                              r_max=16, p_none=1 / 9)
     run = GpuRun(base)
     try:
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
-        note("graph capture of lora_build_apply")
+        note(f"graph capture of lora_build_apply, {n_rows} rows")
         with torch.cuda.graph(graph):
             lb.lora_build_apply(run.stack, run.y.data_ptr(), base.ldy, run.x.data_ptr(), base.ldx,
                                 run.ids.data_ptr(), base.n_rows, run.seg,
@@ -153,13 +156,13 @@ def test_build_apply_graph_replay_any_mix():
             ids = rng.integers(-1, base.n_slots, size=base.n_rows).astype(np.int32)
             if rep == 3:
                 ids[:] = 2   # one dense group
-            p = synth.make_random(41, n_rows=256, k=512, slice_d=[512], n_slots=8, ranks=[16] * 8,
-                                  r_max=16, ids=ids)
+            p = synth.make_random(41, n_rows=n_rows, k=512, slice_d=[512], n_slots=8,
+                                  ranks=[16] * 8, r_max=16, ids=ids)
             p.A, p.B, p.alphas, p.x, p.y = base.A, base.B, base.alphas, base.x, base.y
             run.ids.copy_(torch.from_numpy(ids).to(run.device))
             run.y.copy_(torch.from_numpy(base.y.view(np.int16)).to(run.device))
             torch.cuda.synchronize()
-            note(f"graph replay {rep}")
+            note(f"graph replay {rep}, {n_rows} rows")
             graph.replay()
             torch.cuda.synchronize()
             check_against_oracle(p, run.y_host(), what=f"replay {rep}")
