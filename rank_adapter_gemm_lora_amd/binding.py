@@ -66,6 +66,10 @@ def load(path: str | None = None):
         if not os.path.exists(p):
             raise RuntimeError(f"HIP library not built: {p} is missing "
                                "(run `python -m rank_adapter_gemm_lora_amd.build`)")
+        # torch's wheel carries its own HIP runtime: load it first so the
+        # library binds to that one (opened before torch, it binds to the
+        # system runtime, and its allocations then fail)
+        import torch  # noqa: F401
         lib = ctypes.CDLL(p)
         P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
         PP = ctypes.POINTER(ctypes.c_void_p)
