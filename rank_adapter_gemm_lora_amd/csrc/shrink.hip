@@ -220,138 +220,170 @@ static_assert(kNT * 64 == 256, "one reduction entry per thread");
 
 // 64-row tiles (batches above 4096 rows).  Each wavefront owns 16 rows of the
 // tile over the split's whole k-range, so no cross-wavefront reduction is
-// needed.  Blocks of 128 k; per block each thread loads
-//   x: 4 granules of its wavefront's 16 rows in row-run order -- instruction
-//      i covers rows 4 i .. 4 i + 3 with 16 lanes (256 contiguous bytes) per
-//      row, which reads HBM at ~5.3 TB/s on this part where the MFMA operand
-//      order (16 rows x 64 B per instruction) reads at ~4.2;
-//   A: 4 granules of the block's rank rows, shared by the four wavefronts;
-// into a ring of kTallRing register slots three blocks ahead, then stores them
-// into LDS (x: the wavefront's own buffer, A: one of two shared buffers) and
-// reads the MFMA operands back.  Both layouts XOR the unit index with the row,
-// so the operand reads of 16 rows x 4 units hit 64 distinct banks.  The one
-// barrier per block orders LDS only (lds_barrier), so the loads of the next
-// three blocks stay in flight across it.
-constexpr int kTallRing = 4;
+// needed.  Blocks of 128 k go global -> LDS directly (global_load_lds, 16 bytes
+// per lane, no registers) into a ring of kTallSlots slots, kTallSlots - 1
+// blocks ahead of the MFMAs:
+//   x: each wavefront copies its 16 rows, instruction i covering rows
+//      4 i .. 4 i + 3 with 16 lanes (256 contiguous bytes) per row;
+//   A: the workgroup copies the NTV N-tiles' 16 rank rows each.
+// The copy writes LDS lane-linearly, so the XOR swizzle that makes the operand
+// reads (16 rows x 4 units) conflict-free is applied to the source addresses.
+// Every slot is a separate __shared__ object, named directly in each step, so
+// the compiler can tell which copies a read depends on; each wavefront waits
+// for its own copies of the block (an explicit count: the blocks still in
+// flight behind it), then one LDS barrier makes every wavefront's copies
+// visible and frees the slot read one block earlier for the next copy.
+// Units past the split's k-range read a zero granule.  NTV (valid N-tiles of
+// a pass) is a template parameter, so only those A rows are copied.
+constexpr int kTallSlots = 3;
 constexpr int kBlkUnits = 16;   // 8-element k units per block
+
+__device__ const uint4 g_zero_granule = {0u, 0u, 0u, 0u};
+
+// s_waitcnt immediate: vector-memory count <= n and no LDS access outstanding (the
+// reads of a slot are done before a copy may overwrite it); exports not waited on.
+#define LORA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+
+typedef uint4 TallX[4 * 16 * kBlkUnits];     // [wavefront][row][swizzled unit]
+typedef uint4 TallA[kNT * 16 * kBlkUnits];   // [N-tile][rank row][swizzled unit]
+
+template <int NTV>
+__device__ __forceinline__ void tall_pass(const ApplyArgs &a, const int64_t (&xsrc)[4], int s, int r,
+                                          int p0, int cnt, int ks, int t0, int nj, TallX &xs0,
+                                          TallX &xs1, TallX &xs2, TallA &as0, TallA &as1,
+                                          TallA &as2)
+{
+    static_assert(kTallSlots == 3, "the ring below names three slots");
+    constexpr int L = 4 + NTV;                    // copies per wavefront per block
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t g8 = a.k >> 3;
+    const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
+    const int nb = (int)((ge - gb + kBlkUnits - 1) / kBlkUnits);
+    const uint16_t *X = static_cast<const uint16_t *>(a.x);
+    const uint16_t *A = static_cast<const uint16_t *>(a.A);
+    const uint16_t *Z = reinterpret_cast<const uint16_t *>(&g_zero_granule);
+    // A source rows of this thread: rank row jm of N-tile tt (rows past r
+    // repeat row r - 1: their outputs are never stored)
+    const int jm = threadIdx.x >> 4, su = threadIdx.x & 15;
+    int64_t asrc[NTV];
+#pragma unroll
+    for (int tt = 0; tt < NTV; ++tt) {
+        const int t = t0 + tt;
+        const int q = t / nj, jc = t - q * nj;
+        const int j = min(16 * jc + jm, r - 1);
+        asrc[tt] = (((int64_t)s * a.n_slices + q) * a.r_max + j) * a.k;
+    }
+    auto copy = [&](int b, uint4 *xslot, uint4 *aslot) {
+        const int64_t u0 = gb + (int64_t)b * kBlkUnits;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // LDS unit 64 i + lane of this wavefront's rows: row 4 i + g, holds unit m ^ row
+            const int64_t unit = u0 + (m ^ (4 * i + g));
+            const uint16_t *src = unit < ge ? X + xsrc[i] + unit * 8 : Z;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)src,
+                (__attribute__((address_space(3))) void *)(xslot + 16 * kBlkUnits * wave + 64 * i), 16, 0, 0);
+        }
+#pragma unroll
+        for (int tt = 0; tt < NTV; ++tt) {
+            // LDS unit 256 tt + tid: rank row jm, holds unit su ^ jm
+            const int64_t unit = u0 + (su ^ jm);
+            const uint16_t *src = unit < ge ? A + asrc[tt] + unit * 8 : Z;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)src,
+                (__attribute__((address_space(3))) void *)(aslot + 256 * tt + 64 * wave), 16, 0, 0);
+        }
+    };
+    f32x4_t acc[NTV];
+#pragma unroll
+    for (int tt = 0; tt < NTV; ++tt)
+        acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto mma = [&](const uint4 *xslot, const uint4 *aslot) {
+        const uint4 *xw = xslot + 16 * kBlkUnits * wave;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int unit = 4 * st + g;
+            const uint4 xop = xw[m * kBlkUnits + (unit ^ m)];
+#pragma unroll
+            for (int tt = 0; tt < NTV; ++tt) {
+                const uint4 aop = aslot[(16 * tt + m) * kBlkUnits + (unit ^ m)];
+                acc[tt] = mfma_bf16_16x16x32(xop, aop, acc[tt]);
+            }
+        }
+    };
+    // block b sits in slot b % 3; step: wait for its copies, barrier (also frees
+    // the slot of block b - 1), copy block b + 2 into that slot, MFMAs on block b
+    auto step = [&](int b, uint4 *cur_x, uint4 *cur_a, uint4 *nxt_x, uint4 *nxt_a) {
+        LORA_WAIT_VM(L);           // block b + 1 may still be in flight
+        // a bare barrier: a fence here would wait for every copy in flight.
+        // The wait above completed this wavefront's copies of block b; every
+        // wavefront consumed its reads of block b - 1 before arriving.
+        asm volatile("s_barrier" ::: "memory");
+        copy(b + 2, nxt_x, nxt_a);   // (past the last block: zeros, never read)
+        mma(cur_x, cur_a);
+    };
+    copy(0, xs0, as0);
+    copy(1, xs1, as1);
+    const int nt = nb / 3 * 3;      // whole ring turns, then one or two steps
+    for (int b = 0; b < nt; b += 3) {
+        step(b, xs0, as0, xs2, as2);
+        step(b + 1, xs1, as1, xs0, as0);
+        step(b + 2, xs2, as2, xs1, as1);
+    }
+    // blocks nt and nt + 1 are already in slots 0 and 1 (or zeros past the range)
+    if (nb - nt >= 1) {
+        LORA_WAIT_VM(L);
+        asm volatile("s_barrier" ::: "memory");
+        mma(xs0, as0);
+    }
+    if (nb - nt == 2) {
+        LORA_WAIT_VM(0);
+        asm volatile("s_barrier" ::: "memory");
+        mma(xs1, as1);
+    }
+    // accumulator lane (g, m): rows 16 wave + 4 g + i, rank row m of each N-tile
+#pragma unroll
+    for (int tt = 0; tt < NTV; ++tt) {
+        const int t = t0 + tt;
+        const int q = t / nj, jc = t - q * nj;
+        const int j = 16 * jc + m;
+        if (j < r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int u = 16 * wave + 4 * g + i;
+                if (u < cnt)
+                    v_out(a, ks, p0 + u)[q * a.r_max + j] = acc[tt][i];
+            }
+        }
+    }
+    LORA_WAIT_VM(0);   // the copies past the last block
+    __syncthreads();   // the next pass rewrites every slot
+}
 
 __device__ void sgmv_shrink_tile_tall(const ApplyArgs &a, const int32_t *rows, int s, int r,
                                       int p0, int cnt, int ks)
 {
-    __shared__ uint4 ablk[2][kNT * 16 * kBlkUnits];   // [buffer][rank row * 16 + swizzled unit]
-    __shared__ uint4 xblk[4 * 16 * kBlkUnits];        // [wavefront][row][swizzled unit]
+    // the ring: three slots, each its own object
+    __shared__ TallX xs0, xs1, xs2;
+    __shared__ TallA as0, as1, as2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
+    const int g = lane >> 4;
     const int nj = (r + 15) >> 4;
     const int NT = a.n_slices * nj;
-    const int64_t g8 = a.k >> 3;
-    const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
-    const int nb = (int)((ge - gb + kBlkUnits - 1) / kBlkUnits);
-    // the x granules this lane loads: rows 4 i + lane / 16 of the wavefront's
-    // 16, unit lane % 16 of the block
+    // x rows of this lane's copies: rows 4 i + lane / 16 of the wavefront's 16
+    // (rows past the tile repeat its last row: their outputs are never stored)
     int64_t xsrc[4];
-    bool xval[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int u = 16 * wave + 4 * i + g;
-        xval[i] = u < cnt;
-        xsrc[i] = (int64_t)rows[min(u, cnt - 1)] * a.ldx;
-    }
-    uint4 *xw = xblk + 16 * kBlkUnits * wave;
-
+    for (int i = 0; i < 4; ++i)
+        xsrc[i] = (int64_t)rows[min(16 * wave + 4 * i + g, cnt - 1)] * a.ldx;
     for (int t0 = 0; t0 < NT; t0 += kNT) {
-        const int ntv = min(kNT, NT - t0);            // valid N-tiles in this pass
-        // the four A granules this thread stages per block: rank row jm of
-        // N-tiles 0..3, unit au; consecutive threads read consecutive 16 B of
-        // one rank row
-        const int jm = threadIdx.x >> 4, au = threadIdx.x & 15;
-        const int adst = jm * kBlkUnits + (au ^ jm);   // + 256 tt: N-tile tt's rows
-        int64_t asrc[4];
-        bool aval[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int t = t0 + tt;
-            const int q = t / nj, jc = t - q * nj;
-            const int j = 16 * jc + jm;
-            aval[tt] = tt < ntv && j < r;
-            asrc[tt] = aval[tt] ? (((int64_t)s * a.n_slices + q) * a.r_max + j) * a.k : 0;
+        switch (min(kNT, NT - t0)) {   // (uniform)
+        case 1: tall_pass<1>(a, xsrc, s, r, p0, cnt, ks, t0, nj, xs0, xs1, xs2, as0, as1, as2); break;
+        case 2: tall_pass<2>(a, xsrc, s, r, p0, cnt, ks, t0, nj, xs0, xs1, xs2, as0, as1, as2); break;
+        case 3: tall_pass<3>(a, xsrc, s, r, p0, cnt, ks, t0, nj, xs0, xs1, xs2, as0, as1, as2); break;
+        default: tall_pass<4>(a, xsrc, s, r, p0, cnt, ks, t0, nj, xs0, xs1, xs2, as0, as1, as2); break;
         }
-        auto issue = [&](int b, uint4 (&xs)[4], uint4 (&as)[4]) {
-            const int64_t u0 = gb + (int64_t)b * kBlkUnits;
-            const int64_t xunit = u0 + m;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xs[i] = (xval[i] && xunit < ge) ? load16(a.x, xsrc[i] + xunit * 8)
-                                                : make_uint4(0, 0, 0, 0);
-            const int64_t aunit = u0 + au;
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-                as[tt] = (aval[tt] && aunit < ge) ? load16(a.A, asrc[tt] + aunit * 8)
-                                                  : make_uint4(0, 0, 0, 0);
-        };
-        f32x4_t acc[kNT];
-#pragma unroll
-        for (int tt = 0; tt < kNT; ++tt)
-            acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        uint4 xr[kTallRing][4], ar[kTallRing][4];
-        auto step = [&](int b, uint4 (&xs)[4], uint4 (&as)[4], uint4 (&xn)[4], uint4 (&an)[4]) {
-            if (b + kTallRing - 1 < nb)
-                issue(b + kTallRing - 1, xn, an);
-            uint4 *buf = ablk[b & 1];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-                buf[256 * tt + adst] = as[tt];
-            // x row 4 i + g, unit m -> LDS row 4 i + g, unit m ^ (4 i + g)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xw[(4 * i + g) * kBlkUnits + (m ^ (4 * i + g))] = xs[i];
-            // block b of A and x in LDS; the loads issued above stay in flight
-            lds_barrier();
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int unit = 4 * st + g;
-                const uint4 xop = xw[m * kBlkUnits + (unit ^ m)];
-#pragma unroll
-                for (int tt = 0; tt < kNT; ++tt) {
-                    if (tt < ntv) {
-                        const uint4 aop = buf[(16 * tt + m) * kBlkUnits + (unit ^ m)];
-                        acc[tt] = mfma_bf16_16x16x32(xop, aop, acc[tt]);
-                    }
-                }
-            }
-            // the x buffer is rewritten next block: every lane of this
-            // wavefront must have read it first (LDS ops of a wavefront run in
-            // order, and the next writes follow these reads in program order)
-        };
-#pragma unroll
-        for (int b = 0; b < kTallRing - 1; ++b)
-            if (b < nb)
-                issue(b, xr[b], ar[b]);
-        for (int b = 0; b < nb; b += kTallRing) {
-            step(b, xr[0], ar[0], xr[3], ar[3]);
-            if (b + 1 < nb)
-                step(b + 1, xr[1], ar[1], xr[0], ar[0]);
-            if (b + 2 < nb)
-                step(b + 2, xr[2], ar[2], xr[1], ar[1]);
-            if (b + 3 < nb)
-                step(b + 3, xr[3], ar[3], xr[2], ar[2]);
-        }
-        // accumulator lane (g, m): rows 16 wave + 4 g + i, rank row m of each N-tile
-#pragma unroll
-        for (int tt = 0; tt < kNT; ++tt) {
-            const int t = t0 + tt;
-            const int q = t / nj, jc = t - q * nj;
-            const int j = 16 * jc + m;
-            if (tt < ntv && j < r) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int u = 16 * wave + 4 * g + i;
-                    if (u < cnt)
-                        v_out(a, ks, p0 + u)[q * a.r_max + j] = acc[tt][i];
-                }
-            }
-        }
-        __syncthreads();   // the next pass restages every buffer
     }
 }
 
