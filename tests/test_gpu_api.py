@@ -52,6 +52,18 @@ EDGE_CASES = {
                          r_max=128, p_none=0.05),
     "rank128_slices": dict(n_rows=300, k=128, slice_d=[192, 64], n_slots=2, ranks=[128, 72],
                            r_max=128),
+    # long k at a small batch: 16 k-splits (the v partials summed in two batches)
+    "ks16_long_k": dict(n_rows=100, k=8192, slice_d=[512], n_slots=4, ranks=[16, 8, 32, 64],
+                        r_max=64, p_none=0.1),
+    # the most slices a stack takes, ragged and unaligned (slices * r_max = 256)
+    "max_slices": dict(n_rows=300, k=96, slice_d=[64, 8, 16, 128, 64, 24, 8, 200], n_slots=3,
+                       ranks=[32, 7, 1], r_max=32, p_none=0.1),
+    # both sides of the switch to 64-row dense tiles
+    "rows4096": dict(n_rows=4096, k=128, slice_d=[128], n_slots=3, ranks=[16, 16, 8], r_max=16),
+    "rows4097": dict(n_rows=4097, k=128, slice_d=[128], n_slots=3, ranks=[16, 16, 8], r_max=16),
+    # 64-row dense tiles below 4096 rows: a wide output at r_max >= 32
+    "tall_wide_d": dict(n_rows=1100, k=256, slice_d=[8192], n_slots=4, ranks=[32, 16, 8, 32],
+                        r_max=32, p_none=0.05),
 }
 
 
