@@ -220,23 +220,27 @@ static_assert(kNT * 64 == 256, "one reduction entry per thread");
 
 // 64-row tiles (batches above 4096 rows).  Each wavefront owns 16 rows of the
 // tile over the split's whole k-range, so no cross-wavefront reduction is
-// needed.  Blocks of 128 k go global -> LDS directly (global_load_lds, 16 bytes
+// needed.  Blocks of 64 k go global -> LDS directly (global_load_lds, 16 bytes
 // per lane, no registers) into a ring of kTallSlots slots, kTallSlots - 1
 // blocks ahead of the MFMAs:
 //   x: each wavefront copies its 16 rows, instruction i covering rows
-//      4 i .. 4 i + 3 with 16 lanes (256 contiguous bytes) per row;
-//   A: the workgroup copies the NTV N-tiles' 16 rank rows each.
-// The copy writes LDS lane-linearly, so the XOR swizzle that makes the operand
-// reads (16 rows x 4 units) conflict-free is applied to the source addresses.
-// Every slot is a separate __shared__ object, named directly in each step, so
-// the compiler can tell which copies a read depends on; each wavefront waits
-// for its own copies of the block (an explicit count: the blocks still in
-// flight behind it), then one LDS barrier makes every wavefront's copies
-// visible and frees the slot read one block earlier for the next copy.
-// Units past the split's k-range read a zero granule.  NTV (valid N-tiles of
-// a pass) is a template parameter, so only those A rows are copied.
+//      8 i .. 8 i + 7 with 8 lanes (128 contiguous bytes) per row;
+//   A: the workgroup copies the NTV N-tiles' 16 rank rows each, two N-tiles
+//      per instruction.
+// A slot row is 128 bytes (half the banks), so the XOR swizzle that makes the
+// operand reads (16 rows x 16 bytes) conflict-free pairs the row's parity with
+// the unit XORed by row / 2; the copy writes LDS lane-linearly, so the swizzle
+// is applied to the source addresses.  Every slot is a separate __shared__
+// object, named directly in each step, so the compiler can tell which copies a
+// read depends on; each wavefront waits for its own copies of the block (an
+// explicit count: the blocks still in flight behind it), then one LDS barrier
+// makes every wavefront's copies visible and frees the slot read one block
+// earlier for the next copy.  Units past the split's k-range read a zero
+// granule.  NTV (valid N-tiles of a pass) is a template parameter, so only
+// those A rows are copied.  The ring is small enough (48 KB) for three
+// workgroups per CU, so a prefill's tiles are all resident at once.
 constexpr int kTallSlots = 3;
-constexpr int kBlkUnits = 16;   // 8-element k units per block
+constexpr int kBlkUnits = 8;   // 8-element k units per block
 
 __device__ const uint4 g_zero_granule = {0u, 0u, 0u, 0u};
 
@@ -248,13 +252,14 @@ typedef uint4 TallX[4 * 16 * kBlkUnits];     // [wavefront][row][swizzled unit]
 typedef uint4 TallA[kNT * 16 * kBlkUnits];   // [N-tile][rank row][swizzled unit]
 
 template <int NTV>
-__device__ __forceinline__ void tall_pass(const ApplyArgs &a, const int64_t (&xsrc)[4], int s, int r,
+__device__ __forceinline__ void tall_pass(const ApplyArgs &a, const int64_t (&xsrc)[2], int s, int r,
                                           int p0, int cnt, int ks, int t0, int nj, TallX &xs0,
                                           TallX &xs1, TallX &xs2, TallA &as0, TallA &as1,
                                           TallA &as2)
 {
     static_assert(kTallSlots == 3, "the ring below names three slots");
-    constexpr int L = 4 + NTV;                    // copies per wavefront per block
+    constexpr int NA = (NTV + 1) / 2;             // A copies per wavefront per block
+    constexpr int L = 2 + NA;                     // copies per wavefront per block
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t g8 = a.k >> 3;
@@ -263,36 +268,41 @@ __device__ __forceinline__ void tall_pass(const ApplyArgs &a, const int64_t (&xs
     const uint16_t *X = static_cast<const uint16_t *>(a.x);
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     const uint16_t *Z = reinterpret_cast<const uint16_t *>(&g_zero_granule);
-    // A source rows of this thread: rank row jm of N-tile tt (rows past r
-    // repeat row r - 1: their outputs are never stored)
-    const int jm = threadIdx.x >> 4, su = threadIdx.x & 15;
-    int64_t asrc[NTV];
+    // copy lanes: row (lane / 8) of 8, column lane % 8
+    const int cr = lane >> 3, cc = lane & 7;
+    // A source rows of this thread: rank row jm of N-tile 2 p + th (rows past r
+    // repeat row r - 1, N-tiles past NTV read zeros: neither is ever stored)
+    const int th = threadIdx.x >> 7, jm = (threadIdx.x >> 3) & 15;
+    int64_t asrc[NA];
+    bool aval[NA];
 #pragma unroll
-    for (int tt = 0; tt < NTV; ++tt) {
-        const int t = t0 + tt;
+    for (int p = 0; p < NA; ++p) {
+        const int t = t0 + 2 * p + th;
+        aval[p] = 2 * p + th < NTV;
         const int q = t / nj, jc = t - q * nj;
         const int j = min(16 * jc + jm, r - 1);
-        asrc[tt] = (((int64_t)s * a.n_slices + q) * a.r_max + j) * a.k;
+        asrc[p] = aval[p] ? (((int64_t)s * a.n_slices + q) * a.r_max + j) * a.k : 0;
     }
     auto copy = [&](int b, uint4 *xslot, uint4 *aslot) {
         const int64_t u0 = gb + (int64_t)b * kBlkUnits;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // LDS unit 64 i + lane of this wavefront's rows: row 4 i + g, holds unit m ^ row
-            const int64_t unit = u0 + (m ^ (4 * i + g));
+        for (int i = 0; i < 2; ++i) {
+            // LDS unit 64 i + lane of this wavefront's rows: row 8 i + cr, column cc
+            const int row = 8 * i + cr;
+            const int64_t unit = u0 + (cc ^ (row >> 1));
             const uint16_t *src = unit < ge ? X + xsrc[i] + unit * 8 : Z;
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void *)src,
                 (__attribute__((address_space(3))) void *)(xslot + 16 * kBlkUnits * wave + 64 * i), 16, 0, 0);
         }
 #pragma unroll
-        for (int tt = 0; tt < NTV; ++tt) {
-            // LDS unit 256 tt + tid: rank row jm, holds unit su ^ jm
-            const int64_t unit = u0 + (su ^ jm);
-            const uint16_t *src = unit < ge ? A + asrc[tt] + unit * 8 : Z;
+        for (int p = 0; p < NA; ++p) {
+            // LDS unit 256 p + tid: N-tile 2 p + th, rank row jm, column cc
+            const int64_t unit = u0 + (cc ^ (jm >> 1));
+            const uint16_t *src = (aval[p] && unit < ge) ? A + asrc[p] + unit * 8 : Z;
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void *)src,
-                (__attribute__((address_space(3))) void *)(aslot + 256 * tt + 64 * wave), 16, 0, 0);
+                (__attribute__((address_space(3))) void *)(aslot + 256 * p + 64 * wave), 16, 0, 0);
         }
     };
     f32x4_t acc[NTV];
@@ -302,12 +312,13 @@ __device__ __forceinline__ void tall_pass(const ApplyArgs &a, const int64_t (&xs
     auto mma = [&](const uint4 *xslot, const uint4 *aslot) {
         const uint4 *xw = xslot + 16 * kBlkUnits * wave;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < kBlkUnits / 4; ++st) {
             const int unit = 4 * st + g;
-            const uint4 xop = xw[m * kBlkUnits + (unit ^ m)];
+            const int col = unit ^ (m >> 1);
+            const uint4 xop = xw[m * kBlkUnits + col];
 #pragma unroll
             for (int tt = 0; tt < NTV; ++tt) {
-                const uint4 aop = aslot[(16 * tt + m) * kBlkUnits + (unit ^ m)];
+                const uint4 aop = aslot[(16 * tt + m) * kBlkUnits + col];
                 acc[tt] = mfma_bf16_16x16x32(xop, aop, acc[tt]);
             }
         }
@@ -368,15 +379,14 @@ __device__ void sgmv_shrink_tile_tall(const ApplyArgs &a, const int32_t *rows, i
     __shared__ TallX xs0, xs1, xs2;
     __shared__ TallA as0, as1, as2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4;
     const int nj = (r + 15) >> 4;
     const int NT = a.n_slices * nj;
-    // x rows of this lane's copies: rows 4 i + lane / 16 of the wavefront's 16
+    // x rows of this lane's copies: rows 8 i + lane / 8 of the wavefront's 16
     // (rows past the tile repeat its last row: their outputs are never stored)
-    int64_t xsrc[4];
+    int64_t xsrc[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        xsrc[i] = (int64_t)rows[min(16 * wave + 4 * i + g, cnt - 1)] * a.ldx;
+    for (int i = 0; i < 2; ++i)
+        xsrc[i] = (int64_t)rows[min(16 * wave + 8 * i + (lane >> 3), cnt - 1)] * a.ldx;
     for (int t0 = 0; t0 < NT; t0 += kNT) {
         switch (min(kNT, NT - t0)) {   // (uniform)
         case 1: tall_pass<1>(a, xsrc, s, r, p0, cnt, ks, t0, nj, xs0, xs1, xs2, as0, as1, as2); break;
