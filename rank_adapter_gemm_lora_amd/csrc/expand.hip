@@ -60,8 +60,17 @@ __device__ __forceinline__ void split_pair(float v0, float v1, uint32_t &hi, uin
     lo = pack_bf16x2(v0 - bf16_lo(hi), v1 - bf16_hi(hi));
 }
 
-// v of rows [p0, p0 + cnt) for slices [q_lo, q_lo + nq) -> vs[u][qq * r + j],
-// the sum of the KS k-split partials in split order.  Each pass puts 8 loads
+// LDS row pitch (floats) of the staged v: nq slices of rp8 = round_up(r, 8)
+// ranks each, plus 4, so the row pitch is an odd number of 16-byte units and
+// the 16 rows that one operand read spans start in 16 distinct bank groups.
+__device__ __forceinline__ int v_pitch(int nq, int rp8)
+{
+    return nq * rp8 + 4;
+}
+
+// v of rows [p0, p0 + cnt) for slices [q_lo, q_lo + nq) ->
+// vs[u * v_pitch + qq * rp8 + j] (j < r; ranks r .. rp8 are not written), the
+// sum of the KS k-split partials in split order.  Each pass puts 8 loads
 // per thread in flight (8 / KS elements, every split of each; 16 splits go in
 // two batches of 8) before the first add, so a tile's v costs one round trip
 // per pass.  Indexes past the tile are clamped to its last element (read, not
@@ -73,6 +82,7 @@ __device__ __forceinline__ void stage_v_ks(const ApplyArgs &a, int p0, int cnt, 
     constexpr int kL = KS < 8 ? KS : 8;              // splits per batch of loads
     constexpr int kE = 8 / kL;                       // elements per thread per pass
     const int SR = a.n_slices * a.r_max, pitch = nq * r, total = cnt * pitch;
+    const int rp8 = (r + 7) & ~7, P = v_pitch(nq, rp8);
     const int64_t split = a.max_rows * (int64_t)SR;
     const uint32_t m_pitch = div_magic(pitch), m_r = div_magic(r);   // cnt * pitch <= 2^14
     for (int base = 0; base < total; base += kE * (int)blockDim.x) {
@@ -104,8 +114,13 @@ __device__ __forceinline__ void stage_v_ks(const ApplyArgs &a, int p0, int cnt, 
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
             const int idx = base + e * (int)blockDim.x + (int)threadIdx.x;
-            if (idx < total)
-                vs[idx] = sum[e];
+            if (idx < total) {
+                // (the decomposition again: cheaper than holding it across the loads)
+                const int u = div_small(idx, m_pitch);
+                const int rem = idx - u * pitch;
+                const int qq = div_small(rem, m_r);
+                vs[u * P + qq * rp8 + (rem - qq * r)] = sum[e];
+            }
         }
     }
 }
@@ -149,7 +164,9 @@ __device__ __forceinline__ void merge16(const ApplyArgs &a, int64_t yi, bool h0,
 
 // MT: row tiles (16 rows each) of the dense tile height this launch serves (1
 // for batches up to 4096 rows, 4 above), so the y registers match the shape.
-template <int MT>
+// WO: rank windows in the outer loop (B staged once per window, all MT row
+// tiles accumulated at once), for stacks whose B chunk needs several windows.
+template <int MT, bool WO>
 __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
                                  int p0, int cnt, int64_t c0, float *vs, uint16_t *bs)
 {
@@ -203,7 +220,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     stage_b(0);
     const int q_lo = slice_of(a, c0);
     const int nq = slice_of(a, min(c0 + kCols, a.D) - 1) - q_lo + 1;
-    const int pitch = nq * r;
+    const int P = v_pitch(nq, rp);
     stage_v(a, p0, cnt, r, q_lo, nq, vs);
     __syncthreads();   // B (first window) and v staged
     const int qq = slice_of(a, c0 + 64 * wave) - q_lo;
@@ -213,56 +230,130 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     for (int mt = 0; mt < 4; ++mt)
         bcolumn[mt] = 64 * wave + 16 * (m >> 2) + 4 * mt + (m & 3);
 
-#pragma unroll
-    for (int nt = 0; nt < MT; ++nt) {
-        if (nt >= n_nt)
-            continue;   // (uniform) fully unrolled: y0[nt] / y1[nt] stay in registers
-        const int u = 16 * nt + m;
-        f32x4_t acc[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (WO) {
+        // windows outer, N-tiles inner: B is staged once per window, every N-tile's
+        // accumulators stay live across the windows
+        f32x4_t acc[MT][4];
+    #pragma unroll
+        for (int nt = 0; nt < MT; ++nt)
+    #pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int w = 0; w < n_win; ++w) {
             const int w0 = w * a.b_win, wl = min(a.b_win, rp - w0);
-            if (n_win > 1 && (nt > 0 || w > 0)) {   // (uniform) restage this window
-                __syncthreads();                    // every wavefront is done with the last one
+            if (w > 0) {              // (uniform) restage: every wavefront is done with the last window
+                __syncthreads();
                 stage_b(w0);
                 __syncthreads();
             }
             if (!in_d)
-                continue;
-            for (int jc = w0 >> 4; jc < min(nj, (w0 + wl + 15) >> 4); ++jc) {
-                const int jo = jc * 16 + 8 * (g & 1);
-                float f[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int j = jo + i;
-                    const float v = (u < cnt && j < r) ? vs[u * pitch + qq * r + j] : 0.f;
-                    f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
-                }
-                uint4 vop;
-                vop.x = pack_bf16x2(f[0], f[1]);
-                vop.y = pack_bf16x2(f[2], f[3]);
-                vop.z = pack_bf16x2(f[4], f[5]);
-                vop.w = pack_bf16x2(f[6], f[7]);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const uint4 bop = jo < w0 + wl
-                                          ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + (jo - w0))
-                                          : make_uint4(0, 0, 0, 0);
-                    acc[mt] = mfma_bf16_16x16x32(bop, vop, acc[mt]);
+                continue;             // (uniform per wavefront: D is whole 64-column blocks)
+    #pragma unroll
+            for (int nt = 0; nt < MT; ++nt) {
+                if (nt >= n_nt)
+                    continue;         // (uniform) fully unrolled: the accumulators stay in registers
+                const int u = 16 * nt + m;
+                for (int jc = w0 >> 4; jc < min(nj, (w0 + wl + 15) >> 4); ++jc) {
+                    const int jo = jc * 16 + 8 * (g & 1);
+                    // 8 ranks of row u: two 16-byte reads (ranks past r masked)
+                    const float4 *vr = reinterpret_cast<const float4 *>(vs + u * P + qq * rp + jo);
+                    const float4 va = vr[0], vb = vr[1];
+                    const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+                    float f[8];
+    #pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float v = (u < cnt && jo + i < r) ? vv[i] : 0.f;
+                        f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
+                    }
+                    uint4 vop;
+                    vop.x = pack_bf16x2(f[0], f[1]);
+                    vop.y = pack_bf16x2(f[2], f[3]);
+                    vop.z = pack_bf16x2(f[4], f[5]);
+                    vop.w = pack_bf16x2(f[6], f[7]);
+    #pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        const uint4 bop = jo < w0 + wl
+                                              ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + (jo - w0))
+                                              : make_uint4(0, 0, 0, 0);
+                        acc[nt][mt] = mfma_bf16_16x16x32(bop, vop, acc[nt][mt]);
+                    }
                 }
             }
         }
-        if (in_d && u < cnt) {
-            float f[16];
-#pragma unroll
+        if (in_d) {
+    #pragma unroll
+            for (int nt = 0; nt < MT; ++nt) {
+                const int u = 16 * nt + m;
+                if (nt < n_nt && u < cnt) {
+                    float f[16];
+    #pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            f[4 * mt + i] = acc[nt][mt][i];
+                    merge16<DT_BF16>(a, (int64_t)rows[u] * a.ldy + cb, true, true, y0[nt], y1[nt], scale,
+                                     f);
+                }
+            }
+        }
+    } else {
+        // N-tiles outer: one set of accumulators (fewer registers); B is
+        // restaged per window and N-tile, so this order serves stacks whose
+        // B chunk fits one window
+    #pragma unroll
+        for (int nt = 0; nt < MT; ++nt) {
+            if (nt >= n_nt)
+                continue;   // (uniform) fully unrolled: y0[nt] / y1[nt] stay in registers
+            const int u = 16 * nt + m;
+            f32x4_t acc[4];
+    #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    f[4 * mt + i] = acc[mt][i];
-            merge16<DT_BF16>(a, (int64_t)rows[u] * a.ldy + cb, true, true, y0[nt], y1[nt], scale,
-                             f);
+                acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < n_win; ++w) {
+                const int w0 = w * a.b_win, wl = min(a.b_win, rp - w0);
+                if (n_win > 1 && (nt > 0 || w > 0)) {   // (uniform) restage this window
+                    __syncthreads();                    // every wavefront is done with the last one
+                    stage_b(w0);
+                    __syncthreads();
+                }
+                if (!in_d)
+                    continue;
+                for (int jc = w0 >> 4; jc < min(nj, (w0 + wl + 15) >> 4); ++jc) {
+                    const int jo = jc * 16 + 8 * (g & 1);
+                    // 8 ranks of row u: two 16-byte reads (ranks past r masked)
+                    const float4 *vr = reinterpret_cast<const float4 *>(vs + u * P + qq * rp + jo);
+                    const float4 va = vr[0], vb = vr[1];
+                    const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+                    float f[8];
+    #pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float v = (u < cnt && jo + i < r) ? vv[i] : 0.f;
+                        f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
+                    }
+                    uint4 vop;
+                    vop.x = pack_bf16x2(f[0], f[1]);
+                    vop.y = pack_bf16x2(f[2], f[3]);
+                    vop.z = pack_bf16x2(f[4], f[5]);
+                    vop.w = pack_bf16x2(f[6], f[7]);
+    #pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        const uint4 bop = jo < w0 + wl
+                                              ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + (jo - w0))
+                                              : make_uint4(0, 0, 0, 0);
+                        acc[mt] = mfma_bf16_16x16x32(bop, vop, acc[mt]);
+                    }
+                }
+            }
+            if (in_d && u < cnt) {
+                float f[16];
+    #pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        f[4 * mt + i] = acc[mt][i];
+                merge16<DT_BF16>(a, (int64_t)rows[u] * a.ldy + cb, true, true, y0[nt], y1[nt], scale,
+                                 f);
+            }
         }
     }
 }
@@ -317,7 +408,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     const int q_lo = slice_of(a, c0);
     const int nq = slice_of(a, min(c0 + kCols, a.D) - 1) - q_lo + 1;
     stage_v(a, p0, cnt, r, q_lo, nq, vs);
-    const int pitch = nq * r;
+    const int P = v_pitch(nq, rp);
     const int cl = 64 * wave + 16 * g;               // lane's first column in the chunk
     int qh[2];
 #pragma unroll
@@ -352,7 +443,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                 const int j = j0 + 2 * pp;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const float *vr = vs + m * pitch + qh[hh] * r;
+                    const float *vr = vs + m * P + qh[hh] * rp;
                     const float v0 = (row_ok && j < r) ? vr[j] : 0.f;
                     const float v1 = (row_ok && j + 1 < r) ? vr[j + 1] : 0.f;
                     uint32_t hi, lo;
@@ -372,7 +463,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
             for (int jj = 0; jj < kPassElems && j0 + jj < r; ++jj) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const float vj = row_ok ? vs[m * pitch + qh[hh] * r + j0 + jj] : 0.f;
+                    const float vj = row_ok ? vs[m * P + qh[hh] * rp + j0 + jj] : 0.f;
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
                         acc[8 * hh + c] = fmaf(bf[jj * kCols + cl + 8 * hh + c], vj,
@@ -387,7 +478,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
 
 // Dynamic LDS: [rows: 64 int][slot table: rank, scale (when n_slots <= 256)]
 // [v staging at lds_v_off][B staging at lds_b_off]; the host sizes it.
-template <int DT, int MT>
+template <int DT, int MT, bool WO>
 __device__ __forceinline__ void expand_body(const ApplyArgs &a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -424,7 +515,7 @@ __device__ __forceinline__ void expand_body(const ApplyArgs &a)
         return;   // slot emptied since the grouping was built: rows stay untouched
     if constexpr (DT == DT_BF16) {
         if (h.w == kTileSgmv && a.mfma_ok) {
-            sgmv_expand_tile<MT>(a, rows, s, r, scale, p0, cnt, c0, vs,
+            sgmv_expand_tile<MT, WO>(a, rows, s, r, scale, p0, cnt, c0, vs,
                                  reinterpret_cast<uint16_t *>(bst));
             return;
         }
@@ -437,10 +528,10 @@ __device__ __forceinline__ void expand_body(const ApplyArgs &a)
     }
 }
 
-template <int DT, int MT>
+template <int DT, int MT, bool WO>
 __global__ __launch_bounds__(256) void expand_kernel(ApplyArgs a)
 {
-    expand_body<DT, MT>(a);
+    expand_body<DT, MT, WO>(a);
 }
 
 // bf16 with 16-row dense tiles (every batch up to 4096 rows) fits 80 registers
@@ -449,7 +540,7 @@ __global__ __launch_bounds__(256) void expand_kernel(ApplyArgs a)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6, 8)))
 void expand_kernel_bf16_short(ApplyArgs a)
 {
-    expand_body<DT_BF16, 1>(a);
+    expand_body<DT_BF16, 1, false>(a);
 }
 
 }  // namespace
@@ -460,13 +551,18 @@ hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream
         return hipSuccess;
     const dim3 grid((unsigned)((a.D + kCols - 1) / kCols), max_tiles);
     const bool tall = a.sgmv_rows > kBgmvTileRows;   // 64-row dense tiles
+    // B chunks in rank windows: windows outer (more registers, but such a
+    // launch is held to two workgroups per CU by its LDS anyway)
+    const bool windows = a.b_win < ((a.r_max + 7) & ~7);
     if (dtype == DT_BF16) {
-        if (tall)
-            hipLaunchKernelGGL((expand_kernel<DT_BF16, 4>), grid, dim3(256), a.lds_bytes, stream, a);
+        if (tall && windows)
+            hipLaunchKernelGGL((expand_kernel<DT_BF16, 4, true>), grid, dim3(256), a.lds_bytes, stream, a);
+        else if (tall)
+            hipLaunchKernelGGL((expand_kernel<DT_BF16, 4, false>), grid, dim3(256), a.lds_bytes, stream, a);
         else
             hipLaunchKernelGGL(expand_kernel_bf16_short, grid, dim3(256), a.lds_bytes, stream, a);
     } else {
-        hipLaunchKernelGGL((expand_kernel<DT_F32, 1>), grid, dim3(256), a.lds_bytes, stream, a);
+        hipLaunchKernelGGL((expand_kernel<DT_F32, 1, false>), grid, dim3(256), a.lds_bytes, stream, a);
     }
     return hipGetLastError();
 }

@@ -138,7 +138,8 @@ ExpandLds expand_lds(const lora_stack *st, bool mfma, int tile_rows)
 {
     const int64_t table = st->n_slots <= kExpandTableSlots ? 8 * kExpandTableSlots : 0;
     const int64_t rows = mfma ? tile_rows : kBgmvTileRows;
-    const int64_t v_bytes = round_up(rows * expand_nq_max(st) * st->r_max * 4, 16);
+    // v rows of nq slices x rp ranks plus 4 floats (the kernel's padded pitch)
+    const int64_t v_bytes = round_up(rows * (expand_nq_max(st) * st->rp_max + 4) * 4, 16);
     ExpandLds l;
     l.v_off = (int)(kExpandLdsTable + table);
     l.b_off = (int)(l.v_off + v_bytes);
