@@ -11,9 +11,9 @@
 //
 // The pass reads and writes W once and the product has only r terms per
 // element, so it is bound by HBM.  W is cut into 64 x 128 tiles that each lie
-// inside one slice.  Loads are issued adapter first, W last: a load counter
-// wait for the adapter data then does not also wait for W, whose loads stay in
-// flight while the product is formed.
+// inside one slice.  Every load of a tile (the adapter's rows and columns and
+// the W tile) is issued before the first use of any of them, so a tile costs
+// one round trip before its arithmetic.
 //   bf16: the 64 x 128 x r product of a tile runs on the matrix cores, and the
 //   fp32 result goes through LDS once more so that W is read and written in
 //   16-byte units along its rows.  Weights of fewer than kMergeStreamTiles
@@ -57,11 +57,17 @@ __device__ __forceinline__ int a_unit(int j, int u) { return j * 16 + (u ^ (2 * 
 // The four row groups one accumulator store covers land on distinct banks.
 __device__ __forceinline__ int c_unit(int m, int u) { return m * 32 + (u ^ (4 * ((m >> 2) & 3))); }
 
+// A 16-byte unit of zeros: the source of A copies past the rank or past k.
+__device__ const uint4 g_merge_zero = {0u, 0u, 0u, 0u};
+
 // bf16, one tile per workgroup (weights of fewer than kMergeStreamTiles tiles):
 // NKC chunks of 32 rank values (rank <= 32 * NKC).  The slot's A rows for the
-// tile's 128 columns are staged row-major in LDS (XOR-swizzled 16-byte units)
-// and each lane gathers its 8 rank values of one column with 2-byte reads;
-// wavefront w owns columns 32 w .. + 31 and all 64 rows.
+// tile's 128 columns are copied global -> LDS directly (global_load_lds, no
+// registers held: they go to the B and W loads instead), row-major with
+// XOR-swizzled 16-byte units -- the copy writes LDS lane-linearly, so the
+// swizzle is applied to the source units -- and each lane gathers its 8 rank
+// values of one column with 2-byte reads; wavefront w owns columns
+// 32 w .. + 31 and all 64 rows.
 template <int NKC>
 __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(MergeArgs a)
 {
@@ -82,16 +88,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(MergeArgs a)
     // selected afterwards: no branches around loads, so they all stay in flight.
     const int64_t ccol = col_ok ? scol : a.k - 8;
 
-    // A rows 0 .. 32 NKC - 1 of this column range (rows >= rank read as zero)
-    uint4 ast[2 * NKC];
+    // A rows 0 .. 32 NKC - 1 of this column range (rows >= rank read as zero):
+    // copy p of wavefront w fills LDS units 64 (4 p + w) .. + 63, i.e. rows
+    // 4 (4 p + w) + lane / 16, position lane % 16, which holds unit
+    // (lane % 16) ^ swizzle(row) of that row
+    {
+        const uint16_t *Z = reinterpret_cast<const uint16_t *>(&g_merge_zero);
+        const int pu = lane & 15;
 #pragma unroll
-    for (int p = 0; p < 2 * NKC; ++p) {
-        const int j = (tid >> 4) + 16 * p;
-        const uint4 v = load16(A, (int64_t)min(j, a.rank - 1) * a.k + ccol);
-        ast[p] = keep_if(j < a.rank && col_ok, v);
+        for (int p = 0; p < 2 * NKC; ++p) {
+            const int j = 4 * (4 * p + wave) + (lane >> 4);
+            const int u = pu ^ (2 * ((j >> 3) & 3));
+            const int64_t col = c0 + 8 * u;
+            const uint16_t *src = (j < a.rank && col < a.k) ? A + (int64_t)j * a.k + col : Z;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)src,
+                (__attribute__((address_space(3))) void *)(lds + 64 * (4 * p + wave)), 16, 0, 0);
+        }
     }
     // matrix-core row operand: B rows o0 + 16 mb + lane % 16, rank values
     // 32 c + 8 (lane / 16) .. + 7 (the pool pads each row to rp with zeros)
+    // (raw values: masked where the matrix cores take them, so no select waits
+    // on these loads before the rest are issued)
     uint4 bop[NKC][4];
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
@@ -99,8 +117,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(MergeArgs a)
         for (int mb = 0; mb < 4; ++mb) {
             const int64_t o = o0 + 16 * mb + (lane & 15);
             const int g = 4 * c + (lane >> 4);
-            const uint4 v = load16(B, min(o, o_end - 1) * a.rp + 8 * min(g, a.rp / 8 - 1));
-            bop[c][mb] = keep_if(o < o_end && 8 * g < a.rp, v);
+            bop[c][mb] = load16(B, min(o, o_end - 1) * a.rp + 8 * min(g, a.rp / 8 - 1));
         }
     }
     // this thread's four W units: rows o0 + tid / 16 + 16 p
@@ -110,11 +127,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(MergeArgs a)
         const int64_t o = o0 + (tid >> 4) + 16 * p;
         w[p] = load16(W, min(o, o_end - 1) * a.ldw + ccol);   // unused when out of the tile
     }
+    // every load above is issued before anything that uses one (the scheduler
+    // would otherwise pull a B mask up and wait for all loads before W's)
+    __builtin_amdgcn_sched_barrier(0);
 
-#pragma unroll
-    for (int p = 0; p < 2 * NKC; ++p)
-        lds[a_unit((tid >> 4) + 16 * p, su)] = ast[p];
-    lds_barrier();
+    lds_barrier();   // (waits for the A copies)
 
     // the tile of B A: wave owns columns 32 wave .. + 31, all 64 rows
     f32x4_t acc[4][2];
@@ -134,9 +151,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_bf16_kernel(MergeArgs a)
                 h[e] = as[a_unit(jb + e, n >> 3) * 8 + (n & 7)];
             const uint4 col = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                                          h[6] | (h[7] << 16));
+            const bool g_ok = 8 * (4 * c + (lane >> 4)) < a.rp;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                acc[mb][nb] = mfma_bf16_16x16x32(bop[c][mb], col, acc[mb][nb]);
+            for (int mb = 0; mb < 4; ++mb) {
+                const bool ok = g_ok && o0 + 16 * mb + (lane & 15) < o_end;
+                acc[mb][nb] = mfma_bf16_16x16x32(keep_if(ok, bop[c][mb]), col, acc[mb][nb]);
+            }
         }
     }
     lds_barrier();   // every wave is done with the A rows
