@@ -236,7 +236,7 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
         per[name] = e0.elapsed_time(e1) * 1e3 / steps
     # the same step replayed from HIP graphs (one captured per buffer set): the
     # launch shapes depend only on the batch shape, so a graph serves any mix
-    graph_ms = None
+    graph_ms = graph_chain_ms = None
     if graph:
         graphs = []
         for bs in sets:
@@ -258,12 +258,34 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
         torch.cuda.synchronize()
         graph_ms = e0.elapsed_time(e1) / steps
         del graphs
+        # one graph holding a pass over every buffer set (one step each), as a
+        # serving loop captures many layers per graph: the graph launch cost is
+        # shared by the steps it holds
+        chain = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(chain, stream=stream):
+            for bs in sets:
+                step(bs)
+        torch.cuda.synchronize()
+        reps = max(2, steps // n_sets)
+        with torch.cuda.stream(stream):
+            chain.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                chain.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        graph_chain_ms = e0.elapsed_time(e1) / (reps * n_sets)
+        del chain
     n_bgmv, n_sgmv = lb.lora_segments_tile_counts(sets[0].seg, sh)
     for bs in sets:
         bs.close(lb)
     torch.cuda.synchronize()
     return dict(wall_s=wall, gpu_ms=gpu_ms, n_sets=n_sets, set_bytes=set_bytes(p),
-                kernel_us=per, tiles=dict(bgmv=n_bgmv, sgmv=n_sgmv), graph_ms=graph_ms)
+                kernel_us=per, tiles=dict(bgmv=n_bgmv, sgmv=n_sgmv), graph_ms=graph_ms,
+                graph_chain_ms=graph_chain_ms)
 
 
 # ----------------------------------------------------------------- CPU oracle
@@ -346,6 +368,9 @@ def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -
         "graph_ms_per_step": (round(g["graph_ms"], 5) if g["graph_ms"] is not None else None),
         "graph_tokens_per_s": (round(acct["n_valid"] / (g["graph_ms"] * 1e-3), 1)
                                if g["graph_ms"] is not None else None),
+        "graph_chain_ms_per_step": (round(g["graph_chain_ms"], 5)
+                                    if g["graph_chain_ms"] is not None else None),
+        "graph_chain_steps": g["n_sets"] if g["graph_chain_ms"] is not None else None,
     }
     if cpu:
         line["cpu_baseline"] = run_cpu_baseline(p, acct)
