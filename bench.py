@@ -51,7 +51,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATE_BYTES = 512 << 20       # 2x the 256 MB MALL
 DEFAULT_WORKLOAD = "decode_bgmv"
 FUSED_MAX_ROWS = 1024           # lora_build_shrink groups inside the shrink up to this many
-FUSED_MAX_BLOCKS = 256          # rows and shrink workgroups (the library's own rule)
+FUSED_MAX_BLOCKS = 512          # rows and shrink workgroups (the library's own rule)
 KERNEL_SOURCES = ("seg_build.hip", "shrink.hip", "expand.hip", "group.h", "mfma.h",
                   "device_common.h", "internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_bgmv.json")

@@ -196,6 +196,21 @@ lora_status lora_segments_destroy(lora_segments *seg);
 lora_status lora_segments_set_dense_min(lora_segments *seg, int m_min);
 
 /*
+ * Launch shape of the expand of later lora_add_expand / lora_apply /
+ * lora_build_apply calls on this segments object: 256-column chunks of one
+ * row tile per workgroup.  0 (the default) chooses from the shapes alone: 2
+ * for stacks of rank <= 16 with 16-row dense tiles and at least 8192 (tile,
+ * chunk) pairs in the launch bound (many small groups over a wide output:
+ * each workgroup then keeps the next chunk's y and B in flight while it
+ * computes the current one), else 1.  1..16 forces that many where the
+ * several-chunk expand applies (bf16 stacks with dense tiles, 16-row tiles,
+ * r_max <= 64, v of every slice and one B block within the LDS budget) and is
+ * ignored elsewhere.  A tuning knob: results are bit-identical for every
+ * value.  Errors: LORA_E_ARG (chunks < 0 or > 16).
+ */
+lora_status lora_segments_set_expand_chunks(lora_segments *seg, int chunks);
+
+/*
  * Group the rows of one batch by adapter slot, on the device (page "LoRA
  * hot-loading and adapter routing", batched multi-adapter execution section:
  * one group of row indices per adapter id; page "Multi-LoRA Serving",
@@ -258,7 +273,7 @@ lora_status lora_apply(const lora_stack *st, void *y, int64_t ldy, const void *x
  * routing", batched multi-adapter execution) and the shrink itself.  The
  * segments left in seg and the v left in the stack's scratch are the same as
  * those of the two calls.  For small batches (n_rows <= 1024 and a shrink
- * grid of at most 256 workgroups, one per compute unit) the grouping runs
+ * grid of at most 512 workgroups, two per compute unit) the grouping runs
  * inside the shrink kernel (each of its workgroups groups the ids in LDS): one
  * launch instead of two on the decode critical path.  Other batches take the
  * two launches.  ids is read at the call's stream position.  All argument checks

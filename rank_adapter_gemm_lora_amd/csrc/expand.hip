@@ -534,6 +534,189 @@ __global__ __launch_bounds__(256) void expand_kernel(ApplyArgs a)
     expand_body<DT, MT, WO>(a);
 }
 
+// ------------------------------------------- SGMV, several chunks per tile
+
+// Chunks [ch0, ch0 + n_ch) of one 16-row dense tile (bf16, the slot's whole
+// rank in one B block).  v of every slice is staged once.  While chunk c is on
+// the matrix cores, chunk c + 1's y (registers) and B block (registers,
+// written to LDS once every wavefront is done with chunk c's) are in flight;
+// the barriers in the loop order LDS only, so those loads cross them.  NG:
+// 16-byte B granules per thread and chunk at the stack's widest rank
+// (rp_max / 8 rounded up to 2, 4 or 8); a slot of lower rank loads rp / 8.
+template <int NG>
+__device__ void sgmv_expand_stream(const ApplyArgs &a, const int32_t *rows, int s, int r,
+                                   float scale, int p0, int cnt, int ch0, int n_ch, float *vs,
+                                   uint16_t *bs)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, m = lane & 15;
+    const int rp = (r + 7) & ~7, nj = (r + 15) >> 4, ng = rp >> 3;
+    const bool row_ok = m < cnt;
+    const int64_t yrow = (int64_t)rows[min(m, cnt - 1)] * a.ldy;
+    const int64_t bslot = (int64_t)s * a.b_slot_stride;
+    const int P = v_pitch(a.n_slices, rp);
+    int bcolumn[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+        bcolumn[mt] = 64 * wave + 16 * (m >> 2) + 4 * mt + (m & 3);
+
+    // granules of chunk c's contiguous [ncol][rp] B block
+    auto n_gran = [&](int c) {
+        return (int)min((int64_t)kCols, a.D - (int64_t)(ch0 + c) * kCols) * ng;
+    };
+    auto load_chunk = [&](int c, Vec8<DT_BF16> &ya, Vec8<DT_BF16> &yb, uint4 (&bg)[NG]) {
+        const int64_t c0 = (int64_t)(ch0 + c) * kCols;
+        const int64_t cb = c0 + 64 * wave + 16 * g;
+        if (row_ok && cb < a.D) {
+            ya.load(a.y, yrow + cb);
+            yb.load(a.y, yrow + cb + 8);
+        }
+        const int ngr = n_gran(c);
+        const int64_t b0 = bslot + c0 * rp;
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int e = i * kCols + (int)threadIdx.x;
+            if (i < ng && e < ngr)
+                bg[i] = load16(a.B, b0 + 8 * (int64_t)e);
+        }
+    };
+    auto put_b = [&](int c, const uint4 (&bg)[NG]) {
+        const int ngr = n_gran(c);
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int e = i * kCols + (int)threadIdx.x;
+            if (i < ng && e < ngr)
+                *reinterpret_cast<uint4 *>(bs + 8 * e) = bg[i];
+        }
+    };
+    auto compute = [&](int c, const Vec8<DT_BF16> &ya, const Vec8<DT_BF16> &yb) {
+        const int64_t c0 = (int64_t)(ch0 + c) * kCols;
+        const int64_t cb = c0 + 64 * wave + 16 * g;
+        if (c0 + 64 * wave >= a.D)
+            return;   // (uniform per wavefront: D is whole 64-column blocks)
+        const int qq = slice_of(a, c0 + 64 * wave);
+        f32x4_t acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int jc = 0; jc < nj; ++jc) {
+            const int jo = jc * 16 + 8 * (g & 1);
+            // 8 ranks of row m: two 16-byte reads (ranks past r masked)
+            const float4 *vr = reinterpret_cast<const float4 *>(vs + m * P + qq * rp + jo);
+            const float4 va = vr[0], vb = vr[1];
+            const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+            float f[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = (row_ok && jo + i < r) ? vv[i] : 0.f;
+                f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
+            }
+            uint4 vop;
+            vop.x = pack_bf16x2(f[0], f[1]);
+            vop.y = pack_bf16x2(f[2], f[3]);
+            vop.z = pack_bf16x2(f[4], f[5]);
+            vop.w = pack_bf16x2(f[6], f[7]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const uint4 bop = jo < rp ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * rp + jo)
+                                          : make_uint4(0, 0, 0, 0);
+                acc[mt] = mfma_bf16_16x16x32(bop, vop, acc[mt]);
+            }
+        }
+        if (row_ok) {
+            float f[16];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    f[4 * mt + i] = acc[mt][i];
+            merge16<DT_BF16>(a, yrow + cb, true, true, ya, yb, scale, f);
+        }
+    };
+    // chunk c from (cy, cz) while chunk c + 1 loads into (ny, nz)
+    uint4 bg[NG];
+    auto step = [&](int c, const Vec8<DT_BF16> &cy, const Vec8<DT_BF16> &cz, Vec8<DT_BF16> &ny,
+                    Vec8<DT_BF16> &nz) {
+        const bool more = c + 1 < n_ch;
+        if (more)
+            load_chunk(c + 1, ny, nz, bg);
+        compute(c, cy, cz);
+        if (more) {
+            lds_barrier();   // every wavefront is done with chunk c's B
+            put_b(c + 1, bg);
+            lds_barrier();
+        }
+    };
+
+    Vec8<DT_BF16> ya0, yb0, ya1, yb1;
+    load_chunk(0, ya0, yb0, bg);
+    stage_v(a, p0, cnt, r, 0, a.n_slices, vs);   // one round trip with chunk 0's loads
+    put_b(0, bg);
+    __syncthreads();
+    for (int c = 0; c < n_ch; c += 2) {
+        step(c, ya0, yb0, ya1, yb1);
+        if (c + 1 < n_ch)
+            step(c + 1, ya1, yb1, ya0, yb0);
+    }
+}
+
+// Several consecutive 256-column chunks of one tile per workgroup (a.cpw of
+// them): bf16 batches of 16-row dense tiles whose widest rank fits one B
+// block beside v of every slice.  Dynamic LDS as expand_body, with v sized
+// for all slices.
+template <int NG>
+__global__ __launch_bounds__(256) void expand_stream_kernel(ApplyArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    int32_t *rows = reinterpret_cast<int32_t *>(lds);
+    int32_t *srank = reinterpret_cast<int32_t *>(lds + kExpandLdsTable);
+    float *sscale = reinterpret_cast<float *>(lds + kExpandLdsTable + 4 * kExpandTableSlots);
+    float *vs = reinterpret_cast<float *>(lds + a.lds_v_off);
+    unsigned char *bst = lds + a.lds_b_off;
+    const int n_chunks = (int)((a.D + kCols - 1) / kCols);
+    const int ch0 = (int)blockIdx.x * a.cpw;
+    if (ch0 >= n_chunks)
+        return;   // (the grid's x extent is padded to a multiple of 8)
+    const int n_ch = min(a.cpw, n_chunks - ch0);
+    const int t = blockIdx.y;
+    const ShrinkTile *T = a.tiles + t;
+    const int4 h = *reinterpret_cast<const int4 *>(T);
+    const int32_t my_row = threadIdx.x < kSgmvTileRows ? T->rows[threadIdx.x] : 0;
+    const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
+    const bool table = a.n_slots <= kExpandTableSlots;
+    if (table) {
+        for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x) {
+            srank[e] = a.rank[e];
+            sscale[e] = a.scale[e];
+        }
+    }
+    if (t >= n_tiles)
+        return;
+    const int s = h.x, p0 = h.y, cnt = h.z;
+    if (threadIdx.x < kSgmvTileRows)
+        rows[threadIdx.x] = my_row;
+    __syncthreads();
+    const int r = table ? srank[s] : a.rank[s];
+    const float scale = table ? sscale[s] : a.scale[s];
+    if (r == 0)
+        return;   // slot emptied since the grouping was built: rows stay untouched
+    if (h.w == kTileSgmv && a.mfma_ok) {
+        sgmv_expand_stream<NG>(a, rows, s, r, scale, p0, cnt, ch0, n_ch, vs,
+                               reinterpret_cast<uint16_t *>(bst));
+        return;
+    }
+    // BGMV tile: chunk by chunk
+    for (int c = 0; c < n_ch; ++c) {
+        const int64_t c0 = (int64_t)(ch0 + c) * kCols;
+        for (int sub = 0; sub < cnt; sub += kBgmvTileRows) {
+            bgmv_expand_tile<DT_BF16>(a, rows + sub, s, r, scale, p0 + sub,
+                                      min(kBgmvTileRows, cnt - sub), c0, vs,
+                                      reinterpret_cast<uint32_t *>(bst));
+            __syncthreads();   // LDS is restaged by the next sub-tile
+        }
+    }
+}
+
 // bf16 with 16-row dense tiles (every batch up to 4096 rows) fits 80 registers
 // without spilling, so it is built for 6 wavefronts per SIMD: more of these
 // latency-bound workgroups per CU keep more loads in flight.
@@ -554,6 +737,24 @@ hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream
     // B chunks in rank windows: windows outer (more registers, but such a
     // launch is held to two workgroups per CU by its LDS anyway)
     const bool windows = a.b_win < ((a.r_max + 7) & ~7);
+    if (dtype == DT_BF16 && a.cpw > 1) {
+        // several chunks per workgroup; the x extent is padded to a multiple of
+        // 8 so that every tile's workgroup for a given chunk group sits on the
+        // same XCD (consecutive block indices go to consecutive XCDs)
+        const int n_chunks = (int)((a.D + kCols - 1) / kCols);
+        int gx = (n_chunks + a.cpw - 1) / a.cpw;
+        if (gx >= 8)
+            gx = (gx + 7) & ~7;
+        const dim3 sgrid((unsigned)gx, max_tiles);
+        const int rp_max = (a.r_max + 7) & ~7;
+        if (rp_max <= 16)
+            hipLaunchKernelGGL(expand_stream_kernel<2>, sgrid, dim3(256), a.lds_bytes, stream, a);
+        else if (rp_max <= 32)
+            hipLaunchKernelGGL(expand_stream_kernel<4>, sgrid, dim3(256), a.lds_bytes, stream, a);
+        else
+            hipLaunchKernelGGL(expand_stream_kernel<8>, sgrid, dim3(256), a.lds_bytes, stream, a);
+        return hipGetLastError();
+    }
     if (dtype == DT_BF16) {
         if (tall && windows)
             hipLaunchKernelGGL((expand_kernel<DT_BF16, 4, true>), grid, dim3(256), a.lds_bytes, stream, a);

@@ -22,6 +22,7 @@ constexpr int kExpandLdsMax = 65536;   // dynamic LDS of one expand workgroup, a
 constexpr int kTileBgmv = 0;
 constexpr int kTileSgmv = 1;
 constexpr int kMaxKSplit = 16;      // most k-splits of one shrink
+constexpr int kMaxExpandChunks = 16; // most 256-column chunks per expand workgroup
 constexpr int kMaxSliceRank = 256;  // n_slices * r_max bound (LDS staging of v)
 constexpr int kChunkRows = 256;     // rows per chunk of the large-batch grouping
 
@@ -86,6 +87,7 @@ struct ApplyArgs {
     int lds_v_off;             // expand: dynamic LDS byte offsets of v and B staging
     int lds_b_off;
     int lds_bytes;             // expand: dynamic LDS bytes
+    int cpw;                   // expand: 256-column chunks per workgroup (1: one chunk)
     // batch
     const int32_t *counts;
     const ShrinkTile *tiles;
@@ -184,6 +186,7 @@ struct lora_segments {
     int n_slots_cap;
     int max_tiles;
     int dense_min;
+    int expand_chunks;   // 0: chosen from the shapes
     int32_t *perm;
     int32_t *seg_off;
     int32_t *active;

@@ -163,6 +163,35 @@ ExpandLds expand_lds(const lora_stack *st, bool mfma, int tile_rows)
 // MFMA tiles need bf16, slices made of whole 64-column blocks, and the v of a
 // 64-row tile plus at least a 16-rank window of B within the expand's LDS
 // budget; otherwise the dense tiles of a batch are served by the vector code.
+// The several-chunk expand's LDS: as expand_lds, with v of a 16-row tile for
+// every slice and one B block of the widest rank.
+ExpandLds expand_stream_lds(const lora_stack *st)
+{
+    const int64_t table = st->n_slots <= kExpandTableSlots ? 8 * kExpandTableSlots : 0;
+    const int64_t v_bytes =
+        round_up((int64_t)kBgmvTileRows * (st->n_slices * st->rp_max + 4) * 4, 16);
+    ExpandLds l;
+    l.v_off = (int)(kExpandLdsTable + table);
+    l.b_off = (int)(l.v_off + v_bytes);
+    l.b_win = (int)round_up(st->rp_max, 16);
+    const int64_t b_bytes = std::max<int64_t>((int64_t)kExpandCols * st->rp_max * 2, 8 * kExpandCols * 4);
+    l.bytes = (int)(l.b_off + b_bytes);
+    return l;
+}
+
+// Chunks per expand workgroup, from the shapes alone.  Two pay off where many
+// small groups meet a wide output at low rank: measured on 1024 rows x 100
+// rank-16 adapters into 28672 columns, expand 61 -> 50.5 us (4 chunks 50.8,
+// 8 chunks 53.5).  Elsewhere one: the one-chunk kernel keeps more workgroups
+// per CU (decode 5.7 -> 6.6 us with two, rank-64 gate/up 28.3 -> 30.6 us).
+int choose_cpw(const lora_stack *st, int64_t n_rows, int forced)
+{
+    if (forced > 0)
+        return forced;
+    const int64_t pairs = ((st->D + kExpandCols - 1) / kExpandCols) * max_tiles_for(n_rows, st->n_slots);
+    return st->rp_max <= 16 && pairs >= 8192 ? 2 : 1;
+}
+
 bool stack_has_mfma_path(const lora_stack *st)
 {
     if (st->dtype != LORA_BF16)
@@ -213,6 +242,17 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     a.lds_v_off = l.v_off;
     a.lds_b_off = l.b_off;
     a.lds_bytes = l.bytes;
+    a.cpw = 1;
+    if (a.mfma_ok && a.sgmv_rows == kBgmvTileRows && st->rp_max <= 64) {
+        const int cpw = choose_cpw(st, seg->n_rows, seg->expand_chunks);
+        const ExpandLds ls = expand_stream_lds(st);
+        if (cpw > 1 && ls.bytes <= kExpandLdsMax) {
+            a.cpw = cpw;
+            a.lds_v_off = ls.v_off;
+            a.lds_b_off = ls.b_off;
+            a.lds_bytes = ls.bytes;
+        }
+    }
     a.counts = seg->counts;
     a.tiles = seg->tiles;
     return a;
@@ -482,6 +522,7 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     // 103 -> 83 us); the vector path still serves stacks without matrix-core
     // tiles and any group below a larger threshold set by the caller
     seg->dense_min = 1;
+    seg->expand_chunks = 0;
     seg->built = 0;
     seg->n_rows = 0;
     seg->n_slots = 0;
@@ -520,6 +561,14 @@ lora_status lora_segments_set_dense_min(lora_segments *seg, int m_min)
     if (!seg || m_min < 1)
         return LORA_E_ARG;
     seg->dense_min = m_min;
+    return LORA_OK;
+}
+
+lora_status lora_segments_set_expand_chunks(lora_segments *seg, int chunks)
+{
+    if (!seg || chunks < 0 || chunks > kMaxExpandChunks)
+        return LORA_E_ARG;
+    seg->expand_chunks = chunks;
     return LORA_OK;
 }
 
@@ -569,7 +618,10 @@ void mark_built(lora_segments *seg, const lora_stack *st, int64_t n_rows)
 // Grouping inside the shrink pays while the shrink grid fits on the chip in one
 // go: every workgroup repeats the grouping, so a grid of several waves of
 // workgroups would pay it several times over, more than the separate launch.
-constexpr int kFusedMaxBlocks = 256;   // one workgroup per compute unit
+// Measured: 384 workgroups (512 rows, 16 slots, 8 k-splits) still gain ~2 us
+// over the separate grouping launch; 656 (1024 rows, 100 slots, 4 k-splits)
+// lose ~2.7 us.
+constexpr int kFusedMaxBlocks = 512;   // two workgroups per compute unit
 
 bool fused_build_pays(const lora_stack *st, int64_t n_rows)
 {

@@ -37,7 +37,7 @@ class GpuRun:
     """One stack + one segments object holding problem ``p`` on the GPU."""
 
     def __init__(self, p, device="cuda:0", max_rows=None, dense_min=None, load_from_device=False,
-                 stream=None):
+                 stream=None, expand_chunks=None):
         self.p = p
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
@@ -47,6 +47,8 @@ class GpuRun:
         self.seg = lb.lora_segments_create(self.max_rows, p.n_slots)
         if dense_min is not None:
             lb.lora_segments_set_dense_min(self.seg, dense_min)
+        if expand_chunks is not None:
+            lb.lora_segments_set_expand_chunks(self.seg, expand_chunks)
         self._keep = []
         for s in range(p.n_slots):
             if p.ranks[s] > 0:
