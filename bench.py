@@ -3,9 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is the whole hot path over one batch, one lora_build_apply call: group
-the rows by adapter, shrink (v = A x), expand (y += scale B v).  Up to 1024
-rows that is two kernels (grouping fused into the shrink, then the expand);
-larger batches take three (grouping, shrink, expand).
+the rows by adapter, shrink (v = A x), expand (y += scale B v).  Decode-sized
+batches run it as one kernel (build_apply_kernel); other batches of up to 1024
+rows take two (grouping fused into the shrink, then the expand), larger ones
+three (grouping, shrink, expand).
 Inputs are resident in HBM before the timed region.  Steps rotate through
 independent buffer sets (stack + ids + x + y) totalling >= 512 MB so that the
 256 MB MALL cannot serve them: every step reads its weights and rows from HBM.
@@ -52,6 +53,7 @@ ROTATE_BYTES = 512 << 20       # 2x the 256 MB MALL
 DEFAULT_WORKLOAD = "decode_bgmv"
 FUSED_MAX_ROWS = 1024           # lora_build_shrink groups inside the shrink up to this many
 FUSED_MAX_BLOCKS = 512          # rows and shrink workgroups (the library's own rule)
+ONE_LAUNCH_MAX_BLOCKS = 1024    # grouping, shrink and expand in one launch up to this grid
 KERNEL_SOURCES = ("seg_build.hip", "shrink.hip", "expand.hip", "group.h", "mfma.h",
                   "device_common.h", "internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_bgmv.json")
@@ -81,8 +83,10 @@ def accounting(p) -> dict:
                 bytes=dict(shrink=x_bytes + live_a, expand=y_bytes + live_b,
                            seg_build=8 * p.n_rows + 4 * (p.n_slots + 1),
                            build_shrink=x_bytes + live_a + 8 * p.n_rows + 4 * (p.n_slots + 1),
+                           build_apply=x_bytes + y_bytes + live_a + live_b + 8 * p.n_rows
+                           + 4 * (p.n_slots + 1),
                            total=x_bytes + y_bytes + live_a + live_b),
-                flops=dict(total=int(flops), shrink=int(shrink_flops),
+                flops=dict(total=int(flops), shrink=int(shrink_flops), build_apply=int(flops),
                            build_shrink=int(shrink_flops), expand=int(flops - shrink_flops)))
 
 
@@ -95,8 +99,27 @@ def shrink_blocks(p) -> int:
     return ks * ((p.n_rows + 15) // 16 + min(p.n_slots, p.n_rows))
 
 
+def one_launch(p) -> bool:
+    """Whether lora_build_apply runs as one kernel (the library's rule,
+    restated to label the timings): the fused-grouping batches of 16-row tiles
+    and one expand chunk per workgroup whose grid of (k-splits + 256-column
+    chunks) x tile bound stays within ONE_LAUNCH_MAX_BLOCKS."""
+    if not (0 < p.n_rows <= FUSED_MAX_ROWS and shrink_blocks(p) <= FUSED_MAX_BLOCKS):
+        return False
+    rp_max = (p.r_max + 7) // 8 * 8
+    tiles = (p.n_rows + 15) // 16 + min(p.n_slots, p.n_rows)
+    chunks = (p.D + 255) // 256
+    if p.r_max >= 32 and p.n_rows >= 1024:
+        return False                      # may take 64-row tiles
+    if rp_max <= 16 and chunks * tiles >= 8192:
+        return False                      # several chunks per expand workgroup
+    return (shrink_blocks(p) // tiles + chunks) * tiles <= ONE_LAUNCH_MAX_BLOCKS
+
+
 def step_kernels(p) -> tuple:
     """The kernels one step launches, in order."""
+    if one_launch(p):
+        return ("build_apply",)
     if 0 < p.n_rows <= FUSED_MAX_ROWS and shrink_blocks(p) <= FUSED_MAX_BLOCKS:
         return ("build_shrink", "expand")
     return ("seg_build", "shrink", "expand")
@@ -217,9 +240,13 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
     # set already holds its segments and v, so each launch does its full work);
     # mean launch duration = region time / K, events only at the region's ends.
     # The split path's grouping and shrink are timed too, for comparison.
-    fns = dict(seg_build=build, shrink=shrink, build_shrink=build_shrink, expand=expand)
-    names = list(step_kernels(p)) + [k for k in ("seg_build", "shrink")
-                                     if k not in step_kernels(p)]
+    # With a one-launch step, the two-launch path's kernels (build_shrink,
+    # expand) are timed for comparison as well.
+    fns = dict(seg_build=build, shrink=shrink, build_shrink=build_shrink, expand=expand,
+               build_apply=step)
+    extra = ("build_shrink", "expand", "seg_build", "shrink") if one_launch(p) else \
+        ("seg_build", "shrink")
+    names = list(step_kernels(p)) + [k for k in extra if k not in step_kernels(p)]
     per = {}
     for name in names:
         fn = fns[name]
@@ -749,8 +776,9 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, copy_mb, wor
     # kernel functions behind each timed name (the grouping has a small-batch
     # and a chunked variant)
     names = {"seg_build": ("seg_build_kernel", "seg_build_small_kernel"),
-             "shrink": ("shrink_kernel",), "build_shrink": ("build_shrink_kernel",),
-             "expand": ("expand_kernel", "expand_kernel_bf16_short")}
+             "shrink": ("shrink_kernel", "shrink_kernel_tall"),
+             "build_shrink": ("build_shrink_kernel",), "build_apply": ("build_apply_kernel",),
+             "expand": ("expand_kernel", "expand_kernel_bf16_short", "expand_stream_kernel")}
 
     def bare(kname):
         head = kname.replace("(anonymous namespace)", "").split("(")[0].split("<")[0]

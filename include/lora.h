@@ -286,8 +286,21 @@ lora_status lora_build_shrink(const lora_stack *st, const void *x, int64_t ldx,
 /*
  * lora_build_shrink followed by lora_add_expand: one call for a whole batch
  * (grouping, add_shrink, add_expand with the per-row merge), with the results
- * and segments of lora_build_segments + lora_apply.  n_rows == 0 only writes
- * the (empty) segments.  Errors: LORA_E_ARG, LORA_E_HIP.
+ * and segments of lora_build_segments + lora_apply (y bit-identical: the same
+ * tile code on the same tile plan).  Decode-sized batches (those the fused
+ * grouping serves, on 16-row tiles with one column chunk per expand
+ * workgroup, whose grid of (k-splits + 256-column chunks) x tile bound is at
+ * most 1024 workgroups) run as ONE kernel: shrink and expand workgroups both
+ * group the ids in LDS, and each expand workgroup waits for the shrink
+ * workgroups of its tile through per-tile flags in the segments object
+ * (device-coherent stores and loads of v; every launch leaves the flags zero,
+ * so captured graphs replay correctly).  A wait that never ends is impossible
+ * by construction (an expand workgroup waits only on earlier-dispatched
+ * shrink workgroups that wait on nothing); as a guard, a wait bounded at
+ * well under a second gives up and is reported by lora_get_device_status.
+ * Calls on one segments object must not overlap (the flags are per object).
+ * n_rows == 0 only writes the (empty) segments.  Errors: LORA_E_ARG,
+ * LORA_E_HIP.
  */
 lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const void *x,
                              int64_t ldx, const int32_t *ids, int64_t n_rows, lora_segments *seg,
@@ -406,7 +419,9 @@ lora_status lora_segments_download(const lora_segments *seg, int32_t *perm, int3
                                    int32_t *active, int32_t *counts, void *stream);
 
 /* Number of bad ids seen by the last lora_build_segments (synchronises the
- * stream).  Returns LORA_E_BAD_IDS when it is nonzero, LORA_OK otherwise. */
+ * stream).  Returns LORA_E_BAD_IDS when it is nonzero, LORA_OK otherwise;
+ * LORA_E_HIP if a one-launch lora_build_apply on this object ever gave up
+ * waiting for its shrink (its y is then not valid). */
 lora_status lora_get_device_status(const lora_segments *seg, int64_t *n_bad, void *stream);
 
 /* Number of row tiles the last lora_build_segments gave each path (host

@@ -38,443 +38,11 @@
 #include "device_common.h"
 #include "internal.h"
 #include "mfma.h"
+#include "expand_tiles.h"
 
 namespace lora {
 
 namespace {
-
-constexpr int kCols = kExpandCols;
-
-__device__ __forceinline__ int slice_of(const ApplyArgs &a, int64_t c)
-{
-    int q = 0;
-    while (q + 1 < a.n_slices && c >= a.slice_off[q + 1])
-        ++q;
-    return q;
-}
-
-// bf16 hi / lo parts of two fp32 values, each packed as a bf16 pair.
-__device__ __forceinline__ void split_pair(float v0, float v1, uint32_t &hi, uint32_t &lo)
-{
-    hi = pack_bf16x2(v0, v1);
-    lo = pack_bf16x2(v0 - bf16_lo(hi), v1 - bf16_hi(hi));
-}
-
-// LDS row pitch (floats) of the staged v: nq slices of rp8 = round_up(r, 8)
-// ranks each, plus 4, so the row pitch is an odd number of 16-byte units and
-// the 16 rows that one operand read spans start in 16 distinct bank groups.
-__device__ __forceinline__ int v_pitch(int nq, int rp8)
-{
-    return nq * rp8 + 4;
-}
-
-// v of rows [p0, p0 + cnt) for slices [q_lo, q_lo + nq) ->
-// vs[u * v_pitch + qq * rp8 + j] (j < r; ranks r .. rp8 are not written), the
-// sum of the KS k-split partials in split order.  Each pass puts 8 loads
-// per thread in flight (8 / KS elements, every split of each; 16 splits go in
-// two batches of 8) before the first add, so a tile's v costs one round trip
-// per pass.  Indexes past the tile are clamped to its last element (read, not
-// stored).
-template <int KS>
-__device__ __forceinline__ void stage_v_ks(const ApplyArgs &a, int p0, int cnt, int r, int q_lo,
-                                           int nq, float *vs)
-{
-    constexpr int kL = KS < 8 ? KS : 8;              // splits per batch of loads
-    constexpr int kE = 8 / kL;                       // elements per thread per pass
-    const int SR = a.n_slices * a.r_max, pitch = nq * r, total = cnt * pitch;
-    const int rp8 = (r + 7) & ~7, P = v_pitch(nq, rp8);
-    const int64_t split = a.max_rows * (int64_t)SR;
-    const uint32_t m_pitch = div_magic(pitch), m_r = div_magic(r);   // cnt * pitch <= 2^14
-    for (int base = 0; base < total; base += kE * (int)blockDim.x) {
-        const float *src[kE];
-#pragma unroll
-        for (int e = 0; e < kE; ++e) {
-            const int idx = min(base + e * (int)blockDim.x + (int)threadIdx.x, total - 1);
-            const int u = div_small(idx, m_pitch);
-            const int rem = idx - u * pitch;
-            const int qq = div_small(rem, m_r);
-            const int j = rem - qq * r;
-            src[e] = a.vpart + (int64_t)(p0 + u) * SR + (q_lo + qq) * a.r_max + j;
-        }
-        float sum[kE];
-#pragma unroll
-        for (int k0 = 0; k0 < KS; k0 += kL) {
-            float part[kE][kL];
-#pragma unroll
-            for (int e = 0; e < kE; ++e)
-#pragma unroll
-                for (int kk = 0; kk < kL; ++kk)
-                    part[e][kk] = src[e][(k0 + kk) * split];
-#pragma unroll
-            for (int e = 0; e < kE; ++e)
-#pragma unroll
-                for (int kk = 0; kk < kL; ++kk)
-                    sum[e] = (k0 + kk == 0) ? part[e][0] : sum[e] + part[e][kk];
-        }
-#pragma unroll
-        for (int e = 0; e < kE; ++e) {
-            const int idx = base + e * (int)blockDim.x + (int)threadIdx.x;
-            if (idx < total) {
-                // (the decomposition again: cheaper than holding it across the loads)
-                const int u = div_small(idx, m_pitch);
-                const int rem = idx - u * pitch;
-                const int qq = div_small(rem, m_r);
-                vs[u * P + qq * rp8 + (rem - qq * r)] = sum[e];
-            }
-        }
-    }
-}
-
-__device__ __forceinline__ void stage_v(const ApplyArgs &a, int p0, int cnt, int r, int q_lo,
-                                        int nq, float *vs)
-{
-    switch (a.ks) {
-    case 1: stage_v_ks<1>(a, p0, cnt, r, q_lo, nq, vs); break;
-    case 2: stage_v_ks<2>(a, p0, cnt, r, q_lo, nq, vs); break;
-    case 4: stage_v_ks<4>(a, p0, cnt, r, q_lo, nq, vs); break;
-    case 8: stage_v_ks<8>(a, p0, cnt, r, q_lo, nq, vs); break;
-    default: stage_v_ks<16>(a, p0, cnt, r, q_lo, nq, vs); break;
-    }
-}
-
-template <int DT>
-__device__ __forceinline__ void merge16(const ApplyArgs &a, int64_t yi, bool h0, bool h1,
-                                        const Vec8<DT> &y0, const Vec8<DT> &y1, float scale,
-                                        const float (&acc)[16])
-{
-    if (h0) {
-        float f[8];
-        y0.to_f32(f);
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-            f[c] = fmaf(scale, acc[c], f[c]);
-        Vec8<DT>::store(a.y, yi, f);
-    }
-    if (h1) {
-        float f[8];
-        y1.to_f32(f);
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-            f[c] = fmaf(scale, acc[8 + c], f[c]);
-        Vec8<DT>::store(a.y, yi + 8, f);
-    }
-}
-
-// ---------------------------------------------------------------- SGMV (MFMA)
-
-// MT: row tiles (16 rows each) of the dense tile height this launch serves (1
-// for batches up to 4096 rows, 4 above), so the y registers match the shape.
-// WO: rank windows in the outer loop (B staged once per window, all MT row
-// tiles accumulated at once), for stacks whose B chunk needs several windows.
-template <int MT, bool WO>
-__device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
-                                 int p0, int cnt, int64_t c0, float *vs, uint16_t *bs)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, m = lane & 15;
-    const int n_nt = (cnt + 15) >> 4;
-    const int64_t cb = c0 + 64 * wave + 16 * g;      // lane's 16 columns
-    const bool in_d = cb < a.D;                      // whole 64-column blocks (slices % 64 == 0)
-    const int rp = (r + 7) & ~7, nj = (r + 15) >> 4;
-
-    // y of this lane's rows
-    Vec8<DT_BF16> y0[MT], y1[MT];
-#pragma unroll
-    for (int nt = 0; nt < MT; ++nt) {
-        const int u = 16 * nt + m;
-        if (nt < n_nt && u < cnt && in_d) {
-            const int64_t yi = (int64_t)rows[u] * a.ldy + cb;
-            y0[nt].load(a.y, yi);
-            y1[nt].load(a.y, yi + 8);
-        }
-    }
-    // the B chunk: columns [c0, c0 + 256) of the slot, ranks [w0, w0 + wl) of
-    // each column, as LDS [256][wl] (the whole [256][rp] block when the rank
-    // fits one window).  16-byte granules go global -> LDS directly, 16 bytes
-    // per lane, no register staging; thread t takes granules t, t + 256, ...
-    // The first window is in flight with y while v is staged, so B, v and y
-    // share one round trip.  Granules of columns past D are not loaded: those
-    // columns are whole 64-column blocks (D % 64 == 0 on this path) whose
-    // wavefronts never read B.
-    const int64_t bchunk = (int64_t)s * a.b_slot_stride + c0 * rp;
-    const int ncol = (int)min((int64_t)kCols, a.D - c0);
-    const int n_win = (rp + a.b_win - 1) / a.b_win;
-    auto stage_b = [&](int w0) {
-        const int gpw = min(a.b_win, rp - w0) >> 3;   // granules per column in the window
-        const int n_gran = ncol * gpw;
-        const uint32_t m_gpw = div_magic(gpw);
-        for (int i = 0; i < gpw; ++i) {
-            const int e = i * kCols + threadIdx.x;
-            if (e < n_gran) {
-                // one window: the chunk is contiguous and granule e sits at 8 e
-                const int col = div_small(e, m_gpw), gi = e - col * gpw;
-                const int64_t off = n_win == 1 ? 8 * (int64_t)e : (int64_t)col * rp + w0 + 8 * gi;
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(
-                        reinterpret_cast<const uint16_t *>(a.B) + bchunk + off),
-                    (__attribute__((address_space(3))) void *)(bs + 8 * (i * kCols + 64 * wave)), 16, 0,
-                    0);
-            }
-        }
-    };
-    stage_b(0);
-    const int q_lo = slice_of(a, c0);
-    const int nq = slice_of(a, min(c0 + kCols, a.D) - 1) - q_lo + 1;
-    const int P = v_pitch(nq, rp);
-    stage_v(a, p0, cnt, r, q_lo, nq, vs);
-    __syncthreads();   // B (first window) and v staged
-    const int qq = slice_of(a, c0 + 64 * wave) - q_lo;
-    // LDS column of M-tile mt for row m, in units of the window's rank pitch
-    int bcolumn[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-        bcolumn[mt] = 64 * wave + 16 * (m >> 2) + 4 * mt + (m & 3);
-
-    if constexpr (WO) {
-        // windows outer, N-tiles inner: B is staged once per window, every N-tile's
-        // accumulators stay live across the windows
-        f32x4_t acc[MT][4];
-    #pragma unroll
-        for (int nt = 0; nt < MT; ++nt)
-    #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < n_win; ++w) {
-            const int w0 = w * a.b_win, wl = min(a.b_win, rp - w0);
-            if (w > 0) {              // (uniform) restage: every wavefront is done with the last window
-                __syncthreads();
-                stage_b(w0);
-                __syncthreads();
-            }
-            if (!in_d)
-                continue;             // (uniform per wavefront: D is whole 64-column blocks)
-    #pragma unroll
-            for (int nt = 0; nt < MT; ++nt) {
-                if (nt >= n_nt)
-                    continue;         // (uniform) fully unrolled: the accumulators stay in registers
-                const int u = 16 * nt + m;
-                for (int jc = w0 >> 4; jc < min(nj, (w0 + wl + 15) >> 4); ++jc) {
-                    const int jo = jc * 16 + 8 * (g & 1);
-                    // 8 ranks of row u: two 16-byte reads (ranks past r masked)
-                    const float4 *vr = reinterpret_cast<const float4 *>(vs + u * P + qq * rp + jo);
-                    const float4 va = vr[0], vb = vr[1];
-                    const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-                    float f[8];
-    #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float v = (u < cnt && jo + i < r) ? vv[i] : 0.f;
-                        f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
-                    }
-                    uint4 vop;
-                    vop.x = pack_bf16x2(f[0], f[1]);
-                    vop.y = pack_bf16x2(f[2], f[3]);
-                    vop.z = pack_bf16x2(f[4], f[5]);
-                    vop.w = pack_bf16x2(f[6], f[7]);
-    #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        const uint4 bop = jo < w0 + wl
-                                              ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + (jo - w0))
-                                              : make_uint4(0, 0, 0, 0);
-                        acc[nt][mt] = mfma_bf16_16x16x32(bop, vop, acc[nt][mt]);
-                    }
-                }
-            }
-        }
-        if (in_d) {
-    #pragma unroll
-            for (int nt = 0; nt < MT; ++nt) {
-                const int u = 16 * nt + m;
-                if (nt < n_nt && u < cnt) {
-                    float f[16];
-    #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-    #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            f[4 * mt + i] = acc[nt][mt][i];
-                    merge16<DT_BF16>(a, (int64_t)rows[u] * a.ldy + cb, true, true, y0[nt], y1[nt], scale,
-                                     f);
-                }
-            }
-        }
-    } else {
-        // N-tiles outer: one set of accumulators (fewer registers); B is
-        // restaged per window and N-tile, so this order serves stacks whose
-        // B chunk fits one window
-    #pragma unroll
-        for (int nt = 0; nt < MT; ++nt) {
-            if (nt >= n_nt)
-                continue;   // (uniform) fully unrolled: y0[nt] / y1[nt] stay in registers
-            const int u = 16 * nt + m;
-            f32x4_t acc[4];
-    #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            for (int w = 0; w < n_win; ++w) {
-                const int w0 = w * a.b_win, wl = min(a.b_win, rp - w0);
-                if (n_win > 1 && (nt > 0 || w > 0)) {   // (uniform) restage this window
-                    __syncthreads();                    // every wavefront is done with the last one
-                    stage_b(w0);
-                    __syncthreads();
-                }
-                if (!in_d)
-                    continue;
-                for (int jc = w0 >> 4; jc < min(nj, (w0 + wl + 15) >> 4); ++jc) {
-                    const int jo = jc * 16 + 8 * (g & 1);
-                    // 8 ranks of row u: two 16-byte reads (ranks past r masked)
-                    const float4 *vr = reinterpret_cast<const float4 *>(vs + u * P + qq * rp + jo);
-                    const float4 va = vr[0], vb = vr[1];
-                    const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-                    float f[8];
-    #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float v = (u < cnt && jo + i < r) ? vv[i] : 0.f;
-                        f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
-                    }
-                    uint4 vop;
-                    vop.x = pack_bf16x2(f[0], f[1]);
-                    vop.y = pack_bf16x2(f[2], f[3]);
-                    vop.z = pack_bf16x2(f[4], f[5]);
-                    vop.w = pack_bf16x2(f[6], f[7]);
-    #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        const uint4 bop = jo < w0 + wl
-                                              ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + (jo - w0))
-                                              : make_uint4(0, 0, 0, 0);
-                        acc[mt] = mfma_bf16_16x16x32(bop, vop, acc[mt]);
-                    }
-                }
-            }
-            if (in_d && u < cnt) {
-                float f[16];
-    #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-    #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        f[4 * mt + i] = acc[mt][i];
-                merge16<DT_BF16>(a, (int64_t)rows[u] * a.ldy + cb, true, true, y0[nt], y1[nt], scale,
-                                 f);
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------ BGMV (vector)
-
-// One 16-byte word of a B pass: ranks [elem0, elem0 + 8) (bf16) or
-// [elem0, elem0 + 4) (fp32) of column gc; zero past D or past rp.
-template <int DT>
-__device__ __forceinline__ uint4 b_word(const ApplyArgs &a, int64_t bslot, int64_t gc, int rp,
-                                        int elem0)
-{
-    if (gc >= a.D || elem0 >= rp)
-        return make_uint4(0, 0, 0, 0);
-    if constexpr (DT == DT_BF16)
-        return load16(a.B, bslot + gc * rp + elem0);
-    else
-        return *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(a.B) + bslot +
-                                                gc * rp + elem0);
-}
-
-template <int DT>
-__device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
-                                 int p0, int cnt, int64_t c0, float *vs, uint32_t *bsh)
-{
-    // a pass: 2 words per column = 8 rank pairs (bf16) or 8 ranks (fp32);
-    // bsh[word lane w][column] holds rank pair / rank (pass base + w)
-    constexpr int kWords = 2;
-    constexpr int kElemsPerWord = DT == DT_BF16 ? 8 : 4;
-    constexpr int kPassElems = kWords * kElemsPerWord;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, m = lane & 15;
-    const bool row_ok = m < cnt;
-    const int64_t cb = c0 + 64 * wave + 16 * g;
-    const bool h0 = row_ok && cb < a.D, h1 = row_ok && cb + 8 < a.D;
-    const int64_t yi = (int64_t)rows[min(m, cnt - 1)] * a.ldy + cb;   // rows[0 .. cnt) only
-    Vec8<DT> y0, y1;
-    if (h0)
-        y0.load(a.y, yi);
-    if (h1)
-        y1.load(a.y, yi + 8);
-
-    const int rp = (r + 7) & ~7;
-    const int64_t bslot = (int64_t)s * a.b_slot_stride;
-    const int64_t gcol = c0 + threadIdx.x;            // the column this thread stages
-    // the first pass of B in flight while v is staged
-    uint4 w[kWords];
-#pragma unroll
-    for (int q4 = 0; q4 < kWords; ++q4)
-        w[q4] = b_word<DT>(a, bslot, gcol, rp, kElemsPerWord * q4);
-
-    const int q_lo = slice_of(a, c0);
-    const int nq = slice_of(a, min(c0 + kCols, a.D) - 1) - q_lo + 1;
-    stage_v(a, p0, cnt, r, q_lo, nq, vs);
-    const int P = v_pitch(nq, rp);
-    const int cl = 64 * wave + 16 * g;               // lane's first column in the chunk
-    int qh[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-        qh[hh] = slice_of(a, min(cb + 8 * hh, a.D - 1)) - q_lo;
-
-    float acc[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c)
-        acc[c] = 0.f;
-
-    for (int j0 = 0; j0 < rp; j0 += kPassElems) {
-#pragma unroll
-        for (int q4 = 0; q4 < kWords; ++q4) {
-            bsh[(4 * q4 + 0) * kCols + threadIdx.x] = w[q4].x;
-            bsh[(4 * q4 + 1) * kCols + threadIdx.x] = w[q4].y;
-            bsh[(4 * q4 + 2) * kCols + threadIdx.x] = w[q4].z;
-            bsh[(4 * q4 + 3) * kCols + threadIdx.x] = w[q4].w;
-        }
-        // v and this pass of B staged.  The barriers order LDS only, so the
-        // next pass's B, issued before this pass's arithmetic, stays in flight
-        // across them.
-        lds_barrier();
-        if (j0 + kPassElems < rp) {
-#pragma unroll
-            for (int q4 = 0; q4 < kWords; ++q4)
-                w[q4] = b_word<DT>(a, bslot, gcol, rp, j0 + kPassElems + kElemsPerWord * q4);
-        }
-        if constexpr (DT == DT_BF16) {
-            const int np = min(kPassElems, rp - j0) / 2;
-            for (int pp = 0; pp < np; ++pp) {
-                const int j = j0 + 2 * pp;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const float *vr = vs + m * P + qh[hh] * rp;
-                    const float v0 = (row_ok && j < r) ? vr[j] : 0.f;
-                    const float v1 = (row_ok && j + 1 < r) ? vr[j + 1] : 0.f;
-                    uint32_t hi, lo;
-                    split_pair(v0, v1, hi, lo);
-                    const uint4 b0 = *reinterpret_cast<const uint4 *>(&bsh[pp * kCols + cl + 8 * hh]);
-                    const uint4 b1 = *reinterpret_cast<const uint4 *>(&bsh[pp * kCols + cl + 8 * hh + 4]);
-                    const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        const float t = dot2_bf16(bw[c], hi, acc[8 * hh + c]);
-                        acc[8 * hh + c] = dot2_bf16(bw[c], lo, t);
-                    }
-                }
-            }
-        } else {
-            const float *bf = reinterpret_cast<const float *>(bsh);   // [jj][col]
-            for (int jj = 0; jj < kPassElems && j0 + jj < r; ++jj) {
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const float vj = row_ok ? vs[m * P + qh[hh] * rp + j0 + jj] : 0.f;
-#pragma unroll
-                    for (int c = 0; c < 8; ++c)
-                        acc[8 * hh + c] = fmaf(bf[jj * kCols + cl + 8 * hh + c], vj,
-                                               acc[8 * hh + c]);
-                }
-            }
-        }
-        lds_barrier();   // bsh is restaged by the next pass
-    }
-    merge16<DT>(a, yi, h0, h1, y0, y1, scale, acc);
-}
 
 // Dynamic LDS: [rows: 64 int][slot table: rank, scale (when n_slots <= 256)]
 // [v staging at lds_v_off][B staging at lds_b_off]; the host sizes it.

@@ -88,6 +88,7 @@ struct ApplyArgs {
     int lds_b_off;
     int lds_bytes;             // expand: dynamic LDS bytes
     int cpw;                   // expand: 256-column chunks per workgroup (1: one chunk)
+    int32_t *sync;             // one-launch apply: timeouts, per-tile flags and counters
     // batch
     const int32_t *counts;
     const ShrinkTile *tiles;
@@ -104,6 +105,13 @@ constexpr int kFusedMaxRows = 1024;
 hipError_t launch_build_shrink(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
                                hipStream_t stream);
 hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream);
+// grouping, shrink and expand in one launch (16-row tiles, one chunk per expand
+// workgroup); a.sync: kSyncFlags + max_tiles * kSyncTileInts ints, zeroed at
+// creation (per tile: the split flags, then the expand workgroups' counter)
+constexpr int kSyncTimeouts = 2, kSyncFlags = 16, kSyncTileInts = 32;
+static_assert(kSyncTileInts > kMaxKSplit, "a tile's flags and counter");
+hipError_t launch_build_apply(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
+                              hipStream_t stream);
 // Merge of one slot into a dense weight (rows tiled per slice, 64 rows a tile).
 struct MergeArgs {
     const void *A;             // the slot's A: [n_slices][r_max][k]
@@ -187,6 +195,7 @@ struct lora_segments {
     int max_tiles;
     int dense_min;
     int expand_chunks;   // 0: chosen from the shapes
+    int32_t *sync;       // one-launch apply state: kSyncFlags + max_tiles * kSyncTileInts ints
     int32_t *perm;
     int32_t *seg_off;
     int32_t *active;

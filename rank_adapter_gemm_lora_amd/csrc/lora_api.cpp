@@ -106,6 +106,7 @@ void free_segments(lora_segments *seg)
     (void)hipFree(seg->chunk);
     (void)hipFree(seg->chunk_bad);
     (void)hipFree(seg->binfo);
+    (void)hipFree(seg->sync);
     delete seg;
 }
 
@@ -255,6 +256,7 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     }
     a.counts = seg->counts;
     a.tiles = seg->tiles;
+    a.sync = seg->sync;
     return a;
 }
 
@@ -523,6 +525,7 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     // tiles and any group below a larger threshold set by the caller
     seg->dense_min = 1;
     seg->expand_chunks = 0;
+    seg->sync = nullptr;
     seg->built = 0;
     seg->n_rows = 0;
     seg->n_slots = 0;
@@ -537,6 +540,9 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->chunk), sizeof(int32_t) * n_chunks * (n_slots + 1));
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->chunk_bad), sizeof(int32_t) * n_chunks);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->binfo), sizeof(int4) * (n_slots + 1));
+    const size_t sync_ints = kSyncFlags + (size_t)seg->max_tiles * kSyncTileInts;
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->sync), sizeof(int32_t) * sync_ints);
+    if (e == hipSuccess) e = hipMemset(seg->sync, 0, sizeof(int32_t) * sync_ints);
     if (e == hipSuccess) e = hipMemset(seg->counts, 0, sizeof(int32_t) * kCntSlots);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -630,6 +636,21 @@ bool fused_build_pays(const lora_stack *st, int64_t n_rows)
     return (int64_t)choose_ks(st->k, n_rows, sgmv_rows_for(st, n_rows)) *
                max_tiles_for(n_rows, st->n_slots) <=
            kFusedMaxBlocks;
+}
+
+// Grouping, shrink and expand in one launch: batches the fused grouping
+// serves, on 16-row tiles with one column chunk per expand workgroup, while the
+// whole grid (shrink plus expand workgroups, each grouping the batch in LDS)
+// stays within about one wave of workgroups on the chip.
+constexpr int kOneLaunchMaxBlocks = 1024;
+
+bool one_launch_pays(const lora_stack *st, const ApplyArgs &a, int64_t n_rows)
+{
+    if (!fused_build_pays(st, n_rows) || a.sgmv_rows != kBgmvTileRows || a.cpw != 1)
+        return false;
+    const int64_t tiles = max_tiles_for(n_rows, st->n_slots);
+    const int64_t chunks = (st->D + kExpandCols - 1) / kExpandCols;
+    return (a.ks + chunks) * tiles <= kOneLaunchMaxBlocks;
 }
 
 bool x_ok(const lora_stack *st, const void *x, int64_t ldx)
@@ -746,6 +767,27 @@ lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const v
         return LORA_E_ARG;
     if (n_rows > 0 && (!x_ok(st, x, ldx) || !y_ok(st, y, ldy)))
         return LORA_E_ARG;
+    if (n_rows > 0 && fused_build_pays(st, n_rows)) {
+        // one launch when the grid stays small (the decode step)
+        const int64_t prev_rows = seg->n_rows;
+        const int prev_built = seg->built, prev_slots = seg->n_slots;
+        mark_built(seg, st, n_rows);
+        ApplyArgs a = make_args(st, seg);
+        if (one_launch_pays(st, a, n_rows)) {
+            a.x = x;
+            a.ldx = ldx;
+            a.y = y;
+            a.ldy = ldy;
+            LORA_TRY(launch_build_apply(st->dtype == LORA_BF16 ? DT_BF16 : DT_F32, a,
+                                        make_seg_args(st, ids, n_rows, seg),
+                                        max_tiles_for(n_rows, st->n_slots),
+                                        reinterpret_cast<hipStream_t>(stream)));
+            return LORA_OK;
+        }
+        seg->n_rows = prev_rows;
+        seg->built = prev_built;
+        seg->n_slots = prev_slots;
+    }
     const lora_status s1 = lora_build_shrink(st, x, ldx, ids, n_rows, seg, stream);
     if (s1 != LORA_OK || n_rows == 0)
         return s1;
@@ -776,12 +818,15 @@ lora_status lora_get_device_status(const lora_segments *seg, int64_t *n_bad, voi
 {
     if (!seg || !seg->built)
         return LORA_E_ARG;
-    int32_t c[kCntSlots];
+    int32_t c[kCntSlots], sy[kSyncFlags];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     LORA_TRY(hipMemcpyAsync(c, seg->counts, sizeof c, hipMemcpyDeviceToHost, s));
+    LORA_TRY(hipMemcpyAsync(sy, seg->sync, sizeof sy, hipMemcpyDeviceToHost, s));
     LORA_TRY(hipStreamSynchronize(s));
     if (n_bad)
         *n_bad = c[kCntBad];
+    if (sy[kSyncTimeouts] > 0)
+        return LORA_E_HIP;   // a one-launch apply gave up waiting for its v
     return c[kCntBad] > 0 ? LORA_E_BAD_IDS : LORA_OK;
 }
 

@@ -24,6 +24,7 @@
 // position; the expand sums the splits in split order, so results are
 // bit-reproducible and no workgroup waits on another.
 #include "device_common.h"
+#include "expand_tiles.h"
 #include "group.h"
 #include "internal.h"
 #include "mfma.h"
@@ -41,7 +42,19 @@ __device__ __forceinline__ float *v_out(const ApplyArgs &a, int ks, int pos)
     return a.vpart + ((int64_t)ks * a.max_rows + pos) * SR;
 }
 
-template <int DT>
+// One element of v: a plain store, or a device-coherent one (relaxed agent
+// scope: written through to where every XCD reads it) for a reader in the same
+// launch.
+template <bool COH>
+__device__ __forceinline__ void put_v(float *p, float x)
+{
+    if constexpr (COH)
+        __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = x;
+}
+
+template <int DT, bool COH>
 __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, int p0,
                                  int cnt, int ks)
 {
@@ -90,11 +103,11 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
                 const int j = (lane >> 2) & 15;
                 const float t0 = wave_reduce_scatter16(acc0);
                 if ((lane & 3) == 0 && j0 + j < r)
-                    v_out(a, ks, p0 + u0)[q * a.r_max + j0 + j] = t0;
+                    put_v<COH>(v_out(a, ks, p0 + u0) + q * a.r_max + j0 + j, t0);
                 if (has1) {
                     const float t1 = wave_reduce_scatter16(acc1);
                     if ((lane & 3) == 0 && j0 + j < r)
-                        v_out(a, ks, p0 + u1)[q * a.r_max + j0 + j] = t1;
+                        put_v<COH>(v_out(a, ks, p0 + u1) + q * a.r_max + j0 + j, t1);
                 }
             }
         }
@@ -114,6 +127,7 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 // afterwards, so no branch surrounds a load.  (Measured: branches around the
 // loads, or a select of "load or zero" on a runtime tile count, made the
 // compiler drain the loads in flight at every step.)
+template <bool COH>
 __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, int p0,
                                  int cnt, int ks)
 {
@@ -198,7 +212,7 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
                     for (int i = 0; i < 4; ++i) {
                         const int u = 4 * (ln >> 4) + i;
                         if (u < cnt)
-                            v_out(a, ks, p0 + u)[q * a.r_max + j] = v[i];
+                            put_v<COH>(v_out(a, ks, p0 + u) + q * a.r_max + j, v[i]);
                     }
                 }
             }
@@ -398,26 +412,28 @@ __device__ void sgmv_shrink_tile_tall(const ApplyArgs &a, const int32_t *rows, i
 }
 
 // One tile, its rows already in LDS; r is the slot's rank.
-template <int DT, int MT>
+// COH: v stored device-coherent (read in the same launch; 16-row tiles only).
+template <int DT, int MT, bool COH = false>
 __device__ __forceinline__ void shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r,
                                             int p0, int cnt, int path, int ks)
 {
+    static_assert(!(COH && MT == 4), "coherent v stores: 16-row tiles only");
     if constexpr (DT == DT_BF16) {
         if (path == kTileSgmv && a.mfma_ok) {
             if constexpr (MT == 4)
                 sgmv_shrink_tile_tall(a, rows, s, r, p0, cnt, ks);
             else
-                sgmv_shrink_tile(a, rows, s, r, p0, cnt, ks);
+                sgmv_shrink_tile<COH>(a, rows, s, r, p0, cnt, ks);
             return;
         }
     }
     // BGMV tile, or a dense tile of a stack without the MFMA path
     for (int sub = 0; sub < cnt; sub += kBgmvTileRows)
-        bgmv_shrink_tile<DT>(a, rows + sub, s, r, p0 + sub, min(kBgmvTileRows, cnt - sub), ks);
+        bgmv_shrink_tile<DT, COH>(a, rows + sub, s, r, p0 + sub, min(kBgmvTileRows, cnt - sub), ks);
 }
 
 template <int DT, int MT>
-__global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
+__device__ __forceinline__ void shrink_body(const ApplyArgs &a)
 {
     __shared__ int32_t rows[kSgmvTileRows];
     __shared__ int32_t rank[LORA_MAX_SLOTS];
@@ -438,6 +454,21 @@ __global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
     if (r == 0)
         return;   // slot emptied since the grouping was built: nothing to compute
     shrink_tile<DT, MT>(a, rows, h.x, r, h.y, h.z, h.w, ks);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
+{
+    shrink_body<DT, 1>(a);
+}
+
+// 64-row tiles, held to three wavefronts per SIMD: the tile's 48 KB ring lets
+// three workgroups share a CU, and the register budget is kept to match
+// (without the bound, small code changes tipped it to two).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void shrink_kernel_tall(ApplyArgs a)
+{
+    shrink_body<DT_BF16, 4>(a);
 }
 
 // Grouping and shrink in one launch, for small batches.  Every workgroup
@@ -500,7 +531,178 @@ __global__ __launch_bounds__(256) void build_shrink_kernel(ApplyArgs a, SegBuild
     }
 }
 
+// Grouping, shrink and expand in one launch (decode-sized batches of 16-row
+// tiles).  The grid is one list of workgroups: first ks x tile-bound shrink
+// workgroups (split ks % a.ks of tile b / a.ks, so one split's workgroups share
+// an XCD when 8 | ks), then chunks x tile-bound expand workgroups (chunk
+// c % n_chunks of tile c / n_chunks).  Every workgroup groups the batch in LDS
+// as build_shrink_kernel does, so neither side reads anything the other writes
+// except v:
+//   shrink  computes its split of the tile's v, stores it device-coherent
+//           (written through past the XCD's L2), waits until the stores are
+//           acknowledged, then sets the tile's flag for its split to 1;
+//   expand  puts its y and B loads in flight, then each wavefront polls the
+//           tile's split flags (device-coherent loads) until all are 1, reads
+//           v device-coherent, counts itself on the tile's counter and
+//           finishes the tile; the tile's last expand workgroup to count
+//           clears the tile's flags and counter.
+// So every launch starts and ends with all flags zero: a launch (or a replay of
+// a captured graph) never sees an earlier launch's flags, and no counter is
+// shared by the whole grid (one such counter, bumped by every workgroup,
+// measured ~7 us per launch).  Each tile's state sits in its own 128 bytes.
+// An expand workgroup waits only on shrink workgroups of lower index, which
+// are dispatched before it and wait on nothing, so the waits always end; a
+// wait that exceeds kWaitSpins polls (well under a second) gives up and counts
+// a timeout that lora_get_device_status reports.
+constexpr int kWaitSpins = 1 << 18;
+
+template <int DT>
+__global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildArgs sb, int n_prod,
+                                                          int n_chunks)
+{
+    __shared__ GroupLds g;
+    __shared__ int wc[2][kGroupPer * kGroupWaves];
+    __shared__ int32_t rows[kSgmvTileRows];
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // expand staging
+    const int tid = threadIdx.x, b = blockIdx.x;
+    int32_t *sync = a.sync;
+    const bool prod = b < n_prod;
+    const int t = prod ? b / a.ks : (b - n_prod) / n_chunks;
+    const int ks = prod ? b - t * a.ks : 0;
+    const int N = sb.n_slots;
+    int key[kGroupPer], rank[kGroupPer];
+    group_hist(sb.ids, (int)sb.n, N, sb.slot_rank, g, key);
+    group_scan(g, N, sb.dense_min, 4);
+    if (t < g.n_sg + g.n_bg) {
+        int s, m;
+        locate_tile(g, N, t, s, m);
+        const BucketPlan p = bucket_plan(g, s, N, sb.dense_min, 4);
+        const int lo = m << p.shift;
+        const int cnt = min(1 << p.shift, p.count - lo), p0 = p.first + lo;
+        group_rank(key, s, wc[0], rank);
+#pragma unroll
+        for (int j = 0; j < kGroupPer; ++j) {
+            const int u = rank[j] - lo;
+            if (rank[j] >= 0 && u >= 0 && u < cnt)
+                rows[u] = j * kGroupThreads + tid;
+        }
+        __syncthreads();
+        const int r = g.rank[s];
+        if (prod) {
+            shrink_tile<DT, 1, true>(a, rows, s, r, p0, cnt, p.path, ks);
+            LORA_WAIT_VM(0);   // this wavefront's v stores are acknowledged
+            __syncthreads();   // ... and every other wavefront's
+            if (tid == 0)
+                __hip_atomic_store(sync + kSyncFlags + t * kSyncTileInts + ks, 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            if (ks == 0) {
+                // the segments object receives what the grouping kernel writes
+#pragma unroll
+                for (int j = 0; j < kGroupPer; ++j) {
+                    const int u = rank[j] - lo;
+                    if (rank[j] >= 0 && u >= 0 && u < cnt) {
+                        const int row = j * kGroupThreads + tid;
+                        sb.perm[p0 + u] = row;
+                        sb.tiles[t].rows[u] = row;
+                    }
+                }
+                if (tid == 0)
+                    *reinterpret_cast<int4 *>(&sb.tiles[t]) = make_int4(s, p0, cnt, p.path);
+            }
+        } else {
+            const int64_t c0 = (int64_t)(b - n_prod - t * n_chunks) * kCols;
+            const float scale = a.scale[s];
+            int32_t *flag = sync + kSyncFlags + t * kSyncTileInts;
+            const int n_split = a.ks;
+            // each wavefront polls the tile's split flags itself (no barrier,
+            // so the y and B loads already issued stay in flight)
+            auto wait = [=]() {
+                const int lane = threadIdx.x & 63;
+                for (int spins = 0;; ++spins) {
+                    const bool ok = lane >= n_split ||
+                                    __hip_atomic_load(flag + lane, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) == 1;
+                    if (__all(ok))
+                        break;
+                    if (spins >= kWaitSpins) {
+                        if (lane == 0)
+                            __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                // v is read after this point, never hoisted above the poll
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            };
+            // once every thread's v is in LDS this workgroup is done with the
+            // tile's flags: it counts itself on the tile's counter (the atomic's
+            // round trip overlaps the products; its result is used at the end)
+            int seen = -1;
+            auto v_read = [&]() {
+                lds_barrier();
+                if (tid == 0 && seen < 0)
+                    seen = __hip_atomic_fetch_add(flag + kMaxKSplit, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+            };
+            float *vs = reinterpret_cast<float *>(lds + a.lds_v_off);
+            unsigned char *bst = lds + a.lds_b_off;
+            bool done = false;
+            if constexpr (DT == DT_BF16) {
+                if (p.path == kTileSgmv && a.mfma_ok) {
+                    sgmv_expand_tile<1, false, true>(a, rows, s, r, scale, p0, cnt, c0, vs,
+                                                     reinterpret_cast<uint16_t *>(bst), wait, v_read);
+                    done = true;
+                }
+            }
+            if (!done) {
+                for (int sub = 0; sub < cnt; sub += kBgmvTileRows) {
+                    bgmv_expand_tile<DT, true>(a, rows + sub, s, r, scale, p0 + sub,
+                                               min(kBgmvTileRows, cnt - sub), c0, vs,
+                                               reinterpret_cast<uint32_t *>(bst), wait, v_read);
+                    __syncthreads();   // LDS is restaged by the next sub-tile
+                }
+            }
+            // the tile's last expand workgroup to count itself clears the
+            // tile's flags and counter for the next launch (every other one has
+            // finished polling and reading v before it counted)
+            if (tid == 0 && seen == n_chunks - 1) {
+                for (int k = 0; k < n_split; ++k)
+                    __hip_atomic_store(flag + k, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(flag + kMaxKSplit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    if (prod && ks == 0 && t == 0) {
+        // rows without an adapter, then seg_off, active and the counts
+        group_rank(key, N, wc[1], rank);
+#pragma unroll
+        for (int j = 0; j < kGroupPer; ++j)
+            if (rank[j] >= 0)
+                sb.perm[g.seg[N] + rank[j]] = j * kGroupThreads + tid;
+        group_store(g, N, sb.seg_off, sb.active, sb.counts);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_build_apply(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
+                              hipStream_t stream)
+{
+    if (max_tiles <= 0 || sb.n > kGroupRows || sb.sgmv_rows != kBgmvTileRows || a.cpw != 1 ||
+        a.ks > kMaxKSplit || !a.sync)
+        return hipErrorInvalidValue;
+    const int n_chunks = (int)((a.D + kCols - 1) / kCols);
+    const int n_prod = a.ks * max_tiles;
+    const dim3 grid((unsigned)(n_prod + n_chunks * max_tiles));
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(build_apply_kernel<DT_BF16>, grid, dim3(256), a.lds_bytes, stream, a, sb,
+                           n_prod, n_chunks);
+    else
+        hipLaunchKernelGGL(build_apply_kernel<DT_F32>, grid, dim3(256), a.lds_bytes, stream, a, sb,
+                           n_prod, n_chunks);
+    return hipGetLastError();
+}
 
 hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream)
 {
@@ -510,11 +712,11 @@ hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream
     const bool tall = a.sgmv_rows > kBgmvTileRows;   // 64-row dense tiles
     if (dtype == DT_BF16) {
         if (tall)
-            hipLaunchKernelGGL((shrink_kernel<DT_BF16, 4>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(shrink_kernel_tall, grid, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((shrink_kernel<DT_BF16, 1>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(shrink_kernel<DT_BF16>, grid, dim3(256), 0, stream, a);
     } else {
-        hipLaunchKernelGGL((shrink_kernel<DT_F32, 1>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(shrink_kernel<DT_F32>, grid, dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -42,6 +42,7 @@ def _fused_vs_split(p, dm, what):
             y = run.y_host()
             seg = run.segments()
             tc = lb.lora_segments_tile_counts(run.seg, run.stream)
+            lb.lora_get_device_status(run.seg, run.stream)   # raises if a wait timed out
         finally:
             run.close()
         out.append((y, seg, tc))
@@ -131,6 +132,35 @@ def test_build_apply_repeated_layers():
         run.close()
 
 
+@pytest.mark.parametrize("name", ["decode_bgmv", "tiny_ref"])
+def test_build_apply_back_to_back(name):
+    """Ten one-launch calls in a row on one stream, no host synchronisation
+    between them (each on a fresh copy of the base y, alternating two adapter
+    mixes): every launch opens a new epoch, so none may consume the v of an
+    earlier one.  The last call's y matches the oracle, its segments are
+    exact, and no wait timed out."""
+    base = synth.make_workload(name)
+    other = base.ids.copy()[::-1].copy()
+    run = GpuRun(base)
+    try:
+        y0 = run.y.clone()
+        ids = [torch.from_numpy(base.ids).to(run.device), torch.from_numpy(other).to(run.device)]
+        note(f"back-to-back build_apply {name}")
+        for i in range(10):
+            run.ids.copy_(ids[i % 2], non_blocking=True)
+            run.y.copy_(y0, non_blocking=True)
+            run.build_apply()
+        p = synth.make_random(0, n_rows=base.n_rows, k=base.k, slice_d=base.slice_d,
+                              n_slots=base.n_slots, ranks=base.ranks, r_max=base.r_max,
+                              ids=other, dtype=base.dtype)
+        p.A, p.B, p.alphas, p.x, p.y = base.A, base.B, base.alphas, base.x, base.y
+        check_against_oracle(p, run.y_host(), what=f"{name} back-to-back")
+        _seg_equal(run.segments(), p, f"{name} back-to-back")
+        lb.lora_get_device_status(run.seg, run.stream)
+    finally:
+        run.close()
+
+
 @pytest.mark.parametrize("n_rows", [256, 3000])
 def test_build_apply_graph_replay_any_mix(n_rows):
     """The launch shapes depend only on the batch shape, so one captured HIP
@@ -168,6 +198,7 @@ def test_build_apply_graph_replay_any_mix(n_rows):
             check_against_oracle(p, run.y_host(), what=f"replay {rep}")
             _seg_equal(lb.lora_segments_download(run.seg, p.n_rows, p.n_slots, run.stream), p,
                        f"replay {rep}")
+            lb.lora_get_device_status(run.seg, run.stream)
         del graph
     finally:
         run.close()
