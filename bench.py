@@ -51,9 +51,6 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATE_BYTES = 512 << 20       # 2x the 256 MB MALL
 DEFAULT_WORKLOAD = "decode_bgmv"
-FUSED_MAX_ROWS = 1024           # lora_build_shrink groups inside the shrink up to this many
-FUSED_MAX_BLOCKS = 512          # rows and shrink workgroups (the library's own rule)
-ONE_LAUNCH_MAX_BLOCKS = 1024    # grouping, shrink and expand in one launch up to this grid
 KERNEL_SOURCES = ("seg_build.hip", "shrink.hip", "expand.hip", "group.h", "mfma.h",
                   "device_common.h", "internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_bgmv.json")
@@ -90,39 +87,9 @@ def accounting(p) -> dict:
                            build_shrink=int(shrink_flops), expand=int(flops - shrink_flops)))
 
 
-def shrink_blocks(p) -> int:
-    """Workgroups of the shrink launch: k-splits x tile bound (the library's
-    choice of split count and its tile bound, restated to label the timings)."""
-    ks = max(1, p.k // 512)
-    ks = min(ks, max(1, 4096 // max(1, p.n_rows)), 16)
-    ks = 1 << (ks.bit_length() - 1)
-    return ks * ((p.n_rows + 15) // 16 + min(p.n_slots, p.n_rows))
-
-
-def one_launch(p) -> bool:
-    """Whether lora_build_apply runs as one kernel (the library's rule,
-    restated to label the timings): the fused-grouping batches of 16-row tiles
-    and one expand chunk per workgroup whose grid of (k-splits + 256-column
-    chunks) x tile bound stays within ONE_LAUNCH_MAX_BLOCKS."""
-    if not (0 < p.n_rows <= FUSED_MAX_ROWS and shrink_blocks(p) <= FUSED_MAX_BLOCKS):
-        return False
-    rp_max = (p.r_max + 7) // 8 * 8
-    tiles = (p.n_rows + 15) // 16 + min(p.n_slots, p.n_rows)
-    chunks = (p.D + 255) // 256
-    if p.r_max >= 32 and p.n_rows >= 1024:
-        return False                      # may take 64-row tiles
-    if rp_max <= 16 and chunks * tiles >= 8192:
-        return False                      # several chunks per expand workgroup
-    return (shrink_blocks(p) // tiles + chunks) * tiles <= ONE_LAUNCH_MAX_BLOCKS
-
-
-def step_kernels(p) -> tuple:
-    """The kernels one step launches, in order."""
-    if one_launch(p):
-        return ("build_apply",)
-    if 0 < p.n_rows <= FUSED_MAX_ROWS and shrink_blocks(p) <= FUSED_MAX_BLOCKS:
-        return ("build_shrink", "expand")
-    return ("seg_build", "shrink", "expand")
+# what each launch count of lora_build_apply (lora_build_apply_plan) runs
+STEP_KERNELS = {1: ("build_apply",), 2: ("build_shrink", "expand"),
+                3: ("seg_build", "shrink", "expand"), 5: ("seg_build", "shrink", "expand")}
 
 
 def kernel_source_hash() -> str:
@@ -244,9 +211,11 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
     # expand) are timed for comparison as well.
     fns = dict(seg_build=build, shrink=shrink, build_shrink=build_shrink, expand=expand,
                build_apply=step)
-    extra = ("build_shrink", "expand", "seg_build", "shrink") if one_launch(p) else \
+    n_launch = lb.lora_build_apply_plan(sets[0].stack, p.n_rows, sets[0].seg)
+    step_k = STEP_KERNELS[n_launch]
+    extra = ("build_shrink", "expand", "seg_build", "shrink") if n_launch == 1 else \
         ("seg_build", "shrink")
-    names = list(step_kernels(p)) + [k for k in extra if k not in step_kernels(p)]
+    names = list(step_k) + [k for k in extra if k not in step_k]
     per = {}
     for name in names:
         fn = fns[name]
@@ -311,7 +280,8 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
         bs.close(lb)
     torch.cuda.synchronize()
     return dict(wall_s=wall, gpu_ms=gpu_ms, n_sets=n_sets, set_bytes=set_bytes(p),
-                kernel_us=per, tiles=dict(bgmv=n_bgmv, sgmv=n_sgmv), graph_ms=graph_ms,
+                kernel_us=per, step_kernels=step_k, tiles=dict(bgmv=n_bgmv, sgmv=n_sgmv),
+                graph_ms=graph_ms,
                 graph_chain_ms=graph_chain_ms)
 
 
@@ -357,7 +327,7 @@ def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -
     warm = run_gpu(p, steps, warmup, rotate=False, dense_min=dense_min, graph=False) if rotate else g
     ms = g["gpu_ms"] / steps
     ku = g["kernel_us"]
-    dom = max(step_kernels(p), key=lambda k: ku[k])
+    dom = max(g["step_kernels"], key=lambda k: ku[k])
     achieved = acct["bytes"][dom] / (ku[dom] * 1e-6) / 1e9
     traffic = committed_traffic(name)
     roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
@@ -381,7 +351,7 @@ def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -
                    "parallelism": "single GPU"},
         "step_hbm_gbs": round(acct["bytes"]["total"] / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(acct["bytes"]["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "step_kernels": list(step_kernels(p)),
+        "step_kernels": list(g["step_kernels"]),
         "kernel_us": {k: round(v, 3) for k, v in ku.items()},
         "kernel_gbs": {k: round(acct["bytes"][k] / (ku[k] * 1e-6) / 1e9, 1)
                        for k in ku if k != "seg_build"},

@@ -290,7 +290,8 @@ lora_status lora_build_shrink(const lora_stack *st, const void *x, int64_t ldx,
  * tile code on the same tile plan).  Decode-sized batches (those the fused
  * grouping serves, on 16-row tiles with one column chunk per expand
  * workgroup, whose grid of (k-splits + 256-column chunks) x tile bound is at
- * most 1024 workgroups) run as ONE kernel: shrink and expand workgroups both
+ * at most the workgroups the chip holds at once, plus a quarter) run as ONE
+ * kernel (lora_build_apply_plan tells which): shrink and expand workgroups both
  * group the ids in LDS, and each expand workgroup waits for the shrink
  * workgroups of its tile through per-tile flags in the segments object
  * (device-coherent stores and loads of v; every launch leaves the flags zero,
@@ -305,6 +306,21 @@ lora_status lora_build_shrink(const lora_stack *st, const void *x, int64_t ldx,
 lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const void *x,
                              int64_t ldx, const int32_t *ids, int64_t n_rows, lora_segments *seg,
                              void *stream);
+
+/*
+ * Kernel launches a lora_build_apply of n_rows rows on (st, seg) makes, with
+ * seg's current tile policy: 1 (one kernel: the decode path), 2 (grouping
+ * inside the shrink, then the expand), 3 (grouping, shrink, expand) or 5 (the
+ * chunked grouping's three kernels, shrink, expand); 1 for n_rows == 0.  The
+ * count depends only on shapes, never on the adapter mix (page "LoRA serving:
+ * multi-adapter dynamic loading", section 6: mix-dependent launch shapes are
+ * what breaks graph capture), so it is also the node count of a captured
+ * call.  Host only: nothing is enqueued; seg is not modified.  Errors:
+ * LORA_E_ARG (null pointer, n_rows < 0 or beyond either object's max_rows,
+ * mismatched objects).
+ */
+lora_status lora_build_apply_plan(const lora_stack *st, int64_t n_rows, const lora_segments *seg,
+                                  int32_t *n_launches);
 
 /* --------------------------------------------------------------- residency */
 

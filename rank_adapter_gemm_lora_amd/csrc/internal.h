@@ -112,6 +112,8 @@ constexpr int kSyncTimeouts = 2, kSyncFlags = 16, kSyncTileInts = 32;
 static_assert(kSyncTileInts > kMaxKSplit, "a tile's flags and counter");
 hipError_t launch_build_apply(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
                               hipStream_t stream);
+// workgroups of build_apply_kernel resident per CU with this much dynamic LDS
+int build_apply_wgs_per_cu(int dtype, int lds_bytes);
 // Merge of one slot into a dense weight (rows tiled per slice, 64 rows a tile).
 struct MergeArgs {
     const void *A;             // the slot's A: [n_slices][r_max][k]
@@ -184,6 +186,8 @@ struct lora_stack {
     int32_t *d_rank;
     float *d_scale;
     float *vpart;
+    mutable int n_cu;            // compute units of the device (0: not asked yet)
+    mutable int one_launch_wpc;  // build_apply_kernel workgroups resident per CU (-1: not asked yet)
     std::vector<int> h_rank;
     std::vector<float> h_alpha;
 };

@@ -361,6 +361,8 @@ lora_status lora_stack_create(lora_stack **out, lora_dtype dtype, int n_slots, i
     st->d_rank = nullptr;
     st->d_scale = nullptr;
     st->vpart = nullptr;
+    st->n_cu = 0;
+    st->one_launch_wpc = -1;
     if (hipGetDevice(&st->device) != hipSuccess) {
         delete st;
         return LORA_E_HIP;
@@ -641,16 +643,46 @@ bool fused_build_pays(const lora_stack *st, int64_t n_rows)
 // Grouping, shrink and expand in one launch: batches the fused grouping
 // serves, on 16-row tiles with one column chunk per expand workgroup, while the
 // whole grid (shrink plus expand workgroups, each grouping the batch in LDS)
-// stays within about one wave of workgroups on the chip.
-constexpr int kOneLaunchMaxBlocks = 1024;
-
+// fits on the chip at once, with a quarter to spare for the workgroups of tiles
+// the mix leaves empty (they exit after the grouping).  Measured on q-proj
+// 4096 -> 4096 at 256 rows: 1 to 4 adapters (grids of 408 and 480 at 512
+// resident) 12.7 -> 12.0 us; 16 adapters (768) 13.4 -> 15.2 us, as expand
+// workgroups queued behind waiting ones; rank 128 (one workgroup per CU by
+// LDS) 27.4 -> 28.9 us.
 bool one_launch_pays(const lora_stack *st, const ApplyArgs &a, int64_t n_rows)
 {
     if (!fused_build_pays(st, n_rows) || a.sgmv_rows != kBgmvTileRows || a.cpw != 1)
         return false;
+    if (st->one_launch_wpc < 0) {
+        int n_cu = 0;
+        if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, st->device) != hipSuccess)
+            n_cu = 0;
+        st->n_cu = n_cu;
+        st->one_launch_wpc = build_apply_wgs_per_cu(st->dtype == LORA_BF16 ? DT_BF16 : DT_F32, a.lds_bytes);
+    }
+    const int64_t capacity = (int64_t)st->one_launch_wpc * st->n_cu;
     const int64_t tiles = max_tiles_for(n_rows, st->n_slots);
     const int64_t chunks = (st->D + kExpandCols - 1) / kExpandCols;
-    return (a.ks + chunks) * tiles <= kOneLaunchMaxBlocks;
+    return capacity > 0 && (a.ks + chunks) * tiles <= capacity + capacity / 4;
+}
+
+// The launch arguments of a batch of n_rows on this stack and segments object,
+// the object itself untouched (its fields are plain values and pointers).
+ApplyArgs args_for_rows(const lora_stack *st, const lora_segments *seg, int64_t n_rows)
+{
+    lora_segments tmp = *seg;
+    mark_built(&tmp, st, n_rows);
+    return make_args(st, &tmp);
+}
+
+// Kernel launches lora_build_apply makes for n_rows.
+int build_apply_launches(const lora_stack *st, int64_t n_rows, const lora_segments *seg)
+{
+    if (n_rows <= 0)
+        return 1;   // the empty grouping
+    if (fused_build_pays(st, n_rows))
+        return one_launch_pays(st, args_for_rows(st, seg, n_rows), n_rows) ? 1 : 2;
+    return n_rows <= kFusedMaxRows ? 3 : 5;   // one-workgroup or chunked grouping
 }
 
 bool x_ok(const lora_stack *st, const void *x, int64_t ldx)
@@ -768,11 +800,8 @@ lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const v
     if (n_rows > 0 && (!x_ok(st, x, ldx) || !y_ok(st, y, ldy)))
         return LORA_E_ARG;
     if (n_rows > 0 && fused_build_pays(st, n_rows)) {
-        // one launch when the grid stays small (the decode step)
-        const int64_t prev_rows = seg->n_rows;
-        const int prev_built = seg->built, prev_slots = seg->n_slots;
-        mark_built(seg, st, n_rows);
-        ApplyArgs a = make_args(st, seg);
+        // one launch when the whole grid fits the chip (the decode step)
+        ApplyArgs a = args_for_rows(st, seg, n_rows);
         if (one_launch_pays(st, a, n_rows)) {
             a.x = x;
             a.ldx = ldx;
@@ -782,16 +811,24 @@ lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const v
                                         make_seg_args(st, ids, n_rows, seg),
                                         max_tiles_for(n_rows, st->n_slots),
                                         reinterpret_cast<hipStream_t>(stream)));
+            mark_built(seg, st, n_rows);
             return LORA_OK;
         }
-        seg->n_rows = prev_rows;
-        seg->built = prev_built;
-        seg->n_slots = prev_slots;
     }
     const lora_status s1 = lora_build_shrink(st, x, ldx, ids, n_rows, seg, stream);
     if (s1 != LORA_OK || n_rows == 0)
         return s1;
     return lora_add_expand(st, y, ldy, seg, stream);
+}
+
+lora_status lora_build_apply_plan(const lora_stack *st, int64_t n_rows, const lora_segments *seg,
+                                  int32_t *n_launches)
+{
+    if (!st || !seg || !n_launches || n_rows < 0 || n_rows > st->max_rows || n_rows > seg->max_rows ||
+        seg->n_slots_cap < st->n_slots || !current_device_is(st->device) || seg->device != st->device)
+        return LORA_E_ARG;
+    *n_launches = build_apply_launches(st, n_rows, seg);
+    return LORA_OK;
 }
 
 lora_status lora_segments_download(const lora_segments *seg, int32_t *perm, int32_t *seg_off,

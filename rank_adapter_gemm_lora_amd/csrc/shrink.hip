@@ -704,6 +704,16 @@ hipError_t launch_build_apply(int dtype, const ApplyArgs &a, const SegBuildArgs 
     return hipGetLastError();
 }
 
+int build_apply_wgs_per_cu(int dtype, int lds_bytes)
+{
+    int n = 0;
+    const hipError_t e =
+        dtype == DT_BF16
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, build_apply_kernel<DT_BF16>, 256, lds_bytes)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, build_apply_kernel<DT_F32>, 256, lds_bytes);
+    return e == hipSuccess ? n : 0;
+}
+
 hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream)
 {
     if (max_tiles <= 0)

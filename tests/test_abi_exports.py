@@ -61,6 +61,7 @@ def test_null_handles_rejected_on_host():
     assert lib.lora_slot_info(None, 0, None, None, None) == binding.LORA_E_ARG
     assert lib.lora_segments_set_dense_min(None, 4) == binding.LORA_E_ARG
     assert lib.lora_segments_set_expand_chunks(None, 2) == binding.LORA_E_ARG
+    assert lib.lora_build_apply_plan(None, 8, None, None) == binding.LORA_E_ARG
     assert lib.lora_build_segments(None, None, 0, None, None) == binding.LORA_E_ARG
     assert lib.lora_apply(None, None, 8, None, 8, None, None) == binding.LORA_E_ARG
     assert lib.lora_add_shrink(None, None, 8, None, None) == binding.LORA_E_ARG

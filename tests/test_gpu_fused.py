@@ -83,6 +83,19 @@ def test_build_apply_ragged(n, n_slots):
             check_against_oracle(p, y, what=f"n={n}/{dtype}/{path}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_build_apply_ks16_mixed_ranks(dtype):
+    """Long k at a small batch: 16 k-splits, so each tile's expand workgroups
+    wait on 16 shrink workgroups' flags in the one-launch kernel; mixed ranks
+    up to 64 and two slices."""
+    p = synth.make_random(23, n_rows=100, k=8192, slice_d=[512, 256], n_slots=4,
+                          ranks=[16, 8, 32, 64], r_max=64, p_none=0.1, dtype=dtype)
+    for path, dm in PATHS.items():
+        note(f"build_apply ks16 {dtype} {path}")
+        y = _fused_vs_split(p, dm, f"ks16/{dtype}/{path}")
+        check_against_oracle(p, y, what=f"ks16/{dtype}/{path}")
+
+
 def test_build_apply_empty_and_errors():
     p = synth.make_random(5, n_rows=32, k=64, slice_d=[64], n_slots=3, ranks=[8, 8, 8], r_max=8)
     run = GpuRun(p, max_rows=32)
@@ -159,6 +172,40 @@ def test_build_apply_back_to_back(name):
         lb.lora_get_device_status(run.seg, run.stream)
     finally:
         run.close()
+
+
+def test_build_apply_plan():
+    """Launch counts of lora_build_apply from the host query: one kernel for
+    the decode batch, two where the one-launch grid would not fit the chip (16
+    adapters at 256 rows; rank 128, whose LDS holds one workgroup per CU),
+    three or five for larger batches; the query changes nothing."""
+    cases = {
+        "decode_bgmv": (synth.make_workload("decode_bgmv"), 1),
+        "mlp_gate_up": (synth.make_workload("mlp_gate_up"), 2),
+        "many_adapter": (synth.make_workload("many_adapter"), 3),
+        "16_adapters": (synth.make_random(3, n_rows=256, k=4096, slice_d=[4096], n_slots=16,
+                                          ranks=[16] * 16, r_max=16), 2),
+        "rank128": (synth.make_random(3, n_rows=256, k=4096, slice_d=[4096], n_slots=1,
+                                      ranks=[128], r_max=128), 2),
+        "rows3000": (synth.make_random(3, n_rows=3000, k=512, slice_d=[512], n_slots=8,
+                                       ranks=[16] * 8, r_max=16), 5),
+    }
+    for name, (p, want) in cases.items():
+        note(f"build_apply plan {name}")
+        run = GpuRun(p)
+        try:
+            run.build()
+            before = run.segments()
+            assert lb.lora_build_apply_plan(run.stack, p.n_rows, run.seg) == want, name
+            assert lb.lora_build_apply_plan(run.stack, 0, run.seg) == 1
+            after = run.segments()
+            for key in before:
+                np.testing.assert_array_equal(after[key], before[key], err_msg=f"{name} {key}")
+            with pytest.raises(lb.LoraError) as e:
+                lb.lora_build_apply_plan(run.stack, run.max_rows + 1, run.seg)
+            assert e.value.status == lb.LORA_E_ARG
+        finally:
+            run.close()
 
 
 @pytest.mark.parametrize("n_rows", [256, 3000])
