@@ -82,8 +82,10 @@ def accounting(p) -> dict:
                            build_shrink=x_bytes + live_a + 8 * p.n_rows + 4 * (p.n_slots + 1),
                            build_apply=x_bytes + y_bytes + live_a + live_b + 8 * p.n_rows
                            + 4 * (p.n_slots + 1),
+                           apply=x_bytes + y_bytes + live_a + live_b,
                            total=x_bytes + y_bytes + live_a + live_b),
                 flops=dict(total=int(flops), shrink=int(shrink_flops), build_apply=int(flops),
+                           apply=int(flops),
                            build_shrink=int(shrink_flops), expand=int(flops - shrink_flops)))
 
 
@@ -181,6 +183,9 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
     def expand(bs):
         lb.lora_add_expand(bs.stack, bs.y.data_ptr(), p.ldy, bs.seg, sh)
 
+    def apply(bs):
+        lb.lora_apply(bs.stack, bs.y.data_ptr(), p.ldy, bs.x.data_ptr(), p.ldx, bs.seg, sh)
+
     def step(bs):
         lb.lora_build_apply(bs.stack, bs.y.data_ptr(), p.ldy, bs.x.data_ptr(), p.ldx,
                             bs.ids.data_ptr(), p.n_rows, bs.seg, sh)
@@ -209,12 +214,14 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
     # The split path's grouping and shrink are timed too, for comparison.
     # With a one-launch step, the two-launch path's kernels (build_shrink,
     # expand) are timed for comparison as well.
+    # lora_apply on the grouped sets ("apply": one launch or shrink + expand) is
+    # timed as well: the call a model makes per projection after one grouping.
     fns = dict(seg_build=build, shrink=shrink, build_shrink=build_shrink, expand=expand,
-               build_apply=step)
+               build_apply=step, apply=apply)
     n_launch = lb.lora_build_apply_plan(sets[0].stack, p.n_rows, sets[0].seg)
     step_k = STEP_KERNELS[n_launch]
-    extra = ("build_shrink", "expand", "seg_build", "shrink") if n_launch == 1 else \
-        ("seg_build", "shrink")
+    extra = ("build_shrink", "expand", "seg_build", "shrink", "apply") if n_launch == 1 else \
+        ("seg_build", "shrink", "apply")
     names = list(step_k) + [k for k in extra if k not in step_k]
     per = {}
     for name in names:
@@ -748,6 +755,7 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, copy_mb, wor
     names = {"seg_build": ("seg_build_kernel", "seg_build_small_kernel"),
              "shrink": ("shrink_kernel", "shrink_kernel_tall"),
              "build_shrink": ("build_shrink_kernel",), "build_apply": ("build_apply_kernel",),
+             "apply": ("apply_kernel",),
              "expand": ("expand_kernel", "expand_kernel_bf16_short", "expand_stream_kernel")}
 
     def bare(kname):

@@ -258,10 +258,13 @@ lora_status lora_add_expand(const lora_stack *st, void *y, int64_t ldy,
 
 /*
  * lora_add_shrink followed by lora_add_expand: y_i += (alpha/r) B (A x_i) for
- * every valid row of the batch grouped by seg.  The launch grid depends only on
- * (n_rows, k, slice widths), never on the adapter mix, so the call can be
- * captured in a HIP graph and replayed for any mix.  Errors: LORA_E_ARG,
- * LORA_E_HIP.
+ * every valid row of the batch grouped by seg, with the same bits.  The launch
+ * grid depends only on (n_rows, k, slice widths), never on the adapter mix, so
+ * the call can be captured in a HIP graph and replayed for any mix.  Where the
+ * shrink and expand workgroups of a batch of 16-row tiles fit the chip at once
+ * (as for the one-launch lora_build_apply), both run in one kernel, v handed
+ * over through the segments object's per-tile flags; calls on one segments
+ * object must then not overlap.  Errors: LORA_E_ARG, LORA_E_HIP.
  */
 lora_status lora_apply(const lora_stack *st, void *y, int64_t ldy, const void *x, int64_t ldx,
                        const lora_segments *seg, void *stream);

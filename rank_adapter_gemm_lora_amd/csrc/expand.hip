@@ -44,62 +44,10 @@ namespace lora {
 
 namespace {
 
-// Dynamic LDS: [rows: 64 int][slot table: rank, scale (when n_slots <= 256)]
-// [v staging at lds_v_off][B staging at lds_b_off]; the host sizes it.
-template <int DT, int MT, bool WO>
-__device__ __forceinline__ void expand_body(const ApplyArgs &a)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    int32_t *rows = reinterpret_cast<int32_t *>(lds);
-    int32_t *srank = reinterpret_cast<int32_t *>(lds + kExpandLdsTable);
-    float *sscale = reinterpret_cast<float *>(lds + kExpandLdsTable + 4 * kExpandTableSlots);
-    float *vs = reinterpret_cast<float *>(lds + a.lds_v_off);
-    unsigned char *bst = lds + a.lds_b_off;
-    const int t = blockIdx.y;
-    const ShrinkTile *T = a.tiles + t;
-    // header, row indices, counts and the slot table in one round trip
-    const int4 h = *reinterpret_cast<const int4 *>(T);
-    const int32_t my_row = threadIdx.x < kSgmvTileRows ? T->rows[threadIdx.x] : 0;
-    const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
-    const bool table = a.n_slots <= kExpandTableSlots;
-    if (table) {
-        for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x) {
-            srank[e] = a.rank[e];
-            sscale[e] = a.scale[e];
-        }
-    }
-    if (t >= n_tiles)
-        return;
-    const int64_t c0 = (int64_t)blockIdx.x * kCols;
-    if (c0 >= a.D)
-        return;
-    const int s = h.x, p0 = h.y, cnt = h.z;
-    if (threadIdx.x < kSgmvTileRows)
-        rows[threadIdx.x] = my_row;
-    __syncthreads();
-    const int r = table ? srank[s] : a.rank[s];
-    const float scale = table ? sscale[s] : a.scale[s];
-    if (r == 0)
-        return;   // slot emptied since the grouping was built: rows stay untouched
-    if constexpr (DT == DT_BF16) {
-        if (h.w == kTileSgmv && a.mfma_ok) {
-            sgmv_expand_tile<MT, WO>(a, rows, s, r, scale, p0, cnt, c0, vs,
-                                 reinterpret_cast<uint16_t *>(bst));
-            return;
-        }
-    }
-    // BGMV tile, or a dense tile of a stack without the MFMA path
-    for (int sub = 0; sub < cnt; sub += kBgmvTileRows) {
-        bgmv_expand_tile<DT>(a, rows + sub, s, r, scale, p0 + sub, min(kBgmvTileRows, cnt - sub),
-                             c0, vs, reinterpret_cast<uint32_t *>(bst));
-        __syncthreads();   // LDS is restaged by the next sub-tile
-    }
-}
-
 template <int DT, int MT, bool WO>
 __global__ __launch_bounds__(256) void expand_kernel(ApplyArgs a)
 {
-    expand_body<DT, MT, WO>(a);
+    expand_body<DT, MT, WO>(a, blockIdx.y, blockIdx.x);
 }
 
 // ------------------------------------------- SGMV, several chunks per tile
@@ -291,7 +239,7 @@ __global__ __launch_bounds__(256) void expand_stream_kernel(ApplyArgs a)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6, 8)))
 void expand_kernel_bf16_short(ApplyArgs a)
 {
-    expand_body<DT_BF16, 1, false>(a);
+    expand_body<DT_BF16, 1, false>(a, blockIdx.y, blockIdx.x);
 }
 
 }  // namespace

@@ -479,6 +479,62 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     merge16<DT>(a, yi, h0, h1, y0, y1, scale, acc);
 }
 
+// Dynamic LDS: [rows: 64 int][slot table: rank, scale (when n_slots <= 256)]
+// [v staging at lds_v_off][B staging at lds_b_off]; the host sizes it.
+// Tile t, 256-column chunk `chunk`.  Returns whether the workgroup computed
+// the tile (false: no such tile in this batch, a chunk past D, or a slot
+// emptied since the grouping).  COH, wait and v_read as the tile functions.
+template <int DT, int MT, bool WO, bool COH = false, class Wait = NoWait, class Done = NoWait>
+__device__ __forceinline__ bool expand_body(const ApplyArgs &a, int t, int chunk,
+                                            Wait wait = Wait(), Done v_read = Done())
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    int32_t *rows = reinterpret_cast<int32_t *>(lds);
+    int32_t *srank = reinterpret_cast<int32_t *>(lds + kExpandLdsTable);
+    float *sscale = reinterpret_cast<float *>(lds + kExpandLdsTable + 4 * kExpandTableSlots);
+    float *vs = reinterpret_cast<float *>(lds + a.lds_v_off);
+    unsigned char *bst = lds + a.lds_b_off;
+    const ShrinkTile *T = a.tiles + t;
+    // header, row indices, counts and the slot table in one round trip
+    const int4 h = *reinterpret_cast<const int4 *>(T);
+    const int32_t my_row = threadIdx.x < kSgmvTileRows ? T->rows[threadIdx.x] : 0;
+    const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
+    const bool table = a.n_slots <= kExpandTableSlots;
+    if (table) {
+        for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x) {
+            srank[e] = a.rank[e];
+            sscale[e] = a.scale[e];
+        }
+    }
+    if (t >= n_tiles)
+        return false;
+    const int64_t c0 = (int64_t)chunk * kCols;
+    if (c0 >= a.D)
+        return false;
+    const int s = h.x, p0 = h.y, cnt = h.z;
+    if (threadIdx.x < kSgmvTileRows)
+        rows[threadIdx.x] = my_row;
+    __syncthreads();
+    const int r = table ? srank[s] : a.rank[s];
+    const float scale = table ? sscale[s] : a.scale[s];
+    if (r == 0)
+        return false;   // slot emptied since the grouping was built: rows stay untouched
+    if constexpr (DT == DT_BF16) {
+        if (h.w == kTileSgmv && a.mfma_ok) {
+            sgmv_expand_tile<MT, WO, COH>(a, rows, s, r, scale, p0, cnt, c0, vs,
+                                          reinterpret_cast<uint16_t *>(bst), wait, v_read);
+            return true;
+        }
+    }
+    // BGMV tile, or a dense tile of a stack without the MFMA path
+    for (int sub = 0; sub < cnt; sub += kBgmvTileRows) {
+        bgmv_expand_tile<DT, COH>(a, rows + sub, s, r, scale, p0 + sub, min(kBgmvTileRows, cnt - sub),
+                                  c0, vs, reinterpret_cast<uint32_t *>(bst), wait, v_read);
+        __syncthreads();   // LDS is restaged by the next sub-tile
+    }
+    return true;
+}
+
 }  // namespace
 
 }  // namespace lora

@@ -114,6 +114,10 @@ hipError_t launch_build_apply(int dtype, const ApplyArgs &a, const SegBuildArgs 
                               hipStream_t stream);
 // workgroups of build_apply_kernel resident per CU with this much dynamic LDS
 int build_apply_wgs_per_cu(int dtype, int lds_bytes);
+// shrink and expand of a grouped batch in one launch (same conditions and
+// hand-over as launch_build_apply), and its residency per CU
+hipError_t launch_apply(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream);
+int apply_wgs_per_cu(int dtype, int lds_bytes);
 // Merge of one slot into a dense weight (rows tiled per slice, 64 rows a tile).
 struct MergeArgs {
     const void *A;             // the slot's A: [n_slices][r_max][k]
@@ -188,6 +192,7 @@ struct lora_stack {
     float *vpart;
     mutable int n_cu;            // compute units of the device (0: not asked yet)
     mutable int one_launch_wpc;  // build_apply_kernel workgroups resident per CU (-1: not asked yet)
+    mutable int apply_wpc;       // apply_kernel workgroups resident per CU (-1: not asked yet)
     std::vector<int> h_rank;
     std::vector<float> h_alpha;
 };

@@ -363,6 +363,7 @@ lora_status lora_stack_create(lora_stack **out, lora_dtype dtype, int n_slots, i
     st->vpart = nullptr;
     st->n_cu = 0;
     st->one_launch_wpc = -1;
+    st->apply_wpc = -1;
     if (hipGetDevice(&st->device) != hipSuccess) {
         delete st;
         return LORA_E_HIP;
@@ -675,6 +676,25 @@ ApplyArgs args_for_rows(const lora_stack *st, const lora_segments *seg, int64_t 
     return make_args(st, &tmp);
 }
 
+// lora_apply in one launch: batches of 16-row tiles with one column chunk per
+// expand workgroup whose grid fits the chip at once, a quarter to spare (the
+// same rule as the one-launch lora_build_apply, for apply_kernel's residency).
+bool apply_one_launch_pays(const lora_stack *st, const ApplyArgs &a, int64_t n_rows)
+{
+    if (n_rows <= 0 || a.sgmv_rows != kBgmvTileRows || a.cpw != 1)
+        return false;
+    if (st->apply_wpc < 0) {
+        if (st->n_cu == 0 &&
+            hipDeviceGetAttribute(&st->n_cu, hipDeviceAttributeMultiprocessorCount, st->device) != hipSuccess)
+            st->n_cu = 0;
+        st->apply_wpc = apply_wgs_per_cu(st->dtype == LORA_BF16 ? DT_BF16 : DT_F32, a.lds_bytes);
+    }
+    const int64_t capacity = (int64_t)st->apply_wpc * st->n_cu;
+    const int64_t tiles = max_tiles_for(n_rows, st->n_slots);
+    const int64_t chunks = (st->D + kExpandCols - 1) / kExpandCols;
+    return capacity > 0 && (a.ks + chunks) * tiles <= capacity + capacity / 4;
+}
+
 // Kernel launches lora_build_apply makes for n_rows.
 int build_apply_launches(const lora_stack *st, int64_t n_rows, const lora_segments *seg)
 {
@@ -758,6 +778,17 @@ lora_status lora_apply(const lora_stack *st, void *y, int64_t ldy, const void *x
     // validate both halves before enqueueing either
     if (!x_ok(st, x, ldx) || !y_ok(st, y, ldy))
         return LORA_E_ARG;
+    ApplyArgs a = make_args(st, seg);
+    if (apply_one_launch_pays(st, a, seg->n_rows)) {
+        a.x = x;
+        a.ldx = ldx;
+        a.y = y;
+        a.ldy = ldy;
+        LORA_TRY(launch_apply(st->dtype == LORA_BF16 ? DT_BF16 : DT_F32, a,
+                              max_tiles_for(seg->n_rows, st->n_slots),
+                              reinterpret_cast<hipStream_t>(stream)));
+        return LORA_OK;
+    }
     const lora_status s1 = lora_add_shrink(st, x, ldx, seg, stream);
     if (s1 != LORA_OK)
         return s1;

@@ -432,12 +432,13 @@ __device__ __forceinline__ void shrink_tile(const ApplyArgs &a, const int32_t *r
         bgmv_shrink_tile<DT, COH>(a, rows + sub, s, r, p0 + sub, min(kBgmvTileRows, cnt - sub), ks);
 }
 
-template <int DT, int MT>
-__device__ __forceinline__ void shrink_body(const ApplyArgs &a)
+// Split ks of tile t.  Returns whether the workgroup computed v (false: no
+// such tile in this batch, or a slot emptied since the grouping).
+template <int DT, int MT, bool COH = false>
+__device__ __forceinline__ bool shrink_body(const ApplyArgs &a, int ks, int t)
 {
     __shared__ int32_t rows[kSgmvTileRows];
     __shared__ int32_t rank[LORA_MAX_SLOTS];
-    const int ks = blockIdx.x, t = blockIdx.y;
     const ShrinkTile *T = a.tiles + t;
     // header, row indices, counts and the slot ranks in one round trip
     const int4 h = *reinterpret_cast<const int4 *>(T);
@@ -446,20 +447,21 @@ __device__ __forceinline__ void shrink_body(const ApplyArgs &a)
     for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x)
         rank[e] = a.rank[e];
     if (t >= n_tiles)
-        return;
+        return false;
     if (threadIdx.x < kSgmvTileRows)
         rows[threadIdx.x] = my_row;
     __syncthreads();
     const int r = rank[h.x];
     if (r == 0)
-        return;   // slot emptied since the grouping was built: nothing to compute
-    shrink_tile<DT, MT>(a, rows, h.x, r, h.y, h.z, h.w, ks);
+        return false;   // slot emptied since the grouping was built: nothing to compute
+    shrink_tile<DT, MT, COH>(a, rows, h.x, r, h.y, h.z, h.w, ks);
+    return true;
 }
 
 template <int DT>
 __global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
 {
-    shrink_body<DT, 1>(a);
+    shrink_body<DT, 1>(a, blockIdx.x, blockIdx.y);
 }
 
 // 64-row tiles, held to three wavefronts per SIMD: the tile's 48 KB ring lets
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(ApplyArgs a)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void shrink_kernel_tall(ApplyArgs a)
 {
-    shrink_body<DT_BF16, 4>(a);
+    shrink_body<DT_BF16, 4>(a, blockIdx.x, blockIdx.y);
 }
 
 // Grouping and shrink in one launch, for small batches.  Every workgroup
@@ -531,6 +533,70 @@ __global__ __launch_bounds__(256) void build_shrink_kernel(ApplyArgs a, SegBuild
     }
 }
 
+constexpr int kWaitSpins = 1 << 18;   // polls before a wait gives up
+
+// The handover of one tile's v inside a launch (see build_apply_kernel):
+// shrink workgroups publish(), expand workgroups wait() before reading v,
+// v_read() once every thread's v is in LDS, and finish() at the end.
+struct TileSync {
+    int32_t *flag;   // the tile's split flags, then its expand workgroups' counter
+    int32_t *timeouts;
+    int n_split, n_chunks;
+    int seen;        // thread 0 of an expand workgroup: the counter before its add
+
+    __device__ TileSync(int32_t *sync, int t, int n_split_, int n_chunks_)
+        : flag(sync + kSyncFlags + t * kSyncTileInts), timeouts(sync + kSyncTimeouts),
+          n_split(n_split_), n_chunks(n_chunks_), seen(-1)
+    {
+    }
+    // shrink workgroup of split ks: its device-coherent v stores are issued
+    __device__ void publish(int ks) const
+    {
+        LORA_WAIT_VM(0);   // this wavefront's v stores are acknowledged
+        __syncthreads();   // ... and every other wavefront's
+        if (threadIdx.x == 0)
+            __hip_atomic_store(flag + ks, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // each wavefront polls the split flags itself (no barrier, so loads
+    // already issued stay in flight)
+    __device__ void wait() const
+    {
+        const int lane = threadIdx.x & 63;
+        for (int spins = 0;; ++spins) {
+            const bool ok = lane >= n_split ||
+                            __hip_atomic_load(flag + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1;
+            if (__all(ok))
+                break;
+            if (spins >= kWaitSpins) {
+                if (lane == 0)
+                    __hip_atomic_fetch_add(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        // v is read after this point, never hoisted above the poll
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    // every thread's v is in LDS: count this workgroup done with the flags (the
+    // atomic's round trip overlaps the products; its result is used in finish)
+    __device__ void v_read()
+    {
+        lds_barrier();
+        if (threadIdx.x == 0 && seen < 0)
+            seen = __hip_atomic_fetch_add(flag + kMaxKSplit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the tile's last expand workgroup to count clears the flags and counter
+    // (every other one has finished polling and reading v before it counted)
+    __device__ void finish() const
+    {
+        if (threadIdx.x == 0 && seen == n_chunks - 1) {
+            for (int k = 0; k < n_split; ++k)
+                __hip_atomic_store(flag + k, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(flag + kMaxKSplit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+};
+
 // Grouping, shrink and expand in one launch (decode-sized batches of 16-row
 // tiles).  The grid is one list of workgroups: first ks x tile-bound shrink
 // workgroups (split ks % a.ks of tile b / a.ks, so one split's workgroups share
@@ -554,7 +620,6 @@ __global__ __launch_bounds__(256) void build_shrink_kernel(ApplyArgs a, SegBuild
 // are dispatched before it and wait on nothing, so the waits always end; a
 // wait that exceeds kWaitSpins polls (well under a second) gives up and counts
 // a timeout that lora_get_device_status reports.
-constexpr int kWaitSpins = 1 << 18;
 
 template <int DT>
 __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildArgs sb, int n_prod,
@@ -565,7 +630,6 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
     __shared__ int32_t rows[kSgmvTileRows];
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // expand staging
     const int tid = threadIdx.x, b = blockIdx.x;
-    int32_t *sync = a.sync;
     const bool prod = b < n_prod;
     const int t = prod ? b / a.ks : (b - n_prod) / n_chunks;
     const int ks = prod ? b - t * a.ks : 0;
@@ -588,13 +652,10 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
         }
         __syncthreads();
         const int r = g.rank[s];
+        TileSync sy(a.sync, t, a.ks, n_chunks);
         if (prod) {
             shrink_tile<DT, 1, true>(a, rows, s, r, p0, cnt, p.path, ks);
-            LORA_WAIT_VM(0);   // this wavefront's v stores are acknowledged
-            __syncthreads();   // ... and every other wavefront's
-            if (tid == 0)
-                __hip_atomic_store(sync + kSyncFlags + t * kSyncTileInts + ks, 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            sy.publish(ks);
             if (ks == 0) {
                 // the segments object receives what the grouping kernel writes
 #pragma unroll
@@ -612,39 +673,8 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
         } else {
             const int64_t c0 = (int64_t)(b - n_prod - t * n_chunks) * kCols;
             const float scale = a.scale[s];
-            int32_t *flag = sync + kSyncFlags + t * kSyncTileInts;
-            const int n_split = a.ks;
-            // each wavefront polls the tile's split flags itself (no barrier,
-            // so the y and B loads already issued stay in flight)
-            auto wait = [=]() {
-                const int lane = threadIdx.x & 63;
-                for (int spins = 0;; ++spins) {
-                    const bool ok = lane >= n_split ||
-                                    __hip_atomic_load(flag + lane, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT) == 1;
-                    if (__all(ok))
-                        break;
-                    if (spins >= kWaitSpins) {
-                        if (lane == 0)
-                            __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                }
-                // v is read after this point, never hoisted above the poll
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            };
-            // once every thread's v is in LDS this workgroup is done with the
-            // tile's flags: it counts itself on the tile's counter (the atomic's
-            // round trip overlaps the products; its result is used at the end)
-            int seen = -1;
-            auto v_read = [&]() {
-                lds_barrier();
-                if (tid == 0 && seen < 0)
-                    seen = __hip_atomic_fetch_add(flag + kMaxKSplit, 1, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-            };
+            auto wait = [&]() { sy.wait(); };
+            auto v_read = [&]() { sy.v_read(); };
             float *vs = reinterpret_cast<float *>(lds + a.lds_v_off);
             unsigned char *bst = lds + a.lds_b_off;
             bool done = false;
@@ -663,14 +693,7 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
                     __syncthreads();   // LDS is restaged by the next sub-tile
                 }
             }
-            // the tile's last expand workgroup to count itself clears the
-            // tile's flags and counter for the next launch (every other one has
-            // finished polling and reading v before it counted)
-            if (tid == 0 && seen == n_chunks - 1) {
-                for (int k = 0; k < n_split; ++k)
-                    __hip_atomic_store(flag + k, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(flag + kMaxKSplit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            sy.finish();
         }
     }
     if (prod && ks == 0 && t == 0) {
@@ -684,7 +707,56 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
     }
 }
 
+// Shrink and expand of a grouped batch in one launch (lora_apply of a
+// decode-sized batch): the same grid and hand-over as build_apply_kernel, with
+// the tile records read from the segments object instead of a grouping.
+template <int DT>
+__global__ __launch_bounds__(256) void apply_kernel(ApplyArgs a, int n_prod, int n_chunks)
+{
+    const int b = blockIdx.x;
+    if (b < n_prod) {
+        const int t = b / a.ks, ks = b - t * a.ks;
+        if (shrink_body<DT, 1, true>(a, ks, t)) {
+            const TileSync sy(a.sync, t, a.ks, n_chunks);
+            sy.publish(ks);
+        }
+    } else {
+        const int t = (b - n_prod) / n_chunks, chunk = b - n_prod - t * n_chunks;
+        TileSync sy(a.sync, t, a.ks, n_chunks);
+        auto wait = [&]() { sy.wait(); };
+        auto v_read = [&]() { sy.v_read(); };
+        if (expand_body<DT, 1, false, true>(a, t, chunk, wait, v_read))
+            sy.finish();
+    }
+}
+
 }  // namespace
+
+hipError_t launch_apply(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream)
+{
+    if (max_tiles <= 0 || a.sgmv_rows != kBgmvTileRows || a.cpw != 1 || a.ks > kMaxKSplit || !a.sync)
+        return hipErrorInvalidValue;
+    const int n_chunks = (int)((a.D + kCols - 1) / kCols);
+    const int n_prod = a.ks * max_tiles;
+    const dim3 grid((unsigned)(n_prod + n_chunks * max_tiles));
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(apply_kernel<DT_BF16>, grid, dim3(256), a.lds_bytes, stream, a, n_prod,
+                           n_chunks);
+    else
+        hipLaunchKernelGGL(apply_kernel<DT_F32>, grid, dim3(256), a.lds_bytes, stream, a, n_prod,
+                           n_chunks);
+    return hipGetLastError();
+}
+
+int apply_wgs_per_cu(int dtype, int lds_bytes)
+{
+    int n = 0;
+    const hipError_t e =
+        dtype == DT_BF16
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, apply_kernel<DT_BF16>, 256, lds_bytes)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, apply_kernel<DT_F32>, 256, lds_bytes);
+    return e == hipSuccess ? n : 0;
+}
 
 hipError_t launch_build_apply(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
                               hipStream_t stream)
