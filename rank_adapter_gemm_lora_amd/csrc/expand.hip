@@ -35,6 +35,12 @@
 //     in passes (bf16: 8 rank pairs, fp32: 8 ranks); each lane forms the bf16
 //     hi/lo pairs of its row's v and accumulates packed bf16 dot products
 //     (v_dot2c_f32_bf16), or fp32 FMAs.
+//
+// The tile code and expand_body live in expand_tiles.h (shared with the
+// one-launch kernels); this file holds the expand kernels: expand_kernel (one
+// 256-column chunk per workgroup), expand_kernel_bf16_short (its 16-row bf16
+// instance, built for six waves per SIMD) and expand_stream_kernel (several
+// chunks per workgroup, the next chunk's loads in flight).
 #include "device_common.h"
 #include "internal.h"
 #include "mfma.h"

@@ -22,7 +22,13 @@
 //
 // Each k-split writes its fp32 partial of v, indexed by split and grouping
 // position; the expand sums the splits in split order, so results are
-// bit-reproducible and no workgroup waits on another.
+// bit-reproducible.  In the shrink kernels no workgroup waits on another.
+//
+// The file also holds the launches that put the shrink next to other work:
+// build_shrink_kernel (grouping in LDS + shrink), and the two one-launch
+// kernels, build_apply_kernel (grouping + shrink + expand) and apply_kernel
+// (shrink + expand of a grouped batch), whose expand workgroups wait for the
+// shrink workgroups of their tile through per-tile flags (TileSync).
 #include "device_common.h"
 #include "expand_tiles.h"
 #include "group.h"
