@@ -836,7 +836,7 @@ def main(argv=None):
                  args.out)
         return 0
     names = ["tiny_ref", "decode_bgmv", "prefill_sgmv", "mlp_gate_up", "mlp_down",
-             "many_adapter"] if args.all else [args.workload]
+             "many_adapter", "many_adapter_tp4", "mlp_down_tp4"] if args.all else [args.workload]
     lines = {}
     for name in names:
         line = bench_workload(name, args.steps, args.warmup, rotate=not args.warm,

@@ -28,6 +28,11 @@ import numpy as np
 
 WORKLOADS = ("tiny_ref", "decode_bgmv", "prefill_sgmv", "mlp_gate_up", "mlp_down",
              "many_adapter")
+# One GPU's share of a projection under 4-way tensor parallelism (the whole
+# workload's inputs cut, nothing redrawn): the column-parallel up-projection
+# keeps the first D/4 output columns; the row-parallel down-projection keeps
+# the first k/4 input columns (its v would then be summed across GPUs).
+SHARD_WORKLOADS = ("many_adapter_tp4", "mlp_down_tp4")
 
 
 def f32_to_bf16_bits(a) -> np.ndarray:
@@ -226,8 +231,33 @@ def _many_adapter(seed):
                    note="1024 rows, 8192->28672, 100 slots r=16, Zipf(1.1)")
 
 
+def tp_share(p: Problem, degree: int, mode: str) -> Problem:
+    """One GPU's share of ``p`` under ``degree``-way tensor parallelism:
+    mode "column" keeps the first d_q / degree columns of every slice (B rows,
+    y columns), mode "row" the first k / degree input columns (x, A)."""
+    if mode == "column":
+        keep = [d // degree for d in p.slice_d]
+        cols = np.concatenate([off + np.arange(kq) for off, kq in
+                               zip(np.cumsum([0] + list(p.slice_d[:-1])), keep)])
+        B = [None if b is None else np.ascontiguousarray(b[cols]) for b in p.B]
+        y = np.ascontiguousarray(p.y[:, cols])
+        return replace(p, name=f"{p.name}_tp{degree}", slice_d=keep, B=B, y=y,
+                       note=p.note + f"; column share 1/{degree}: D = {sum(keep)}")
+    if mode == "row":
+        k = p.k // degree
+        A = [None if a is None else np.ascontiguousarray(a[:, :, :k]) for a in p.A]
+        x = np.ascontiguousarray(p.x[:, :k])
+        return replace(p, name=f"{p.name}_tp{degree}", k=k, A=A, x=x,
+                       note=p.note + f"; row share 1/{degree}: k = {k}")
+    raise ValueError(mode)
+
+
 def make_workload(name: str, seed: int = 0) -> Problem:
-    """One of the named workloads (see WORKLOADS)."""
+    """One of the named workloads (see WORKLOADS and SHARD_WORKLOADS)."""
+    if name == "many_adapter_tp4":
+        return tp_share(_many_adapter(seed), 4, "column")
+    if name == "mlp_down_tp4":
+        return tp_share(_mlp_pair(seed)[1], 4, "row")
     if name == "tiny_ref":
         return _tiny_ref(seed)
     if name == "decode_bgmv":

@@ -18,7 +18,7 @@ from gpu_helpers import GpuRun, check_against_oracle, note, sample_rows
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ("tiny_ref", "decode_bgmv", "mlp_gate_up", "mlp_down", "many_adapter")
+SMALL = ("tiny_ref", "decode_bgmv", "mlp_gate_up", "mlp_down", "many_adapter") + synth.SHARD_WORKLOADS
 ALL = SMALL + ("prefill_sgmv",)
 PATHS = {"auto": None, "bgmv": 1 << 30, "sgmv": 1}
 SAMPLE = {"prefill_sgmv": 256}

@@ -89,3 +89,24 @@ def test_strides_keep_data():
     assert q.ldx == p.k + 8 and q.ldy == p.D + 16
     np.testing.assert_array_equal(q.x[:, :p.k], p.x)
     np.testing.assert_array_equal(q.y[:, :p.D], p.y)
+
+
+def test_tensor_parallel_shares_cut_the_full_workload():
+    """The one-GPU shares are cuts of the full workloads, nothing redrawn:
+    columns [0, D/4) of the up-projection, input columns [0, k/4) of the
+    down-projection."""
+    full, share = synth.make_workload("many_adapter"), synth.make_workload("many_adapter_tp4")
+    assert share.slice_d == [7168] and share.k == full.k
+    np.testing.assert_array_equal(share.y, full.y[:, :7168])
+    np.testing.assert_array_equal(share.x, full.x)
+    for s in (0, 57, 99):
+        np.testing.assert_array_equal(share.B[s], full.B[s][:7168])
+        np.testing.assert_array_equal(share.A[s], full.A[s])
+    full, share = synth.make_workload("mlp_down"), synth.make_workload("mlp_down_tp4")
+    assert share.k == 3584 and share.slice_d == full.slice_d
+    np.testing.assert_array_equal(share.x, full.x[:, :3584])
+    np.testing.assert_array_equal(share.y, full.y)
+    for s in (0, 3, 15):
+        np.testing.assert_array_equal(share.A[s], full.A[s][:, :, :3584])
+        np.testing.assert_array_equal(share.B[s], full.B[s])
+    np.testing.assert_array_equal(share.ids, full.ids)
