@@ -51,8 +51,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATE_BYTES = 512 << 20       # 2x the 256 MB MALL
 DEFAULT_WORKLOAD = "decode_bgmv"
-KERNEL_SOURCES = ("seg_build.hip", "shrink.hip", "expand.hip", "group.h", "mfma.h",
-                  "device_common.h", "internal.h")
+KERNEL_SOURCES = ("seg_build.hip", "shrink.hip", "expand.hip", "expand_tiles.h", "group.h",
+                  "mfma.h", "device_common.h", "internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_bgmv.json")
 
 
@@ -120,12 +120,14 @@ def committed_traffic(workload: str):
 class BufferSet:
     """One independent copy of the stack, ids, x and y of a workload."""
 
-    def __init__(self, p, lb, torch, dev, stream, dA, dB, dense_min):
+    def __init__(self, p, lb, torch, dev, stream, dA, dB, dense_min, expand_chunks=None):
         dt = lb.LORA_BF16 if p.dtype == "bf16" else lb.LORA_F32
         self.stack = lb.lora_stack_create(dt, p.n_slots, p.r_max, p.k, p.slice_d, p.n_rows)
         self.seg = lb.lora_segments_create(p.n_rows, p.n_slots)
         if dense_min is not None:
             lb.lora_segments_set_dense_min(self.seg, dense_min)
+        if expand_chunks is not None:
+            lb.lora_segments_set_expand_chunks(self.seg, expand_chunks)
         for s in range(p.n_slots):
             if p.ranks[s] > 0:
                 lb.lora_load_slot(self.stack, s, int(p.ranks[s]), float(p.alphas[s]),
@@ -148,7 +150,7 @@ def set_bytes(p) -> int:
     return pool + p.x.nbytes + p.y.nbytes + p.ids.nbytes
 
 
-def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
+def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None, expand_chunks=None,
             graph: bool = True) -> dict:
     import torch
     from rank_adapter_gemm_lora_amd import binding as lb
@@ -166,7 +168,8 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None,
     n_sets = max(2, math.ceil(ROTATE_BYTES / set_bytes(p))) if rotate else 1
     n_sets = min(n_sets, 4096)
     with torch.cuda.stream(stream):
-        sets = [BufferSet(p, lb, torch, dev, sh, dA, dB, dense_min) for _ in range(n_sets)]
+        sets = [BufferSet(p, lb, torch, dev, sh, dA, dB, dense_min, expand_chunks)
+                for _ in range(n_sets)]
     torch.cuda.synchronize()
     del dA, dB
 
@@ -323,15 +326,17 @@ def run_cpu_baseline(p, acct, budget_s: float = 10.0, budget_1t_s: float = 3.0) 
 
 # ----------------------------------------------------------------- modes
 
-def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None) -> dict:
+def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None,
+                   expand_chunks=None) -> dict:
     from rank_adapter_gemm_lora_amd import synth
     p = synth.make_workload(name)
     acct = accounting(p)
     log(f"[bench] {name}: {p.note}; valid rows {acct['n_valid']}, "
         f"algorithmic bytes {acct['bytes']['total'] / 1e6:.2f} MB/step")
-    g = run_gpu(p, steps, warmup, rotate=rotate, dense_min=dense_min)
+    g = run_gpu(p, steps, warmup, rotate=rotate, dense_min=dense_min, expand_chunks=expand_chunks)
     # the same step on one buffer set, cache-resident (MALL / L2 served, not HBM)
-    warm = run_gpu(p, steps, warmup, rotate=False, dense_min=dense_min, graph=False) if rotate else g
+    warm = run_gpu(p, steps, warmup, rotate=False, dense_min=dense_min, expand_chunks=expand_chunks,
+                   graph=False) if rotate else g
     ms = g["gpu_ms"] / steps
     ku = g["kernel_us"]
     dom = max(g["step_kernels"], key=lambda k: ku[k])
@@ -789,6 +794,8 @@ def main(argv=None):
     ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-served)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--dense-min", type=int, default=None, help="SGMV threshold (rows per group)")
+    ap.add_argument("--expand-chunks", type=int, default=None,
+                    help="256-column chunks per expand workgroup (lora_segments_set_expand_chunks)")
     ap.add_argument("--merge", action="store_true",
                     help="bench lora_merge_slot on the named projections instead")
     ap.add_argument("--sweep", action="store_true",
@@ -841,7 +848,7 @@ def main(argv=None):
     for name in names:
         line = bench_workload(name, args.steps, args.warmup, rotate=not args.warm,
                               cpu=not args.no_cpu and (not args.all or name == DEFAULT_WORKLOAD),
-                              dense_min=args.dense_min)
+                              dense_min=args.dense_min, expand_chunks=args.expand_chunks)
         lines[name] = line
         emit(line, args.out)
     if "mlp_gate_up" in lines and "mlp_down" in lines:

@@ -198,11 +198,12 @@ lora_status lora_segments_set_dense_min(lora_segments *seg, int m_min);
 /*
  * Launch shape of the expand of later lora_add_expand / lora_apply /
  * lora_build_apply calls on this segments object: 256-column chunks of one
- * row tile per workgroup.  0 (the default) chooses from the shapes alone: 2
- * for stacks of rank <= 16 with 16-row dense tiles and at least 8192 (tile,
- * chunk) pairs in the launch bound (many small groups over a wide output:
- * each workgroup then keeps the next chunk's y and B in flight while it
- * computes the current one), else 1.  1..16 forces that many where the
+ * row tile per workgroup.  0 (the default) chooses from the shapes alone: for
+ * stacks of rank <= 16 with 16-row dense tiles whose groups average at most
+ * 16 rows (n_rows <= 16 n_slots) and at least 2048 (tile, chunk) pairs in the
+ * launch bound, 4 when the output has at most 32 chunks, else 2 (many small
+ * groups: each workgroup then keeps the next chunk's y and B in flight while
+ * it computes the current one); otherwise 1.  1..16 forces that many where the
  * several-chunk expand applies (bf16 stacks with dense tiles, 16-row tiles,
  * r_max <= 64, v of every slice and one B block within the LDS budget) and is
  * ignored elsewhere.  A tuning knob: results are bit-identical for every

@@ -180,17 +180,24 @@ ExpandLds expand_stream_lds(const lora_stack *st)
     return l;
 }
 
-// Chunks per expand workgroup, from the shapes alone.  Two pay off where many
-// small groups meet a wide output at low rank: measured on 1024 rows x 100
-// rank-16 adapters into 28672 columns, expand 61 -> 50.5 us (4 chunks 50.8,
-// 8 chunks 53.5).  Elsewhere one: the one-chunk kernel keeps more workgroups
-// per CU (decode 5.7 -> 6.6 us with two, rank-64 gate/up 28.3 -> 30.6 us).
+// Chunks per expand workgroup, from the shapes alone.  Several pay off where
+// the groups average less than one 16-row tile (so most tiles carry a few rows
+// and each workgroup's fixed cost -- its record, v, the first round trip --
+// is spread over more columns) at low rank.  Measured on 1024 rows x 100
+// rank-16 adapters: into 28672 columns (112 chunks) expand 60.6 / 50.4 / 50.8
+// us with 1 / 2 / 4 chunks; into 7168 columns (28 chunks) 17.7 / 16.2 / 15.0
+// us.  Elsewhere one: the one-chunk kernel keeps more workgroups per CU
+// (decode, 32 rows per slot: 5.7 / 6.7 / 9.4 us; rank-64 MLP gate/up: 28.1 /
+// 30.4 / 34.8 us).
 int choose_cpw(const lora_stack *st, int64_t n_rows, int forced)
 {
     if (forced > 0)
         return forced;
-    const int64_t pairs = ((st->D + kExpandCols - 1) / kExpandCols) * max_tiles_for(n_rows, st->n_slots);
-    return st->rp_max <= 16 && pairs >= 8192 ? 2 : 1;
+    const int64_t chunks = (st->D + kExpandCols - 1) / kExpandCols;
+    const int64_t pairs = chunks * max_tiles_for(n_rows, st->n_slots);
+    if (st->rp_max > 16 || n_rows > (int64_t)kBgmvTileRows * st->n_slots || pairs < 2048)
+        return 1;
+    return chunks <= 32 ? 4 : 2;
 }
 
 bool stack_has_mfma_path(const lora_stack *st)
