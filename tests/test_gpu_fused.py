@@ -264,13 +264,21 @@ def test_build_apply_plan():
         "rows3000": (synth.make_random(3, n_rows=3000, k=512, slice_d=[512], n_slots=8,
                                        ranks=[16] * 8, r_max=16), 5),
     }
+    # the one-launch rule compares grids with what the chip holds at once: the
+    # counts below are those of a whole MI355X (256 CUs); a partitioned device
+    # only gets the checks that do not depend on the CU count
+    whole_chip = torch.cuda.get_device_properties(0).multi_processor_count == 256
     for name, (p, want) in cases.items():
         note(f"build_apply plan {name}")
         run = GpuRun(p)
         try:
             run.build()
             before = run.segments()
-            assert lb.lora_build_apply_plan(run.stack, p.n_rows, run.seg) == want, name
+            got = lb.lora_build_apply_plan(run.stack, p.n_rows, run.seg)
+            if whole_chip or want > 2:
+                assert got == want, name
+            else:
+                assert got in (1, 2), name
             assert lb.lora_build_apply_plan(run.stack, 0, run.seg) == 1
             after = run.segments()
             for key in before:
