@@ -212,6 +212,20 @@ lora_status lora_segments_set_dense_min(lora_segments *seg, int m_min);
 lora_status lora_segments_set_expand_chunks(lora_segments *seg, int chunks);
 
 /*
+ * Bound on the polls a one-launch call (lora_build_apply / lora_apply run as
+ * one kernel) makes while an expand workgroup waits for the shrink workgroups
+ * of its tile.  The wait always ends by construction (an expand workgroup
+ * waits only on earlier-dispatched shrink workgroups that wait on nothing), so
+ * the bound is a guard; the default (2^18 polls) is well under a second.  A
+ * workgroup that gives up leaves its rows of y untouched and counts a timeout;
+ * later one-launch calls on the object then leave y untouched until
+ * lora_get_device_status reports LORA_E_HIP, which also resets the object's
+ * hand-over state.  polls = 0 checks once (a host-side way to exercise the
+ * guard without any kernel misbehaving).  Errors: LORA_E_ARG (polls < 0).
+ */
+lora_status lora_segments_set_wait_limit(lora_segments *seg, int polls);
+
+/*
  * Group the rows of one batch by adapter slot, on the device (page "LoRA
  * hot-loading and adapter routing", batched multi-adapter execution section:
  * one group of row indices per adapter id; page "Multi-LoRA Serving",
@@ -440,8 +454,10 @@ lora_status lora_segments_download(const lora_segments *seg, int32_t *perm, int3
 
 /* Number of bad ids seen by the last lora_build_segments (synchronises the
  * stream).  Returns LORA_E_BAD_IDS when it is nonzero, LORA_OK otherwise;
- * LORA_E_HIP if a one-launch lora_build_apply on this object ever gave up
- * waiting for its shrink (its y is then not valid). */
+ * LORA_E_HIP if a one-launch call on this object gave up waiting for its
+ * shrink since the last such report (rows of the affected tiles were left
+ * untouched, and calls after it left y untouched); the report resets the
+ * object's hand-over state, so the next call computes normally. */
 lora_status lora_get_device_status(const lora_segments *seg, int64_t *n_bad, void *stream);
 
 /* Number of row tiles the last lora_build_segments gave each path (host

@@ -29,6 +29,7 @@ STATUS_NAMES = {0: "LORA_OK", 1: "LORA_E_ARG", 2: "LORA_E_RANK", 3: "LORA_E_SLOT
 EXPORTS = ("lora_stack_create", "lora_stack_destroy", "lora_load_slot", "lora_evict_slot",
            "lora_slot_info", "lora_merge_slot", "lora_segments_create", "lora_segments_destroy",
            "lora_segments_set_dense_min", "lora_segments_set_expand_chunks",
+           "lora_segments_set_wait_limit",
            "lora_build_segments", "lora_add_shrink",
            "lora_add_expand", "lora_apply", "lora_build_shrink", "lora_build_apply",
            "lora_build_apply_plan",
@@ -86,6 +87,7 @@ def load(path: str | None = None):
             "lora_segments_destroy": [P],
             "lora_segments_set_dense_min": [P, I],
             "lora_segments_set_expand_chunks": [P, I],
+            "lora_segments_set_wait_limit": [P, I],
             "lora_build_segments": [P, P, I64, P, P],
             "lora_add_shrink": [P, P, I64, P, P],
             "lora_add_expand": [P, P, I64, P, P],
@@ -179,6 +181,10 @@ def lora_segments_set_dense_min(seg, m_min: int):
 def lora_segments_set_expand_chunks(seg, chunks: int):
     _check(load().lora_segments_set_expand_chunks(seg, int(chunks)),
            "lora_segments_set_expand_chunks")
+
+
+def lora_segments_set_wait_limit(seg, polls: int):
+    _check(load().lora_segments_set_wait_limit(seg, int(polls)), "lora_segments_set_wait_limit")
 
 
 def lora_build_segments(stack, ids: int, n_rows: int, seg, stream=None):

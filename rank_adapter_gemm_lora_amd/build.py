@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["lora_api.cpp", "seg_build.hip", "shrink.hip", "expand.hip", "pool.hip", "merge.hip",
-           "residency.cpp"]
+SOURCES = ["lora_api.cpp", "seg_build.hip", "shrink.hip", "expand.hip", "decode.hip", "pool.hip",
+           "merge.hip", "residency.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC,

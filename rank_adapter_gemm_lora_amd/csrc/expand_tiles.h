@@ -11,7 +11,8 @@
 // the one-launch kernel, the wait for the shrink workgroups that produce the
 // tile's v), and `v_read`, called by every thread once its v loads have
 // landed in LDS (there, the tile's expand workgroups count themselves done
-// with the tile's flags).  COH reads v with device-coherent loads (they bypass the XCD's
+// with the tile's flags), which returns whether the tile's y is to be written
+// (false when the wait gave up).  COH reads v with device-coherent loads (they bypass the XCD's
 // non-coherent L2), for v written by a workgroup of the same launch.
 #pragma once
 
@@ -25,6 +26,11 @@ namespace {
 
 struct NoWait {
     __device__ __forceinline__ void operator()() const {}
+};
+
+// v_read hook of the expand kernels: every tile's y is written.
+struct KeepAll {
+    __device__ __forceinline__ bool operator()() const { return true; }
 };
 
 constexpr int kCols = kExpandCols;
@@ -163,7 +169,7 @@ __device__ __forceinline__ void merge16(const ApplyArgs &a, int64_t yi, bool h0,
 // for batches up to 4096 rows, 4 above), so the y registers match the shape.
 // WO: rank windows in the outer loop (B staged once per window, all MT row
 // tiles accumulated at once), for stacks whose B chunk needs several windows.
-template <int MT, bool WO, bool COH = false, class Wait = NoWait, class Done = NoWait>
+template <int MT, bool WO, bool COH = false, class Wait = NoWait, class Done = KeepAll>
 __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
                                  int p0, int cnt, int64_t c0, float *vs, uint16_t *bs,
                                  Wait wait = Wait(), Done v_read = Done())
@@ -222,7 +228,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     wait();
     stage_v<COH>(a, p0, cnt, r, q_lo, nq, vs);
     __syncthreads();   // B (first window) and v staged
-    v_read();
+    const bool keep = v_read();   // false: the wait gave up, y stays untouched
     const int qq = slice_of(a, c0 + 64 * wave) - q_lo;
     // LDS column of M-tile mt for row m, in units of the window's rank pitch
     int bcolumn[4];
@@ -280,7 +286,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                 }
             }
         }
-        if (in_d) {
+        if (in_d && keep) {
     #pragma unroll
             for (int nt = 0; nt < MT; ++nt) {
                 const int u = 16 * nt + m;
@@ -344,7 +350,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                     }
                 }
             }
-            if (in_d && u < cnt) {
+            if (in_d && u < cnt && keep) {
                 float f[16];
     #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
@@ -375,7 +381,7 @@ __device__ __forceinline__ uint4 b_word(const ApplyArgs &a, int64_t bslot, int64
                                                 gc * rp + elem0);
 }
 
-template <int DT, bool COH = false, class Wait = NoWait, class Done = NoWait>
+template <int DT, bool COH = false, class Wait = NoWait, class Done = KeepAll>
 __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, float scale,
                                  int p0, int cnt, int64_t c0, float *vs, uint32_t *bsh,
                                  Wait wait = Wait(), Done v_read = Done())
@@ -410,7 +416,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     const int nq = slice_of(a, min(c0 + kCols, a.D) - 1) - q_lo + 1;
     wait();
     stage_v<COH>(a, p0, cnt, r, q_lo, nq, vs);
-    v_read();
+    const bool keep = v_read();   // false: the wait gave up, y stays untouched
     const int P = v_pitch(nq, rp);
     const int cl = 64 * wave + 16 * g;               // lane's first column in the chunk
     int qh[2];
@@ -476,7 +482,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
         }
         lds_barrier();   // bsh is restaged by the next pass
     }
-    merge16<DT>(a, yi, h0, h1, y0, y1, scale, acc);
+    merge16<DT>(a, yi, h0 && keep, h1 && keep, y0, y1, scale, acc);
 }
 
 // Dynamic LDS: [rows: 64 int][slot table: rank, scale (when n_slots <= 256)]
@@ -484,7 +490,7 @@ __device__ void bgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
 // Tile t, 256-column chunk `chunk`.  Returns whether the workgroup computed
 // the tile (false: no such tile in this batch, a chunk past D, or a slot
 // emptied since the grouping).  COH, wait and v_read as the tile functions.
-template <int DT, int MT, bool WO, bool COH = false, class Wait = NoWait, class Done = NoWait>
+template <int DT, int MT, bool WO, bool COH = false, class Wait = NoWait, class Done = KeepAll>
 __device__ __forceinline__ bool expand_body(const ApplyArgs &a, int t, int chunk,
                                             Wait wait = Wait(), Done v_read = Done())
 {

@@ -89,6 +89,7 @@ struct ApplyArgs {
     int lds_bytes;             // expand: dynamic LDS bytes
     int cpw;                   // expand: 256-column chunks per workgroup (1: one chunk)
     int32_t *sync;             // one-launch apply: timeouts, per-tile flags and counters
+    int wait_limit;            // one-launch apply: polls before a wait gives up
     // batch
     const int32_t *counts;
     const ShrinkTile *tiles;
@@ -118,6 +119,49 @@ int build_apply_wgs_per_cu(int dtype, int lds_bytes);
 // hand-over as launch_build_apply), and its residency per CU
 hipError_t launch_apply(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream);
 int apply_wgs_per_cu(int dtype, int lds_bytes);
+// One-launch decode (decode.hip): grouping, shrink and expand of a batch of at
+// most kDecodeMaxRows rows over at most kDecodeMaxSlots slots (bf16, one
+// slice, rank <= 16), v handed over as tagged 64-bit words.
+constexpr int kDecodeMaxRows = 256;
+constexpr int kDecodeMaxSlots = 63;
+constexpr int kDecodeMaxKs = 8;
+constexpr int kDecEpoch = 20, kDecCount = 21;   // ints of a tile's sync record (after the flags)
+static_assert(kDecCount < kSyncTileInts && kDecEpoch > kMaxKSplit, "decode state beside the flags");
+constexpr int kWaitSpinsDefault = 1 << 18;      // polls before a one-launch wait gives up
+struct DecodeArgs {
+    const int32_t *ids;
+    int n;
+    int n_slots;
+    const int32_t *slot_rank;
+    const float *slot_scale;
+    const void *A;            // pool [n_slots][r_max][k]
+    const void *B;            // pool, slot s at s * b_slot_stride: [D][rp_s]
+    int64_t b_slot_stride;
+    int r_max;
+    int64_t k;
+    int64_t D;
+    const void *x;
+    int64_t ldx;
+    void *y;
+    int64_t ldy;
+    int ks;                   // k-splits (<= kDecodeMaxKs, (k / 8) % (16 ks) == 0)
+    int cpw;                  // 256-column chunks per expand workgroup (1, 2, 4)
+    int ncg;                  // expand workgroups per tile: ceil(D / (256 cpw))
+    int tiles_bound;          // T = ceil(n / 16) + min(n_slots, n)
+    uint64_t *vtag;           // [kDecodeMaxKs][vtag_tiles][16][16] tagged v partials
+    int vtag_tiles;           // tile stride of vtag: fixed per segments object, >= T
+    int32_t *tile_state;      // per tile kSyncTileInts ints (epoch, counter)
+    int32_t *timeouts;
+    int wait_limit;
+    // segments object
+    int32_t *perm;
+    int32_t *seg_off;
+    int32_t *active;
+    int32_t *counts;
+    ShrinkTile *tiles;
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+int decode_wgs_per_cu(int ks, int cpw);
 // Merge of one slot into a dense weight (rows tiled per slice, 64 rows a tile).
 struct MergeArgs {
     const void *A;             // the slot's A: [n_slices][r_max][k]
@@ -205,6 +249,9 @@ struct lora_segments {
     int dense_min;
     int expand_chunks;   // 0: chosen from the shapes
     int32_t *sync;       // one-launch apply state: kSyncFlags + max_tiles * kSyncTileInts ints
+    uint64_t *vtag;      // one-launch decode: tagged v partials, [kDecodeMaxKs][vtag_tiles][16][16]
+    int vtag_tiles;      // tile bound the decode buffer holds (0: no decode path)
+    int wait_limit;      // polls before a one-launch wait gives up
     int32_t *perm;
     int32_t *seg_off;
     int32_t *active;

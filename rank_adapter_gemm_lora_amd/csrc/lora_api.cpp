@@ -107,6 +107,7 @@ void free_segments(lora_segments *seg)
     (void)hipFree(seg->chunk_bad);
     (void)hipFree(seg->binfo);
     (void)hipFree(seg->sync);
+    (void)hipFree(seg->vtag);
     delete seg;
 }
 
@@ -264,6 +265,7 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     a.counts = seg->counts;
     a.tiles = seg->tiles;
     a.sync = seg->sync;
+    a.wait_limit = seg->wait_limit;
     return a;
 }
 
@@ -536,6 +538,11 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     seg->dense_min = 1;
     seg->expand_chunks = 0;
     seg->sync = nullptr;
+    seg->vtag = nullptr;
+    seg->vtag_tiles = n_slots <= kDecodeMaxSlots
+                          ? max_tiles_for(std::min<int64_t>(max_rows, kDecodeMaxRows), n_slots)
+                          : 0;
+    seg->wait_limit = kWaitSpinsDefault;
     seg->built = 0;
     seg->n_rows = 0;
     seg->n_slots = 0;
@@ -553,6 +560,11 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     const size_t sync_ints = kSyncFlags + (size_t)seg->max_tiles * kSyncTileInts;
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->sync), sizeof(int32_t) * sync_ints);
     if (e == hipSuccess) e = hipMemset(seg->sync, 0, sizeof(int32_t) * sync_ints);
+    const size_t vtag_words = (size_t)kDecodeMaxKs * seg->vtag_tiles * 16 * 16;
+    if (e == hipSuccess && vtag_words > 0)
+        e = hipMalloc(reinterpret_cast<void **>(&seg->vtag), sizeof(uint64_t) * vtag_words);
+    if (e == hipSuccess && vtag_words > 0)
+        e = hipMemset(seg->vtag, 0, sizeof(uint64_t) * vtag_words);
     if (e == hipSuccess) e = hipMemset(seg->counts, 0, sizeof(int32_t) * kCntSlots);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -585,6 +597,14 @@ lora_status lora_segments_set_expand_chunks(lora_segments *seg, int chunks)
     if (!seg || chunks < 0 || chunks > kMaxExpandChunks)
         return LORA_E_ARG;
     seg->expand_chunks = chunks;
+    return LORA_OK;
+}
+
+lora_status lora_segments_set_wait_limit(lora_segments *seg, int polls)
+{
+    if (!seg || polls < 0)
+        return LORA_E_ARG;
+    seg->wait_limit = polls;
     return LORA_OK;
 }
 
@@ -702,11 +722,96 @@ bool apply_one_launch_pays(const lora_stack *st, const ApplyArgs &a, int64_t n_r
     return capacity > 0 && (a.ks + chunks) * tiles <= capacity + capacity / 4;
 }
 
+// k-splits of the one-launch decode: the most (a power of two, at most
+// kDecodeMaxKs and at least 512 k per split) that leave every wavefront's
+// k-quarter whole 32-k matrix-core steps; 0 when none does.
+int decode_ks(int64_t k)
+{
+    if (k % 128 != 0)
+        return 0;
+    int ks = 1;
+    while (ks * 2 <= kDecodeMaxKs && k / (ks * 2) >= 512 && (k / 8) % (16 * ks * 2) == 0)
+        ks *= 2;
+    return ks;
+}
+
+// 256-column chunks per expand workgroup of the one-launch decode: 1 (the
+// caller's 2 or 4 on request).  Measured on the decode workload: 8.3 / 8.4 /
+// 8.7 us per step for 1 / 2 / 4 -- the merge into y runs on more SIMDs.
+int decode_cpw(const lora_stack *, const lora_segments *seg)
+{
+    const int f = seg->expand_chunks;
+    return f == 2 || f == 4 ? f : 1;
+}
+
+// The one-launch decode serves bf16 stacks of one slice with rank <= 16 and
+// whole 64-column output blocks, batches of 1 .. 256 rows over at most 63
+// slots with the default tile policy, while the grid fits the chip at once
+// with a quarter to spare (workgroups of tiles the mix leaves empty exit after
+// the grouping).
+bool decode_pays(const lora_stack *st, const lora_segments *seg, int64_t n_rows)
+{
+    if (st->dtype != LORA_BF16 || st->n_slices != 1 || st->r_max > 16 || st->D % 64 != 0 ||
+        n_rows < 1 || n_rows > kDecodeMaxRows || st->n_slots > kDecodeMaxSlots || !seg->vtag ||
+        seg->dense_min != 1 || decode_ks(st->k) == 0)
+        return false;
+    const int64_t tiles = max_tiles_for(n_rows, st->n_slots);
+    if (tiles > seg->vtag_tiles)
+        return false;
+    const int cpw = decode_cpw(st, seg);
+    if (st->n_cu == 0 &&
+        hipDeviceGetAttribute(&st->n_cu, hipDeviceAttributeMultiprocessorCount, st->device) != hipSuccess)
+        st->n_cu = 0;
+    const int wpc = decode_wgs_per_cu(decode_ks(st->k), cpw);
+    const int64_t capacity = (int64_t)wpc * st->n_cu;
+    const int64_t ncg = (st->D + 256 * cpw - 1) / (256 * cpw);
+    return capacity > 0 && (decode_ks(st->k) + ncg) * tiles <= capacity + capacity / 4;
+}
+
+DecodeArgs decode_args(const lora_stack *st, lora_segments *seg, const int32_t *ids, int64_t n_rows,
+                       const void *x, int64_t ldx, void *y, int64_t ldy)
+{
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.ids = ids;
+    a.n = (int)n_rows;
+    a.n_slots = st->n_slots;
+    a.slot_rank = st->d_rank;
+    a.slot_scale = st->d_scale;
+    a.A = st->A_pool;
+    a.B = st->B_pool;
+    a.b_slot_stride = st->D * st->rp_max;
+    a.r_max = st->r_max;
+    a.k = st->k;
+    a.D = st->D;
+    a.x = x;
+    a.ldx = ldx;
+    a.y = y;
+    a.ldy = ldy;
+    a.ks = decode_ks(st->k);
+    a.cpw = decode_cpw(st, seg);
+    a.ncg = (int)((st->D + 256 * a.cpw - 1) / (256 * a.cpw));
+    a.tiles_bound = max_tiles_for(n_rows, st->n_slots);
+    a.vtag = seg->vtag;
+    a.vtag_tiles = seg->vtag_tiles;
+    a.tile_state = seg->sync + kSyncFlags;
+    a.timeouts = seg->sync + kSyncTimeouts;
+    a.wait_limit = seg->wait_limit;
+    a.perm = seg->perm;
+    a.seg_off = seg->seg_off;
+    a.active = seg->active;
+    a.counts = seg->counts;
+    a.tiles = seg->tiles;
+    return a;
+}
+
 // Kernel launches lora_build_apply makes for n_rows.
 int build_apply_launches(const lora_stack *st, int64_t n_rows, const lora_segments *seg)
 {
     if (n_rows <= 0)
         return 1;   // the empty grouping
+    if (decode_pays(st, seg, n_rows))
+        return 1;
     if (fused_build_pays(st, n_rows))
         return one_launch_pays(st, args_for_rows(st, seg, n_rows), n_rows) ? 1 : 2;
     return n_rows <= kFusedMaxRows ? 3 : 5;   // one-workgroup or chunked grouping
@@ -837,6 +942,12 @@ lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const v
         return LORA_E_ARG;
     if (n_rows > 0 && (!x_ok(st, x, ldx) || !y_ok(st, y, ldy)))
         return LORA_E_ARG;
+    if (decode_pays(st, seg, n_rows)) {
+        LORA_TRY(launch_decode(decode_args(st, seg, ids, n_rows, x, ldx, y, ldy),
+                               reinterpret_cast<hipStream_t>(stream)));
+        mark_built(seg, st, n_rows);
+        return LORA_OK;
+    }
     if (n_rows > 0 && fused_build_pays(st, n_rows)) {
         // one launch when the whole grid fits the chip (the decode step)
         ApplyArgs a = args_for_rows(st, seg, n_rows);
@@ -900,8 +1011,18 @@ lora_status lora_get_device_status(const lora_segments *seg, int64_t *n_bad, voi
     LORA_TRY(hipStreamSynchronize(s));
     if (n_bad)
         *n_bad = c[kCntBad];
-    if (sy[kSyncTimeouts] > 0)
-        return LORA_E_HIP;   // a one-launch apply gave up waiting for its v
+    if (sy[kSyncTimeouts] > 0) {
+        // a one-launch apply gave up waiting for its v: reset the hand-over
+        // state (flags, counters, epochs, tagged v) so that later calls start
+        // clean; nothing runs on this stream meanwhile (it was synchronised)
+        const size_t sync_ints = kSyncFlags + (size_t)seg->max_tiles * kSyncTileInts;
+        LORA_TRY(hipMemsetAsync(seg->sync, 0, sizeof(int32_t) * sync_ints, s));
+        if (seg->vtag)
+            LORA_TRY(hipMemsetAsync(seg->vtag, 0,
+                                    sizeof(uint64_t) * kDecodeMaxKs * seg->vtag_tiles * 16 * 16, s));
+        LORA_TRY(hipStreamSynchronize(s));
+        return LORA_E_HIP;
+    }
     return c[kCntBad] > 0 ? LORA_E_BAD_IDS : LORA_OK;
 }
 

@@ -539,20 +539,20 @@ __global__ __launch_bounds__(256) void build_shrink_kernel(ApplyArgs a, SegBuild
     }
 }
 
-constexpr int kWaitSpins = 1 << 18;   // polls before a wait gives up
-
 // The handover of one tile's v inside a launch (see build_apply_kernel):
 // shrink workgroups publish(), expand workgroups wait() before reading v,
 // v_read() once every thread's v is in LDS, and finish() at the end.
 struct TileSync {
     int32_t *flag;   // the tile's split flags, then its expand workgroups' counter
     int32_t *timeouts;
+    int *gave_up;    // LDS: set when a wavefront's wait gave up (zeroed at kernel start)
     int n_split, n_chunks;
+    int wait_limit;  // polls before a wait gives up
     int seen;        // thread 0 of an expand workgroup: the counter before its add
 
-    __device__ TileSync(int32_t *sync, int t, int n_split_, int n_chunks_)
-        : flag(sync + kSyncFlags + t * kSyncTileInts), timeouts(sync + kSyncTimeouts),
-          n_split(n_split_), n_chunks(n_chunks_), seen(-1)
+    __device__ TileSync(const ApplyArgs &a, int t, int n_chunks_, int *gave_up_)
+        : flag(a.sync + kSyncFlags + t * kSyncTileInts), timeouts(a.sync + kSyncTimeouts),
+          gave_up(gave_up_), n_split(a.ks), n_chunks(n_chunks_), wait_limit(a.wait_limit), seen(-1)
     {
     }
     // shrink workgroup of split ks: its device-coherent v stores are issued
@@ -573,9 +573,11 @@ struct TileSync {
                             __hip_atomic_load(flag + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1;
             if (__all(ok))
                 break;
-            if (spins >= kWaitSpins) {
-                if (lane == 0)
+            if (spins >= wait_limit) {
+                if (lane == 0) {
                     __hip_atomic_fetch_add(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    *gave_up = 1;
+                }
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
@@ -584,12 +586,14 @@ struct TileSync {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
     // every thread's v is in LDS: count this workgroup done with the flags (the
-    // atomic's round trip overlaps the products; its result is used in finish)
-    __device__ void v_read()
+    // atomic's round trip overlaps the products; its result is used in finish).
+    // Returns whether y is to be written: not when any wavefront's wait gave up.
+    __device__ bool v_read()
     {
         lds_barrier();
         if (threadIdx.x == 0 && seen < 0)
             seen = __hip_atomic_fetch_add(flag + kMaxKSplit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return *gave_up == 0;
     }
     // the tile's last expand workgroup to count clears the flags and counter
     // (every other one has finished polling and reading v before it counted)
@@ -624,7 +628,7 @@ struct TileSync {
 // measured ~7 us per launch).  Each tile's state sits in its own 128 bytes.
 // An expand workgroup waits only on shrink workgroups of lower index, which
 // are dispatched before it and wait on nothing, so the waits always end; a
-// wait that exceeds kWaitSpins polls (well under a second) gives up and counts
+// wait that exceeds a.wait_limit polls (by default well under a second) gives up and counts
 // a timeout that lora_get_device_status reports.
 
 template <int DT>
@@ -634,12 +638,19 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
     __shared__ GroupLds g;
     __shared__ int wc[2][kGroupPer * kGroupWaves];
     __shared__ int32_t rows[kSgmvTileRows];
+    __shared__ int gave_up;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // expand staging
     const int tid = threadIdx.x, b = blockIdx.x;
     const bool prod = b < n_prod;
     const int t = prod ? b / a.ks : (b - n_prod) / n_chunks;
     const int ks = prod ? b - t * a.ks : 0;
     const int N = sb.n_slots;
+    // a wait of an earlier launch gave up: leave y untouched until the host
+    // has read the status (which resets the flags)
+    const bool poisoned =
+        __hip_atomic_load(a.sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    if (tid == 0)
+        gave_up = 0;   // ordered before any use by the grouping's barriers
     int key[kGroupPer], rank[kGroupPer];
     group_hist(sb.ids, (int)sb.n, N, sb.slot_rank, g, key);
     group_scan(g, N, sb.dense_min, 4);
@@ -658,10 +669,12 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
         }
         __syncthreads();
         const int r = g.rank[s];
-        TileSync sy(a.sync, t, a.ks, n_chunks);
+        TileSync sy(a, t, n_chunks, &gave_up);
         if (prod) {
-            shrink_tile<DT, 1, true>(a, rows, s, r, p0, cnt, p.path, ks);
-            sy.publish(ks);
+            if (!poisoned) {
+                shrink_tile<DT, 1, true>(a, rows, s, r, p0, cnt, p.path, ks);
+                sy.publish(ks);
+            }
             if (ks == 0) {
                 // the segments object receives what the grouping kernel writes
 #pragma unroll
@@ -676,11 +689,11 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
                 if (tid == 0)
                     *reinterpret_cast<int4 *>(&sb.tiles[t]) = make_int4(s, p0, cnt, p.path);
             }
-        } else {
+        } else if (!poisoned) {
             const int64_t c0 = (int64_t)(b - n_prod - t * n_chunks) * kCols;
             const float scale = a.scale[s];
             auto wait = [&]() { sy.wait(); };
-            auto v_read = [&]() { sy.v_read(); };
+            auto v_read = [&]() { return sy.v_read(); };
             float *vs = reinterpret_cast<float *>(lds + a.lds_v_off);
             unsigned char *bst = lds + a.lds_b_off;
             bool done = false;
@@ -719,18 +732,25 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
 template <int DT>
 __global__ __launch_bounds__(256) void apply_kernel(ApplyArgs a, int n_prod, int n_chunks)
 {
+    __shared__ int gave_up;
     const int b = blockIdx.x;
+    // a wait of an earlier launch gave up: leave y untouched until the host
+    // has read the status (which resets the flags)
+    if (__hip_atomic_load(a.sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+        return;
+    if (threadIdx.x == 0)
+        gave_up = 0;   // ordered before any use by the barriers of the tile code
     if (b < n_prod) {
         const int t = b / a.ks, ks = b - t * a.ks;
         if (shrink_body<DT, 1, true>(a, ks, t)) {
-            const TileSync sy(a.sync, t, a.ks, n_chunks);
+            const TileSync sy(a, t, n_chunks, &gave_up);
             sy.publish(ks);
         }
     } else {
         const int t = (b - n_prod) / n_chunks, chunk = b - n_prod - t * n_chunks;
-        TileSync sy(a.sync, t, a.ks, n_chunks);
+        TileSync sy(a, t, n_chunks, &gave_up);
         auto wait = [&]() { sy.wait(); };
-        auto v_read = [&]() { sy.v_read(); };
+        auto v_read = [&]() { return sy.v_read(); };
         if (expand_body<DT, 1, false, true>(a, t, chunk, wait, v_read))
             sy.finish();
     }

@@ -250,15 +250,16 @@ def test_apply_back_to_back_and_graph():
 
 def test_build_apply_plan():
     """Launch counts of lora_build_apply from the host query: one kernel for
-    the decode batch, two where the one-launch grid would not fit the chip (16
-    adapters at 256 rows; rank 128, whose LDS holds one workgroup per CU),
-    three or five for larger batches; the query changes nothing."""
+    decode batches (the decode kernel up to 63 slots of rank <= 16, so 16
+    adapters at 256 rows too), two where no one-launch grid fits the chip
+    (rank 128, whose LDS holds one workgroup per CU), three or five for larger
+    batches; the query changes nothing."""
     cases = {
         "decode_bgmv": (synth.make_workload("decode_bgmv"), 1),
         "mlp_gate_up": (synth.make_workload("mlp_gate_up"), 2),
         "many_adapter": (synth.make_workload("many_adapter"), 3),
         "16_adapters": (synth.make_random(3, n_rows=256, k=4096, slice_d=[4096], n_slots=16,
-                                          ranks=[16] * 16, r_max=16), 2),
+                                          ranks=[16] * 16, r_max=16), 1),
         "rank128": (synth.make_random(3, n_rows=256, k=4096, slice_d=[4096], n_slots=1,
                                       ranks=[128], r_max=128), 2),
         "rows3000": (synth.make_random(3, n_rows=3000, k=512, slice_d=[512], n_slots=8,
@@ -290,21 +291,32 @@ def test_build_apply_plan():
             run.close()
 
 
-@pytest.mark.parametrize("n_rows", [256, 3000])
-def test_build_apply_graph_replay_any_mix(n_rows):
+GRAPH_CASES = {
+    # name: (rows, k, output width, launches lora_build_apply makes)
+    "one_launch": (256, 512, 512, 1),        # the decode kernel
+    "two_launches": (512, 4096, 4096, 2),    # grouping inside the shrink, then the expand
+    "five_launches": (3000, 512, 512, 5),    # chunked grouping, shrink, expand
+}
+
+
+@pytest.mark.parametrize("case", list(GRAPH_CASES))
+def test_build_apply_graph_replay_any_mix(case):
     """The launch shapes depend only on the batch shape, so one captured HIP
     graph of lora_build_apply serves every adapter mix: replays with new ids
     (and a fresh base y) each match the oracle, segments included.  The new
-    inputs are copied in eagerly between replays, with synchronisations.
-    256 rows: grouping inside the shrink (two launches); 3000 rows: the chunked
-    grouping, shrink and expand (five launches)."""
-    base = synth.make_random(41, n_rows=n_rows, k=512, slice_d=[512], n_slots=8, ranks=[16] * 8,
+    inputs are copied in eagerly between replays, with synchronisations.  The
+    cases cover every launch layout of the call (the plan query confirms it)."""
+    n_rows, k, d, launches = GRAPH_CASES[case]
+    base = synth.make_random(41, n_rows=n_rows, k=k, slice_d=[d], n_slots=8, ranks=[16] * 8,
                              r_max=16, p_none=1 / 9)
     run = GpuRun(base)
     try:
+        got = lb.lora_build_apply_plan(run.stack, base.n_rows, run.seg)
+        if torch.cuda.get_device_properties(0).multi_processor_count == 256 or launches > 2:
+            assert got == launches, (case, got)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
-        note(f"graph capture of lora_build_apply, {n_rows} rows")
+        note(f"graph capture of lora_build_apply, {case}")
         with torch.cuda.graph(graph):
             lb.lora_build_apply(run.stack, run.y.data_ptr(), base.ldy, run.x.data_ptr(), base.ldx,
                                 run.ids.data_ptr(), base.n_rows, run.seg,
@@ -315,13 +327,13 @@ def test_build_apply_graph_replay_any_mix(n_rows):
             ids = rng.integers(-1, base.n_slots, size=base.n_rows).astype(np.int32)
             if rep == 3:
                 ids[:] = 2   # one dense group
-            p = synth.make_random(41, n_rows=n_rows, k=512, slice_d=[512], n_slots=8,
+            p = synth.make_random(41, n_rows=n_rows, k=k, slice_d=[d], n_slots=8,
                                   ranks=[16] * 8, r_max=16, ids=ids)
             p.A, p.B, p.alphas, p.x, p.y = base.A, base.B, base.alphas, base.x, base.y
             run.ids.copy_(torch.from_numpy(ids).to(run.device))
             run.y.copy_(torch.from_numpy(base.y.view(np.int16)).to(run.device))
             torch.cuda.synchronize()
-            note(f"graph replay {rep}, {n_rows} rows")
+            note(f"graph replay {rep}, {case}")
             graph.replay()
             torch.cuda.synchronize()
             check_against_oracle(p, run.y_host(), what=f"replay {rep}")
@@ -329,5 +341,79 @@ def test_build_apply_graph_replay_any_mix(n_rows):
                        f"replay {rep}")
             lb.lora_get_device_status(run.seg, run.stream)
         del graph
+    finally:
+        run.close()
+
+
+def _untouched_or_correct(p, y_out, what):
+    """Rows without an adapter and columns past D bitwise untouched; every
+    element of a valid row either bitwise untouched or within the gate's
+    per-element bound (4 bf16 ulps at max(|yref|, 2^-8 max|yref|)) of the
+    oracle.  Returns the fraction of valid-row elements left untouched."""
+    from oracle import compare
+    from gpu_helpers import oracle_rows, valid_mask
+    ok = valid_mask(p)
+    np.testing.assert_array_equal(y_out[~ok], p.y[~ok], err_msg=f"{what}: rows without adapter")
+    np.testing.assert_array_equal(y_out[:, p.D:], p.y[:, p.D:], err_msg=f"{what}: padding columns")
+    sel = np.nonzero(ok)[0]
+    ref = oracle_rows(p, rows=sel)
+    got = compare.to_f64(y_out[sel, :p.D], p.dtype)
+    same = y_out[sel, :p.D] == p.y[sel, :p.D]
+    floor = compare.ULP_FLOOR_FRACTION * np.max(np.abs(ref))
+    ulps = np.abs(got - ref) / compare.ulp_of(np.maximum(np.abs(ref), floor), p.dtype)
+    bad = ~same & ~(ulps <= compare.BF16_MAX_ULP)
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements neither untouched nor correct"
+    return float(same.mean())
+
+
+WAIT_GUARD_CASES = {
+    # name: (tile policy, call)
+    "decode_kernel": (None, "build_apply"),          # lora_build_apply, the decode kernel
+    "build_apply_kernel": (1 << 30, "build_apply"),  # vector tiles: the general one-launch kernel
+    "apply_kernel": (None, "apply"),                 # lora_apply of a grouped batch
+}
+
+
+@pytest.mark.parametrize("case", list(WAIT_GUARD_CASES))
+def test_wait_guard_leaves_y_untouched(case):
+    """The one-launch hand-over's bounded wait, forced to give up from the host
+    (a wait limit of 0 polls: each expand wavefront checks once, before its
+    shrink workgroups can have finished; every kernel still exits normally).
+    Rows of a tile whose wait gave up stay bitwise untouched, the rest are
+    correct; the next call on the object, made before the status is read,
+    leaves y wholly untouched; lora_get_device_status reports LORA_E_HIP and
+    resets the hand-over state, after which a call with the default limit
+    matches the oracle and reports no error."""
+    dm, call = WAIT_GUARD_CASES[case]
+    p = synth.make_workload("decode_bgmv")
+    run = GpuRun(p, dense_min=dm)
+    try:
+        y0 = run.y.clone()
+        assert lb.lora_build_apply_plan(run.stack, p.n_rows, run.seg) == 1   # one kernel
+        if call == "apply":
+            run.build()
+        fn = run.build_apply if call == "build_apply" else run.apply
+        lb.lora_segments_set_wait_limit(run.seg, 0)
+        note(f"wait guard {case}: limit 0")
+        fn()
+        frac = _untouched_or_correct(p, run.y_host(), f"{case} first call")
+        run.y.copy_(y0)
+        torch.cuda.synchronize()
+        note(f"wait guard {case}: call before the status is read")
+        fn()
+        y2 = run.y_host()
+        with pytest.raises(lb.LoraError) as e:
+            lb.lora_get_device_status(run.seg, run.stream)
+        assert e.value.status == lb.LORA_E_HIP, case
+        np.testing.assert_array_equal(y2, p.y, err_msg=f"{case}: call after a timeout wrote y")
+        note(f"wait guard {case}: {frac:.2f} of the first call's elements untouched")
+        lb.lora_segments_set_wait_limit(run.seg, 1 << 18)
+        run.y.copy_(y0)
+        torch.cuda.synchronize()
+        fn()
+        check_against_oracle(p, run.y_host(), what=f"{case} after the reset")
+        assert lb.lora_get_device_status(run.seg, run.stream) == 0   # no bad ids, no timeout
+        with pytest.raises(lb.LoraError):
+            lb.lora_segments_set_wait_limit(run.seg, -1)
     finally:
         run.close()
