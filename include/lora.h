@@ -326,6 +326,35 @@ lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const v
                              void *stream);
 
 /*
+ * lora_build_apply for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the one-launch decode of lora_build_apply with no segments object.  Its
+ * hand-over state -- per-tile epochs and counters and the tagged v partials,
+ * 1,304,576 bytes -- lives in a static device array that the library holds on
+ * each GPU it runs on until the process ends; nothing is allocated per call
+ * (the array's address is looked up once per device, on the first call with
+ * that device current).  y and the grouping's arithmetic are those of
+ * lora_build_apply on the same batch (bit-identical y); no segments are
+ * written.
+ *
+ *   y, ldy, x, ldx, ids, n_rows   as lora_build_apply (device pointers)
+ *   timeouts   DEVICE int32 or NULL: waits that gave up are added to it (a
+ *              guard that by construction never fires; rows of a tile whose
+ *              wait gave up are left untouched)
+ *
+ * Served shapes: bf16 stacks of one slice with r_max <= 16 and an output width
+ * of whole 64-column blocks, k a multiple of 128, at most 63 slots, 1 .. 256
+ * rows (the decode batches), and a grid that fits the chip at once.  Anything
+ * else returns LORA_E_UNSUPPORTED before anything is enqueued (n_rows == 0
+ * returns LORA_OK and does nothing).  Every call on one GPU shares the array:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be ordered by the caller.  Errors: LORA_E_ARG, LORA_E_UNSUPPORTED, LORA_E_HIP.
+ */
+lora_status lora_build_apply_noalloc(const lora_stack *st, void *y, int64_t ldy, const void *x,
+                                     int64_t ldx, const int32_t *ids, int64_t n_rows,
+                                     int32_t *timeouts, void *stream);
+
+/*
  * Kernel launches a lora_build_apply of n_rows rows on (st, seg) makes, with
  * seg's current tile policy: 1 (one kernel: the decode path), 2 (grouping
  * inside the shrink, then the expand), 3 (grouping, shrink, expand) or 5 (the

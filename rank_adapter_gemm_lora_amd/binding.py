@@ -32,7 +32,7 @@ EXPORTS = ("lora_stack_create", "lora_stack_destroy", "lora_load_slot", "lora_ev
            "lora_segments_set_wait_limit",
            "lora_build_segments", "lora_add_shrink",
            "lora_add_expand", "lora_apply", "lora_build_shrink", "lora_build_apply",
-           "lora_build_apply_plan",
+           "lora_build_apply_noalloc", "lora_build_apply_plan",
            "lora_residency_create", "lora_residency_destroy", "lora_residency_register",
            "lora_residency_unregister", "lora_residency_map_batch", "lora_residency_slot_of",
            "lora_residency_stats",
@@ -94,6 +94,7 @@ def load(path: str | None = None):
             "lora_apply": [P, P, I64, P, I64, P, P],
             "lora_build_shrink": [P, P, I64, P, I64, P, P],
             "lora_build_apply": [P, P, I64, P, I64, P, I64, P, P],
+            "lora_build_apply_noalloc": [P, P, I64, P, I64, P, I64, P, P],
             "lora_build_apply_plan": [P, I64, P, P],
             "lora_residency_create": [PP, P, I, I, I64, I, P, I, I],
             "lora_residency_destroy": [P],
@@ -217,6 +218,14 @@ def lora_build_apply(stack, y: int, ldy: int, x: int, ldx: int, ids: int, n_rows
     _check(load().lora_build_apply(stack, ctypes.c_void_p(y), int(ldy), ctypes.c_void_p(x),
                                    int(ldx), ctypes.c_void_p(ids), int(n_rows), seg,
                                    _stream(stream)), "lora_build_apply")
+
+
+def lora_build_apply_noalloc(stack, y: int, ldy: int, x: int, ldx: int, ids: int, n_rows: int,
+                             timeouts: int = 0, stream=None):
+    _check(load().lora_build_apply_noalloc(stack, ctypes.c_void_p(y), int(ldy), ctypes.c_void_p(x),
+                                           int(ldx), ctypes.c_void_p(ids), int(n_rows),
+                                           ctypes.c_void_p(timeouts or None), _stream(stream)),
+           "lora_build_apply_noalloc")
 
 
 def lora_build_apply_plan(stack, n_rows: int, seg) -> int:

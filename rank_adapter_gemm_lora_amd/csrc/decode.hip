@@ -56,6 +56,12 @@
 // untouched and counts a timeout; after that every launch on the segments
 // object leaves y untouched (it checks the count at its start) until
 // lora_get_device_status reports the timeout and resets the hand-over state.
+//
+// The allocation-free entry point at the end of this file runs the same
+// kernel with its hand-over state in a static device array instead of a
+// segments object.
+#include <mutex>
+
 #include "device_common.h"
 #include "group.h"
 #include "internal.h"
@@ -431,7 +437,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     const float sc_l = a.slot_scale[min(lane, a.n_slots - 1)];
     int32_t *st = a.tile_state + t * kSyncTileInts;
     const int epoch = __hip_atomic_load(st + kDecEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int poisoned = __hip_atomic_load(a.timeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int poisoned =
+        a.poison ? __hip_atomic_load(a.poison, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
     // (every workgroup issues the load, expand workgroups at the ids, so the
     // count of loads in flight is the same on every path)
     const uint32_t pf = *(prod ? dec_prefetch(a, t, part) : reinterpret_cast<const uint32_t *>(a.ids));
@@ -442,13 +449,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     if (prod) {
         if (tile_ok && poisoned == 0)
             dec_shrink(a, t, part, P, L, tag);
-        dec_store_segments(a, t, tile_ok && part == 0, b == 0, L, P);
+        if (a.perm)
+            dec_store_segments(a, t, tile_ok && part == 0, b == 0, L, P);
     } else if (tile_ok && poisoned == 0) {
         const int r = __shfl(rk_l, P.s);
         const float scale = __shfl(sc_l, P.s);
         const bool ok = dec_expand<KS, CPW>(a, t, part, P, L, tag, scale, r);
         if (tid == 0) {
-            if (!ok)
+            if (!ok && a.timeouts)
                 __hip_atomic_fetch_add(a.timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // every expand workgroup of the tile is done with its v: the last
             // advances the tile's epoch
@@ -480,7 +488,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
     if (a.n < 1 || a.n > kDecodeMaxRows || a.n_slots < 1 || a.n_slots > kDecodeMaxSlots || a.r_max > 16 ||
         a.ks < 1 || a.ks > kDecodeMaxKs || (a.k >> 3) % (16 * a.ks) != 0 || a.D % 64 != 0 ||
-        a.tiles_bound < 1 || a.tiles_bound > a.vtag_tiles || !a.vtag || !a.tile_state || !a.timeouts)
+        a.tiles_bound < 1 || a.tiles_bound > a.vtag_tiles || !a.vtag || !a.tile_state)
         return hipErrorInvalidValue;
     const int n_prod = a.ks * a.tiles_bound;
     const dim3 grid((unsigned)(n_prod + a.ncg * a.tiles_bound));
@@ -509,3 +517,79 @@ int decode_wgs_per_cu(int ks, int cpw)
 }
 
 }  // namespace lora
+
+// ---------------------------------------------------------------------------
+// lora_build_apply_noalloc: the one-launch decode with its hand-over state
+// (per-tile epochs and counters, then the tagged v words) in `scratch`, a
+// static device array every call on a GPU shares, so the call allocates
+// nothing.  The array starts zeroed (static storage) and every launch leaves
+// the counters zero; epochs only grow, and a tagged word from an earlier call
+// never matches a later call's tag.
+
+namespace lora {
+
+namespace {
+
+constexpr int kNoAllocTiles = kDecodeMaxRows / 16 + kDecodeMaxSlots;   // tile bound of any eligible batch
+constexpr size_t kNoAllocStateBytes = (size_t)kNoAllocTiles * kSyncTileInts * sizeof(int32_t);
+constexpr size_t kNoAllocStateAligned = (kNoAllocStateBytes + 255) / 256 * 256;
+constexpr size_t kNoAllocVtagBytes = (size_t)kDecodeMaxKs * kNoAllocTiles * 16 * 16 * sizeof(uint64_t);
+constexpr size_t kNoAllocScratchBytes = kNoAllocStateAligned + kNoAllocVtagBytes;   // 1,304,576 bytes
+static_assert(kNoAllocScratchBytes == 1304576, "the size the header states");
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kNoAllocMaxDevices];   // device address of `scratch`, per device
+
+// The device address of this device's copy of `scratch` (looked up once per
+// device, with that device current).
+hipError_t scratch_of(int dev, void **out)
+{
+    if (dev < 0 || dev >= kNoAllocMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!ptr)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+}  // namespace lora
+
+extern "C" lora_status lora_build_apply_noalloc(const lora_stack *st, void *y, int64_t ldy, const void *x,
+                                                int64_t ldx, const int32_t *ids, int64_t n_rows,
+                                                int32_t *timeouts, void *stream)
+{
+    using namespace lora;
+    if (!st || n_rows < 0 || (n_rows > 0 && !ids) || (reinterpret_cast<uintptr_t>(ids) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(timeouts) & 3u) != 0 || !device_is_current(st->device))
+        return LORA_E_ARG;
+    if (n_rows == 0)
+        return LORA_OK;
+    if (!x_ok(st, x, ldx) || !y_ok(st, y, ldy))
+        return LORA_E_ARG;
+    if (n_rows > kDecodeMaxRows || !decode_fits(st, n_rows, 1, kNoAllocTiles))
+        return LORA_E_UNSUPPORTED;
+    void *base = nullptr;
+    const lora_status ls = status_of(scratch_of(st->device, &base));
+    if (ls != LORA_OK)
+        return ls;
+    DecodeArgs a = decode_args_for(st, ids, n_rows, x, ldx, y, ldy, 1);
+    a.tile_state = static_cast<int32_t *>(base);
+    a.vtag = reinterpret_cast<uint64_t *>(static_cast<unsigned char *>(base) + kNoAllocStateAligned);
+    a.vtag_tiles = kNoAllocTiles;
+    a.timeouts = timeouts;
+    a.poison = nullptr;
+    return status_of(launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
+}

@@ -151,9 +151,10 @@ struct DecodeArgs {
     uint64_t *vtag;           // [kDecodeMaxKs][vtag_tiles][16][16] tagged v partials
     int vtag_tiles;           // tile stride of vtag: fixed per segments object, >= T
     int32_t *tile_state;      // per tile kSyncTileInts ints (epoch, counter)
-    int32_t *timeouts;
+    int32_t *timeouts;        // waits that gave up are counted here (may be null)
+    const int32_t *poison;    // nonzero at the start: leave y untouched (may be null)
     int wait_limit;
-    // segments object
+    // segments object (perm null: not written)
     int32_t *perm;
     int32_t *seg_off;
     int32_t *active;
@@ -162,6 +163,16 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 int decode_wgs_per_cu(int ks, int cpw);
+// Tiles of one batch never exceed ceil(rows / 16) plus one ragged tile per group.
+int max_tiles_for(int64_t n_rows, int n_slots);
+int decode_ks(int64_t k);
+bool decode_fits(const lora_stack *st, int64_t n_rows, int cpw, int vt_tiles);
+DecodeArgs decode_args_for(const lora_stack *st, const int32_t *ids, int64_t n_rows, const void *x,
+                           int64_t ldx, void *y, int64_t ldy, int cpw);
+bool x_ok(const lora_stack *st, const void *x, int64_t ldx);
+bool y_ok(const lora_stack *st, const void *y, int64_t ldy);
+lora_status status_of(hipError_t e);
+bool device_is_current(int dev);
 // Merge of one slot into a dense weight (rows tiled per slice, 64 rows a tile).
 struct MergeArgs {
     const void *A;             // the slot's A: [n_slices][r_max][k]

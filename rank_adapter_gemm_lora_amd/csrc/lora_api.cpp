@@ -67,13 +67,6 @@ int choose_ks(int64_t k, int64_t n_rows, int tile_rows)
     return (int)p;
 }
 
-// Tiles of one batch never exceed ceil(rows / 16) plus one ragged tile per
-// group.
-int max_tiles_for(int64_t n_rows, int n_slots)
-{
-    return (int)((n_rows + kBgmvTileRows - 1) / kBgmvTileRows +
-                 std::min<int64_t>(n_slots, n_rows));
-}
 
 bool current_device_is(int dev)
 {
@@ -321,6 +314,90 @@ void lora::note_loaded(lora_stack *st, int slot, int rank, float alpha)
 {
     st->h_rank[slot] = rank;
     st->h_alpha[slot] = alpha;
+}
+
+bool lora::x_ok(const lora_stack *st, const void *x, int64_t ldx)
+{
+    return x && aligned16(x) && ldx >= st->k && ldx % 8 == 0;
+}
+
+bool lora::y_ok(const lora_stack *st, const void *y, int64_t ldy)
+{
+    return y && aligned16(y) && ldy >= st->D && ldy % 8 == 0;
+}
+
+int lora::max_tiles_for(int64_t n_rows, int n_slots)
+{
+    return (int)((n_rows + kBgmvTileRows - 1) / kBgmvTileRows + std::min<int64_t>(n_slots, n_rows));
+}
+
+lora_status lora::status_of(hipError_t e) { return from_hip(e); }
+
+bool lora::device_is_current(int dev) { return current_device_is(dev); }
+
+// k-splits of the one-launch decode: the most (a power of two, at most
+// kDecodeMaxKs and at least 512 k per split) that leave every wavefront's
+// k-quarter whole 32-k matrix-core steps; 0 when none does.
+int lora::decode_ks(int64_t k)
+{
+    if (k % 128 != 0)
+        return 0;
+    int ks = 1;
+    while (ks * 2 <= kDecodeMaxKs && k / (ks * 2) >= 512 && (k / 8) % (16 * ks * 2) == 0)
+        ks *= 2;
+    return ks;
+}
+
+// The one-launch decode serves bf16 stacks of one slice with rank <= 16 and
+// whole 64-column output blocks, batches of 1 .. 256 rows over at most 63
+// slots, while the grid fits the chip at once with a quarter to spare
+// (workgroups of tiles the mix leaves empty exit after the grouping), and
+// the hand-over state holds vt_tiles tiles.
+bool lora::decode_fits(const lora_stack *st, int64_t n_rows, int cpw, int vt_tiles)
+{
+    if (st->dtype != LORA_BF16 || st->n_slices != 1 || st->r_max > 16 || st->D % 64 != 0 ||
+        n_rows < 1 || n_rows > kDecodeMaxRows || st->n_slots > kDecodeMaxSlots || decode_ks(st->k) == 0)
+        return false;
+    const int64_t tiles = max_tiles_for(n_rows, st->n_slots);
+    if (tiles > vt_tiles)
+        return false;
+    if (st->n_cu == 0 &&
+        hipDeviceGetAttribute(&st->n_cu, hipDeviceAttributeMultiprocessorCount, st->device) != hipSuccess)
+        st->n_cu = 0;
+    const int wpc = decode_wgs_per_cu(decode_ks(st->k), cpw);
+    const int64_t capacity = (int64_t)wpc * st->n_cu;
+    const int64_t ncg = (st->D + 256 * cpw - 1) / (256 * cpw);
+    return capacity > 0 && (decode_ks(st->k) + ncg) * tiles <= capacity + capacity / 4;
+}
+
+// Launch arguments of the one-launch decode, without its hand-over state and
+// segments outputs (the caller sets those).
+DecodeArgs lora::decode_args_for(const lora_stack *st, const int32_t *ids, int64_t n_rows, const void *x,
+                                 int64_t ldx, void *y, int64_t ldy, int cpw)
+{
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.ids = ids;
+    a.n = (int)n_rows;
+    a.n_slots = st->n_slots;
+    a.slot_rank = st->d_rank;
+    a.slot_scale = st->d_scale;
+    a.A = st->A_pool;
+    a.B = st->B_pool;
+    a.b_slot_stride = st->D * st->rp_max;
+    a.r_max = st->r_max;
+    a.k = st->k;
+    a.D = st->D;
+    a.x = x;
+    a.ldx = ldx;
+    a.y = y;
+    a.ldy = ldy;
+    a.ks = decode_ks(st->k);
+    a.cpw = cpw;
+    a.ncg = (int)((st->D + 256 * cpw - 1) / (256 * cpw));
+    a.tiles_bound = max_tiles_for(n_rows, st->n_slots);
+    a.wait_limit = kWaitSpinsDefault;
+    return a;
 }
 
 extern "C" {
@@ -722,19 +799,6 @@ bool apply_one_launch_pays(const lora_stack *st, const ApplyArgs &a, int64_t n_r
     return capacity > 0 && (a.ks + chunks) * tiles <= capacity + capacity / 4;
 }
 
-// k-splits of the one-launch decode: the most (a power of two, at most
-// kDecodeMaxKs and at least 512 k per split) that leave every wavefront's
-// k-quarter whole 32-k matrix-core steps; 0 when none does.
-int decode_ks(int64_t k)
-{
-    if (k % 128 != 0)
-        return 0;
-    int ks = 1;
-    while (ks * 2 <= kDecodeMaxKs && k / (ks * 2) >= 512 && (k / 8) % (16 * ks * 2) == 0)
-        ks *= 2;
-    return ks;
-}
-
 // 256-column chunks per expand workgroup of the one-launch decode: 1 (the
 // caller's 2 or 4 on request).  Measured on the decode workload: 8.3 / 8.4 /
 // 8.7 us per step for 1 / 2 / 4 -- the merge into y runs on more SIMDs.
@@ -744,58 +808,21 @@ int decode_cpw(const lora_stack *, const lora_segments *seg)
     return f == 2 || f == 4 ? f : 1;
 }
 
-// The one-launch decode serves bf16 stacks of one slice with rank <= 16 and
-// whole 64-column output blocks, batches of 1 .. 256 rows over at most 63
-// slots with the default tile policy, while the grid fits the chip at once
-// with a quarter to spare (workgroups of tiles the mix leaves empty exit after
-// the grouping).
 bool decode_pays(const lora_stack *st, const lora_segments *seg, int64_t n_rows)
 {
-    if (st->dtype != LORA_BF16 || st->n_slices != 1 || st->r_max > 16 || st->D % 64 != 0 ||
-        n_rows < 1 || n_rows > kDecodeMaxRows || st->n_slots > kDecodeMaxSlots || !seg->vtag ||
-        seg->dense_min != 1 || decode_ks(st->k) == 0)
-        return false;
-    const int64_t tiles = max_tiles_for(n_rows, st->n_slots);
-    if (tiles > seg->vtag_tiles)
-        return false;
-    const int cpw = decode_cpw(st, seg);
-    if (st->n_cu == 0 &&
-        hipDeviceGetAttribute(&st->n_cu, hipDeviceAttributeMultiprocessorCount, st->device) != hipSuccess)
-        st->n_cu = 0;
-    const int wpc = decode_wgs_per_cu(decode_ks(st->k), cpw);
-    const int64_t capacity = (int64_t)wpc * st->n_cu;
-    const int64_t ncg = (st->D + 256 * cpw - 1) / (256 * cpw);
-    return capacity > 0 && (decode_ks(st->k) + ncg) * tiles <= capacity + capacity / 4;
+    return seg->vtag && seg->dense_min == 1 &&
+           decode_fits(st, n_rows, decode_cpw(st, seg), seg->vtag_tiles);
 }
 
 DecodeArgs decode_args(const lora_stack *st, lora_segments *seg, const int32_t *ids, int64_t n_rows,
                        const void *x, int64_t ldx, void *y, int64_t ldy)
 {
-    DecodeArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.ids = ids;
-    a.n = (int)n_rows;
-    a.n_slots = st->n_slots;
-    a.slot_rank = st->d_rank;
-    a.slot_scale = st->d_scale;
-    a.A = st->A_pool;
-    a.B = st->B_pool;
-    a.b_slot_stride = st->D * st->rp_max;
-    a.r_max = st->r_max;
-    a.k = st->k;
-    a.D = st->D;
-    a.x = x;
-    a.ldx = ldx;
-    a.y = y;
-    a.ldy = ldy;
-    a.ks = decode_ks(st->k);
-    a.cpw = decode_cpw(st, seg);
-    a.ncg = (int)((st->D + 256 * a.cpw - 1) / (256 * a.cpw));
-    a.tiles_bound = max_tiles_for(n_rows, st->n_slots);
+    DecodeArgs a = decode_args_for(st, ids, n_rows, x, ldx, y, ldy, decode_cpw(st, seg));
     a.vtag = seg->vtag;
     a.vtag_tiles = seg->vtag_tiles;
     a.tile_state = seg->sync + kSyncFlags;
     a.timeouts = seg->sync + kSyncTimeouts;
+    a.poison = seg->sync + kSyncTimeouts;
     a.wait_limit = seg->wait_limit;
     a.perm = seg->perm;
     a.seg_off = seg->seg_off;
@@ -817,17 +844,8 @@ int build_apply_launches(const lora_stack *st, int64_t n_rows, const lora_segmen
     return n_rows <= kFusedMaxRows ? 3 : 5;   // one-workgroup or chunked grouping
 }
 
-bool x_ok(const lora_stack *st, const void *x, int64_t ldx)
-{
-    return x && aligned16(x) && ldx >= st->k && ldx % 8 == 0;
-}
-
-bool y_ok(const lora_stack *st, const void *y, int64_t ldy)
-{
-    return y && aligned16(y) && ldy >= st->D && ldy % 8 == 0;
-}
-
 }  // namespace
+
 
 lora_status lora_build_segments(const lora_stack *st, const int32_t *ids, int64_t n_rows,
                                 lora_segments *seg, void *stream)
