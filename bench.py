@@ -4,9 +4,10 @@
 
 A step is the whole hot path over one batch, one lora_build_apply call: group
 the rows by adapter, shrink (v = A x), expand (y += scale B v).  Decode-sized
-batches run it as one kernel (build_apply_kernel); other batches of up to 1024
-rows take two (grouping fused into the shrink, then the expand), larger ones
-three (grouping, shrink, expand).
+batches run it as one kernel (decode_kernel, or build_apply_kernel for shapes
+the decode kernel does not serve); other batches of up to 1024 rows take two
+(grouping fused into the shrink, then the expand), larger ones three or five
+(grouping, shrink, expand).
 Inputs are resident in HBM before the timed region.  Steps rotate through
 independent buffer sets (stack + ids + x + y) totalling >= 512 MB so that the
 256 MB MALL cannot serve them: every step reads its weights and rows from HBM.
@@ -16,19 +17,23 @@ One JSON line goes to stdout:
   roofline   the dominant kernel's algorithmic bytes per launch over its mean
              launch duration (that kernel launched K times back to back on the
              rotating sets, HIP events on the launch stream), against the
-             8 TB/s HBM peak; traffic = HBM bytes per launch from rocprofv3
-             FETCH_SIZE/WRITE_SIZE (scaled by a copy-kernel calibration) when a
-             committed measurement matches the current kernel sources, else null
+             8 TB/s HBM peak and against the achievable ceiling (a plain copy
+             kernel moving the same bytes in one launch, timed in the same run:
+             ceiling_gbs, frac_of_ceiling); traffic = HBM bytes per launch from
+             rocprofv3 FETCH_SIZE/WRITE_SIZE (scaled by a copy-kernel
+             calibration) when the committed measurement for the workload
+             (profiles/traffic.json) matches the current kernel sources, else null
   cpu_baseline  the CPU oracle on the host cores on a bounded sample
 
 Other modes: --all (every workload, lines to --out); --merge (lora_merge_slot
 on named projections, one line each); --sweep (adapter count x rank against the
 base GEMM of the same layer); --residency (adapter load bandwidth from the
 pinned host tier, decode steps under Zipf adapter churn); --copy-probe (plain copy
-kernel at the decode size and at 1 GB: the achievable HBM ceiling);
+kernel at each workload's step size and at 2 GiB: the achievable HBM ceiling);
 --copy-calib MB (a plain copy of known size, the calibration run for the PMC
 byte counters); --pmc-summary (fold two rocprofv3 --pmc runs and their
-calibration runs into bytes per launch).
+calibration runs into bytes per launch; --traffic-update stores them as the
+workload's entry of profiles/traffic.json).
 """
 from __future__ import annotations
 
@@ -53,7 +58,8 @@ ROTATE_BYTES = 512 << 20       # 2x the 256 MB MALL
 DEFAULT_WORKLOAD = "decode_bgmv"
 KERNEL_SOURCES = ("seg_build.hip", "shrink.hip", "expand.hip", "expand_tiles.h", "group.h",
                   "mfma.h", "device_common.h", "internal.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_bgmv.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = KERNEL_SOURCES + ("decode.hip",)
 
 
 def log(msg):
@@ -76,12 +82,13 @@ def accounting(p) -> dict:
     y_bytes = 2 * n_valid * p.D * b
     flops = sum(2 * int(p.ranks[s]) * (p.n_slices * p.k + p.D) + p.D for s in p.ids[ok])
     shrink_flops = sum(2 * int(p.ranks[s]) * p.n_slices * p.k for s in p.ids[ok])
+    # ids, the slot table and the grouping's outputs are metadata and are not
+    # counted (seg_build alone is priced by its ids and segments bytes)
     return dict(n_valid=n_valid, distinct_slots=int(slots.size),
                 bytes=dict(shrink=x_bytes + live_a, expand=y_bytes + live_b,
                            seg_build=8 * p.n_rows + 4 * (p.n_slots + 1),
-                           build_shrink=x_bytes + live_a + 8 * p.n_rows + 4 * (p.n_slots + 1),
-                           build_apply=x_bytes + y_bytes + live_a + live_b + 8 * p.n_rows
-                           + 4 * (p.n_slots + 1),
+                           build_shrink=x_bytes + live_a,
+                           build_apply=x_bytes + y_bytes + live_a + live_b,
                            apply=x_bytes + y_bytes + live_a + live_b,
                            total=x_bytes + y_bytes + live_a + live_b),
                 flops=dict(total=int(flops), shrink=int(shrink_flops), build_apply=int(flops),
@@ -103,14 +110,15 @@ def kernel_source_hash() -> str:
 
 
 def committed_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources and this workload; else None."""
+    """HBM bytes per launch of this workload's kernels from the committed
+    counter summary (one entry per workload), if the entry was taken on the
+    current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            t = json.load(f).get(workload)
+    except (OSError, ValueError, AttributeError):
         return None
-    if t.get("kernel_sources") != kernel_source_hash() or t.get("workload") != workload:
+    if not t or t.get("kernel_sources") != kernel_source_hash():
         return None
     return t
 
@@ -252,7 +260,9 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None, exp
             graphs.append(g)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
-            for i in range(min(warmup, n_sets)):
+            # every graph replayed once (a graph's first replay costs more),
+            # then the warm-up count
+            for i in range(n_sets + warmup):
                 graphs[i % n_sets].replay()
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
@@ -297,11 +307,30 @@ def run_gpu(p, steps: int, warmup: int, rotate: bool = True, dense_min=None, exp
 
 # ----------------------------------------------------------------- CPU oracle
 
+def host_cpu() -> dict:
+    """The host's CPU model and core counts: threads this process may run on
+    (its affinity mask) and CPUs online (os.cpu_count)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        visible = os.cpu_count() or 1
+    return dict(model=model, cores_visible=visible, cpus_online=os.cpu_count() or 1)
+
+
 def run_cpu_baseline(p, acct, budget_s: float = 10.0, budget_1t_s: float = 3.0) -> dict:
     """The oracle as it stands: OpenMP over rows on up to 16 host threads for
     ~budget_s, then one thread for ~budget_1t_s; full passes of the batch."""
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = max(1, min(16, host_cpu()["cores_visible"]))
     ranks = p.ranks
 
     def passes(n_threads, budget):
@@ -317,7 +346,10 @@ def run_cpu_baseline(p, acct, budget_s: float = 10.0, budget_1t_s: float = 3.0) 
 
     reps, el = passes(threads, budget_s)
     reps1, el1 = passes(1, budget_1t_s)
+    host = host_cpu()
     return dict(value=acct["n_valid"] * reps / el, unit="tokens/s", cores=threads, kind="oracle",
+                host_cores_visible=host["cores_visible"], host_cpus_online=host["cpus_online"],
+                cpu_model=host["model"],
                 sample=f"{reps} full passes of the {p.name} batch ({p.n_rows} rows, "
                        f"{acct['n_valid']} with an adapter): segments + fp64 apply, "
                        f"{el:.1f} s, OpenMP over rows",
@@ -342,11 +374,16 @@ def bench_workload(name, steps, warmup, rotate=True, cpu=True, dense_min=None,
     dom = max(g["step_kernels"], key=lambda k: ku[k])
     achieved = acct["bytes"][dom] / (ku[dom] * 1e-6) / 1e9
     traffic = committed_traffic(name)
+    # the achievable ceiling: a plain copy moving the same bytes in one launch
+    ceil = copy_probe((acct["bytes"][dom],), reps=max(20, steps))[0]
     roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=(traffic["per_launch_bytes"].get(dom) if traffic else None),
                 algorithmic_bytes_per_launch=acct["bytes"][dom],
-                mean_launch_us=round(ku[dom], 3))
+                mean_launch_us=round(ku[dom], 3),
+                ceiling_gbs=ceil["gbs"], frac_of_ceiling=round(achieved / ceil["gbs"], 4),
+                ceiling_note=f"plain device copy moving {ceil['bytes_moved']} bytes per launch "
+                             f"(HBM-cold rotation), {ceil['mean_us']} us")
     line = {
         "metric": "LoRA-applied tokens/s per layer + achieved HBM GB/s (% of MI355X peak)",
         "value": round(acct["n_valid"] * steps / (g["gpu_ms"] * 1e-3), 1),
@@ -682,18 +719,21 @@ def bench_residency(steps, warmup, out=None) -> list:
     return lines
 
 
-def copy_probe(reps: int = 50) -> list:
-    """A plain device copy at the decode step's size and at 1 GB (rotated past
-    the MALL): the achievable HBM ceiling, and the calibration kernel for the
-    PMC byte counters."""
+def copy_probe(moved=(7_626_752, 2 << 30), reps: int = 50) -> list:
+    """A plain device copy (torch's copy kernel) moving each of ``moved`` bytes
+    per launch (half read, half written), rotated over buffers totalling
+    >= 512 MB so the MALL cannot serve them: the achievable HBM rate of one
+    streaming launch of that size, launch overhead included, to set beside the
+    8 TB/s paper peak."""
     import torch
     dev = torch.device("cuda:0")
     out = []
-    for nbytes in (7_690_000 // 256 * 256, 1 << 30):
-        n_buf = max(2, math.ceil(ROTATE_BYTES / nbytes))
+    for total in moved:
+        nbytes = max(256, total // 2 // 256 * 256)
+        n_buf = max(2, math.ceil(ROTATE_BYTES / (2 * nbytes)))
         src = [torch.empty(nbytes // 2, dtype=torch.int16, device=dev).fill_(1) for _ in range(n_buf)]
         dst = [torch.empty_like(s) for s in src]
-        for i in range(5):
+        for i in range(n_buf + 5):
             dst[i % n_buf].copy_(src[i % n_buf])
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -703,9 +743,9 @@ def copy_probe(reps: int = 50) -> list:
             dst[i % n_buf].copy_(src[i % n_buf])
         e1.record()
         torch.cuda.synchronize()
-        us = np.array([e0.elapsed_time(e1) * 1e3 / reps])
-        out.append(dict(bytes_moved=2 * nbytes, mean_us=float(us.mean()),
-                        gbs=round(2 * nbytes / (us.mean() * 1e-6) / 1e9, 1)))
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out.append(dict(bytes_moved=2 * nbytes, mean_us=round(us, 3),
+                        gbs=round(2 * nbytes / (us * 1e-6) / 1e9, 1)))
         del src, dst
         torch.cuda.empty_cache()
     return out
@@ -759,7 +799,8 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, copy_mb, wor
     # and a chunked variant)
     names = {"seg_build": ("seg_build_kernel", "seg_build_small_kernel"),
              "shrink": ("shrink_kernel", "shrink_kernel_tall"),
-             "build_shrink": ("build_shrink_kernel",), "build_apply": ("build_apply_kernel",),
+             "build_shrink": ("build_shrink_kernel",),
+             "build_apply": ("decode_kernel", "build_apply_kernel"),
              "apply": ("apply_kernel",),
              "expand": ("expand_kernel", "expand_kernel_bf16_short", "expand_stream_kernel")}
 
@@ -809,11 +850,24 @@ def main(argv=None):
     ap.add_argument("--pmc-summary", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"))
     ap.add_argument("--copy-mb", type=int, default=256)
+    ap.add_argument("--traffic-update", action="store_true",
+                    help="with --pmc-summary: store the result as --workload's entry of "
+                         "profiles/traffic.json")
     args = ap.parse_args(argv)
 
     if args.pmc_summary:
         res = pmc_summary(*args.pmc_summary, args.copy_mb, args.workload)
         print(json.dumps(res, indent=1))
+        if args.traffic_update:
+            try:
+                with open(TRAFFIC_FILE) as f:
+                    table = json.load(f)
+            except (OSError, ValueError):
+                table = {}
+            table[args.workload] = res
+            with open(TRAFFIC_FILE, "w") as f:
+                json.dump(table, f, indent=1, sort_keys=True)
+                f.write("\n")
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -827,7 +881,12 @@ def main(argv=None):
         copy_calibration(args.copy_calib)
         return 0
     if args.copy_probe:
-        res = copy_probe()
+        from rank_adapter_gemm_lora_amd import synth
+        sizes = {n: accounting(synth.make_workload(n))["bytes"]["total"]
+                 for n in ("decode_bgmv", "mlp_down", "mlp_gate_up", "many_adapter", "prefill_sgmv")}
+        res = copy_probe(tuple(sizes.values()) + (2 << 30,))
+        for r, n in zip(res, list(sizes) + ["2 GiB"]):
+            r["size_of"] = n
         print(json.dumps({"copy_probe": res}))
         return 0
 

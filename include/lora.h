@@ -330,7 +330,7 @@ lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const v
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * the one-launch decode of lora_build_apply with no segments object.  Its
  * hand-over state -- per-tile epochs and counters and the tagged v partials,
- * 1,304,576 bytes -- lives in a static device array that the library holds on
+ * 1,223,680 bytes -- lives in a static device array that the library holds on
  * each GPU it runs on until the process ends; nothing is allocated per call
  * (the array's address is looked up once per device, on the first call with
  * that device current).  y and the grouping's arithmetic are those of

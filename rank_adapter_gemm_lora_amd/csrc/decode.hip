@@ -23,27 +23,32 @@
 //
 //   shrink  x and A of its tile's rows over its k-range on the matrix cores
 //           (M = rows, N = ranks, K = k), the four wavefronts' k-quarters
-//           summed in LDS in a fixed order, then every (row, rank) partial
-//           stored as one 64-bit word {fp32 value, 32-bit tag} with a relaxed
-//           device-scope atomic store (written through to where every XCD
-//           reads it);
+//           summed in LDS in a fixed order, then every (row, rank) partial of
+//           the tile -- all 16 rows, whatever the tile's row count -- stored
+//           as one 32-bit word (the fp32 value with its lowest fraction bit
+//           replaced by a tag bit) with a relaxed device-scope atomic store
+//           (written through to where every XCD reads it);
 //   expand  y and B of its columns in flight, then each thread polls the KS
 //           words of one (row, rank) of v with device-scope atomic loads until
-//           every tag is the tile's current one, sums them in split order,
-//           and the tile is expanded on the matrix cores (M = columns, N =
-//           rows, K = 16 ranks of v's bf16 high part + the same 16 of its low
-//           part) and merged into y with one rounding.
+//           every tag bit is the launch's, sums them (tag bits cleared) in
+//           split order, and the tile is expanded on the matrix cores (M =
+//           columns, N = rows, K = 16 ranks of v's bf16 high part + the same
+//           16 of its low part) and merged into y with one rounding.
 //
-// Word (split, tile, row, rank) has a fixed address for the segments object
-// (the tile stride is its allocation bound, not this launch's T), so only tile
-// t ever writes tile t's words.  A word is valid when its tag equals the
-// tile's epoch + 1.  The epoch (one
-// int per tile, in the segments object) is read by every workgroup of the tile
-// at its start; the tile's last expand workgroup (found with a per-tile
-// counter) advances it.  A word from an earlier launch carries an older tag,
-// so no flag has to be cleared and a captured graph replays correctly.  Since
-// a word's value and tag travel in one atomic access, no fence or store
-// acknowledgement sits between the shrink and the expand.
+// The words of (tile t, k-split count class c = log2 KS) have fixed addresses
+// for the segments object (the tile stride is its allocation bound, not this
+// launch's T), written only by launches where tile t is live with KS splits,
+// and every such launch rewrites all of them.  The class has an epoch (an int
+// per tile and class in the segments object), read by every workgroup of the
+// tile at its start; a launch's tag bit is the parity of epoch + 1, and the
+// tile's last expand workgroup (found with a per-tile counter) advances the
+// epoch.  So when a launch starts, every word of (t, c) carries the parity of
+// the epoch it reads, the opposite of what it waits for, and a word is valid
+// only once this launch has written it: no flag has to be cleared, and a
+// captured graph replays correctly.  Since a word's value and tag travel in
+// one atomic access, no fence or store acknowledgement sits between the
+// shrink and the expand.  Every path of the library stores v partials with
+// that bit cleared, so the paths stay bit-identical.
 //
 // Before the grouping, shrink workgroups prefetch into L2 the rows and the
 // slot weights their k-split will read (the workgroups of one split sit on one
@@ -211,9 +216,17 @@ __device__ __forceinline__ void dec_store_segments(const DecodeArgs &a, int t, b
     }
 }
 
-__device__ __forceinline__ uint64_t tagged(float v, uint32_t tag)
+// A v partial with the launch's tag bit in place of its lowest fraction bit.
+__device__ __forceinline__ uint32_t tagged(float v, uint32_t tag)
 {
-    return ((uint64_t)tag << 32) | __float_as_uint(v);
+    return (__float_as_uint(v) & ~1u) | tag;
+}
+
+// The words of k-split class log2(KS): [ks][tile][16 rows][16 ranks].
+template <int KS>
+__device__ __forceinline__ uint32_t *class_words(const DecodeArgs &a)
+{
+    return a.vtag + (int64_t)(KS - 1) * a.vtag_tiles * kT * kT;
 }
 
 // Prefetch into L2 (through this XCD) what the k-split's shrink workgroups
@@ -249,7 +262,9 @@ __device__ __forceinline__ const uint32_t *dec_prefetch(const DecodeArgs &a, int
     return reinterpret_cast<const uint32_t *>(p);
 }
 
-// Shrink of tile (s, rows) over k-split ks: v partials stored tagged.
+// Shrink of tile (s, rows) over k-split ks: v partials stored tagged (all 16
+// rows; rows past the tile's count repeat its last row).
+template <int KS>
 __device__ __forceinline__ void dec_shrink(const DecodeArgs &a, int t, int ks, const DecPlan &P,
                                            DecLds &L, uint32_t tag)
 {
@@ -285,9 +300,8 @@ __device__ __forceinline__ void dec_shrink(const DecodeArgs &a, int t, int ks, c
     const int u = tid >> 4, j = tid & 15;
     const int src = 16 * (u >> 2) + j, i = u & 3;
     const float v = ((L.red[0][src][i] + L.red[1][src][i]) + L.red[2][src][i]) + L.red[3][src][i];
-    if (u < P.cnt)
-        __hip_atomic_store(a.vtag + (((int64_t)ks * a.vtag_tiles + t) * kT + u) * kT + j, tagged(v, tag),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(class_words<KS>(a) + (((int64_t)ks * a.vtag_tiles + t) * kT + u) * kT + j,
+                       tagged(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Expand of tile (s, rows) over column group cg (CPW quads of 64 columns per
@@ -331,24 +345,24 @@ __device__ __forceinline__ bool dec_expand(const DecodeArgs &a, int t, int cg, c
     float vsum = 0.f;
     bool gave_up = false;
     if (u < P.cnt) {
-        const uint64_t *src = a.vtag + ((int64_t)t * kT + u) * kT + j;
+        const uint32_t *src = class_words<KS>(a) + ((int64_t)t * kT + u) * kT + j;
         const int64_t stride = (int64_t)a.vtag_tiles * kT * kT;
-        auto poll = [&](uint64_t (&w)[KS]) {
+        auto poll = [&](uint32_t (&w)[KS]) {
 #pragma unroll
             for (int k2 = 0; k2 < KS; ++k2)
                 w[k2] = __hip_atomic_load(src + k2 * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         };
-        // all KS words carry this launch's tag: their sum in split order
-        auto ready = [&](const uint64_t (&w)[KS]) {
+        // all KS words carry this launch's tag bit: their sum in split order
+        auto ready = [&](const uint32_t (&w)[KS]) {
             bool ok = true;
 #pragma unroll
             for (int k2 = 0; k2 < KS; ++k2)
-                ok = ok && (uint32_t)(w[k2] >> 32) == tag;
+                ok = ok && (w[k2] & 1u) == tag;
             if (ok) {
-                float sum = __uint_as_float((uint32_t)w[0]);
+                float sum = __uint_as_float(w[0] & ~1u);
 #pragma unroll
                 for (int k2 = 1; k2 < KS; ++k2)
-                    sum += __uint_as_float((uint32_t)w[k2]);
+                    sum += __uint_as_float(w[k2] & ~1u);
                 vsum = sum;
             }
             return ok;
@@ -356,7 +370,7 @@ __device__ __forceinline__ bool dec_expand(const DecodeArgs &a, int t, int cg, c
         // one poll in flight at a time (measured: a second one in flight adds
         // memory traffic that slows the step by 0.7 us)
         for (int spin = 0;; ++spin) {
-            uint64_t w[KS];
+            uint32_t w[KS];
             poll(w);
             if (ready(w))
                 break;
@@ -436,7 +450,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     const int rk_l = a.slot_rank[min(lane, a.n_slots - 1)];
     const float sc_l = a.slot_scale[min(lane, a.n_slots - 1)];
     int32_t *st = a.tile_state + t * kSyncTileInts;
-    const int epoch = __hip_atomic_load(st + kDecEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    constexpr int kClass = KS == 1 ? 0 : KS == 2 ? 1 : KS == 4 ? 2 : 3;   // log2 KS
+    const int epoch = __hip_atomic_load(st + kDecEpoch + kClass, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int poisoned =
         a.poison ? __hip_atomic_load(a.poison, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
     // (every workgroup issues the load, expand workgroups at the ids, so the
@@ -445,10 +460,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     DecPlan P;
     dec_group(a, t, id, rk_l, L, P);
     const bool tile_ok = t < P.n_tiles;
-    const uint32_t tag = (uint32_t)epoch + 1u;
+    const uint32_t tag = ((uint32_t)epoch + 1u) & 1u;
     if (prod) {
         if (tile_ok && poisoned == 0)
-            dec_shrink(a, t, part, P, L, tag);
+            dec_shrink<KS>(a, t, part, P, L, tag);
         if (a.perm)
             dec_store_segments(a, t, tile_ok && part == 0, b == 0, L, P);
     } else if (tile_ok && poisoned == 0) {
@@ -463,7 +478,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             const int seen = __hip_atomic_fetch_add(st + kDecCount, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (seen == a.ncg - 1) {
                 __hip_atomic_store(st + kDecCount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(st + kDecEpoch, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(st + kDecEpoch + kClass, epoch + 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -487,7 +503,8 @@ hipError_t launch_decode_ks(const DecodeArgs &a, dim3 grid, hipStream_t stream)
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
     if (a.n < 1 || a.n > kDecodeMaxRows || a.n_slots < 1 || a.n_slots > kDecodeMaxSlots || a.r_max > 16 ||
-        a.ks < 1 || a.ks > kDecodeMaxKs || (a.k >> 3) % (16 * a.ks) != 0 || a.D % 64 != 0 ||
+        a.ks < 1 || a.ks > kDecodeMaxKs || (a.ks & (a.ks - 1)) != 0 || (a.k >> 3) % (16 * a.ks) != 0 ||
+        a.D % 64 != 0 ||
         a.tiles_bound < 1 || a.tiles_bound > a.vtag_tiles || !a.vtag || !a.tile_state)
         return hipErrorInvalidValue;
     const int n_prod = a.ks * a.tiles_bound;
@@ -533,9 +550,9 @@ namespace {
 constexpr int kNoAllocTiles = kDecodeMaxRows / 16 + kDecodeMaxSlots;   // tile bound of any eligible batch
 constexpr size_t kNoAllocStateBytes = (size_t)kNoAllocTiles * kSyncTileInts * sizeof(int32_t);
 constexpr size_t kNoAllocStateAligned = (kNoAllocStateBytes + 255) / 256 * 256;
-constexpr size_t kNoAllocVtagBytes = (size_t)kDecodeMaxKs * kNoAllocTiles * 16 * 16 * sizeof(uint64_t);
-constexpr size_t kNoAllocScratchBytes = kNoAllocStateAligned + kNoAllocVtagBytes;   // 1,304,576 bytes
-static_assert(kNoAllocScratchBytes == 1304576, "the size the header states");
+constexpr size_t kNoAllocVtagBytes = (size_t)kDecodeWordsPerTile * kNoAllocTiles * sizeof(uint32_t);
+constexpr size_t kNoAllocScratchBytes = kNoAllocStateAligned + kNoAllocVtagBytes;   // 1,223,680 bytes
+static_assert(kNoAllocScratchBytes == 1223680, "the size the header states");
 
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
@@ -587,7 +604,7 @@ extern "C" lora_status lora_build_apply_noalloc(const lora_stack *st, void *y, i
         return ls;
     DecodeArgs a = decode_args_for(st, ids, n_rows, x, ldx, y, ldy, 1);
     a.tile_state = static_cast<int32_t *>(base);
-    a.vtag = reinterpret_cast<uint64_t *>(static_cast<unsigned char *>(base) + kNoAllocStateAligned);
+    a.vtag = reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(base) + kNoAllocStateAligned);
     a.vtag_tiles = kNoAllocTiles;
     a.timeouts = timeouts;
     a.poison = nullptr;

@@ -40,6 +40,10 @@ __device__ __forceinline__ int div_small(int n, uint32_t m)
     return (int)(((uint64_t)(uint32_t)n * m) >> 24);
 }
 
+// A k-split partial of v as stored: its lowest fraction bit cleared (a
+// relative change below 2^-22, far inside the output's rounding).
+__device__ __forceinline__ float v_word(float x) { return __uint_as_float(__float_as_uint(x) & ~1u); }
+
 // Workgroup barrier that orders LDS only: waits for this wavefront's LDS
 // stores (lgkmcnt), not for its global loads, so loads issued ahead of the
 // barrier stay in flight across it.  __syncthreads() is a full release fence

@@ -125,8 +125,12 @@ int apply_wgs_per_cu(int dtype, int lds_bytes);
 constexpr int kDecodeMaxRows = 256;
 constexpr int kDecodeMaxSlots = 63;
 constexpr int kDecodeMaxKs = 8;
-constexpr int kDecEpoch = 20, kDecCount = 21;   // ints of a tile's sync record (after the flags)
+// a tile's sync record, after the flags: the epoch of each k-split class (1,
+// 2, 4, 8 splits: ints kDecEpoch + log2 ks), then the expand workgroups' counter
+constexpr int kDecEpoch = 20, kDecCount = 24;
 static_assert(kDecCount < kSyncTileInts && kDecEpoch > kMaxKSplit, "decode state beside the flags");
+// tagged v words per tile: one region per k-split class, ks x 16 rows x 16 ranks each
+constexpr int kDecodeWordsPerTile = (2 * kDecodeMaxKs - 1) * 16 * 16;
 constexpr int kWaitSpinsDefault = 1 << 18;      // polls before a one-launch wait gives up
 struct DecodeArgs {
     const int32_t *ids;
@@ -148,7 +152,8 @@ struct DecodeArgs {
     int cpw;                  // 256-column chunks per expand workgroup (1, 2, 4)
     int ncg;                  // expand workgroups per tile: ceil(D / (256 cpw))
     int tiles_bound;          // T = ceil(n / 16) + min(n_slots, n)
-    uint64_t *vtag;           // [kDecodeMaxKs][vtag_tiles][16][16] tagged v partials
+    uint32_t *vtag;           // tagged v partials: region of class c at (2^c - 1) * vtag_tiles * 256
+                              // words, [ks][tile][16 rows][16 ranks] in it
     int vtag_tiles;           // tile stride of vtag: fixed per segments object, >= T
     int32_t *tile_state;      // per tile kSyncTileInts ints (epoch, counter)
     int32_t *timeouts;        // waits that gave up are counted here (may be null)
@@ -260,7 +265,7 @@ struct lora_segments {
     int dense_min;
     int expand_chunks;   // 0: chosen from the shapes
     int32_t *sync;       // one-launch apply state: kSyncFlags + max_tiles * kSyncTileInts ints
-    uint64_t *vtag;      // one-launch decode: tagged v partials, [kDecodeMaxKs][vtag_tiles][16][16]
+    uint32_t *vtag;      // one-launch decode: tagged v partials, kDecodeWordsPerTile per tile
     int vtag_tiles;      // tile bound the decode buffer holds (0: no decode path)
     int wait_limit;      // polls before a one-launch wait gives up
     int32_t *perm;

@@ -637,11 +637,11 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     const size_t sync_ints = kSyncFlags + (size_t)seg->max_tiles * kSyncTileInts;
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->sync), sizeof(int32_t) * sync_ints);
     if (e == hipSuccess) e = hipMemset(seg->sync, 0, sizeof(int32_t) * sync_ints);
-    const size_t vtag_words = (size_t)kDecodeMaxKs * seg->vtag_tiles * 16 * 16;
+    const size_t vtag_words = (size_t)kDecodeWordsPerTile * seg->vtag_tiles;
     if (e == hipSuccess && vtag_words > 0)
-        e = hipMalloc(reinterpret_cast<void **>(&seg->vtag), sizeof(uint64_t) * vtag_words);
+        e = hipMalloc(reinterpret_cast<void **>(&seg->vtag), sizeof(uint32_t) * vtag_words);
     if (e == hipSuccess && vtag_words > 0)
-        e = hipMemset(seg->vtag, 0, sizeof(uint64_t) * vtag_words);
+        e = hipMemset(seg->vtag, 0, sizeof(uint32_t) * vtag_words);
     if (e == hipSuccess) e = hipMemset(seg->counts, 0, sizeof(int32_t) * kCntSlots);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -1037,7 +1037,7 @@ lora_status lora_get_device_status(const lora_segments *seg, int64_t *n_bad, voi
         LORA_TRY(hipMemsetAsync(seg->sync, 0, sizeof(int32_t) * sync_ints, s));
         if (seg->vtag)
             LORA_TRY(hipMemsetAsync(seg->vtag, 0,
-                                    sizeof(uint64_t) * kDecodeMaxKs * seg->vtag_tiles * 16 * 16, s));
+                                    sizeof(uint32_t) * kDecodeWordsPerTile * seg->vtag_tiles, s));
         LORA_TRY(hipStreamSynchronize(s));
         return LORA_E_HIP;
     }

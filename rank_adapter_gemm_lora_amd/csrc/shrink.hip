@@ -50,10 +50,13 @@ __device__ __forceinline__ float *v_out(const ApplyArgs &a, int ks, int pos)
 
 // One element of v: a plain store, or a device-coherent one (relaxed agent
 // scope: written through to where every XCD reads it) for a reader in the same
-// launch.
+// launch.  Every path stores a partial with its lowest fraction bit cleared
+// (the one-launch decode carries its hand-over tag in that bit), so all paths
+// sum the same values.
 template <bool COH>
 __device__ __forceinline__ void put_v(float *p, float x)
 {
+    x = v_word(x);
     if constexpr (COH)
         __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
@@ -384,7 +387,7 @@ __device__ __forceinline__ void tall_pass(const ApplyArgs &a, const int64_t (&xs
             for (int i = 0; i < 4; ++i) {
                 const int u = 16 * wave + 4 * g + i;
                 if (u < cnt)
-                    v_out(a, ks, p0 + u)[q * a.r_max + j] = acc[tt][i];
+                    v_out(a, ks, p0 + u)[q * a.r_max + j] = v_word(acc[tt][i]);
             }
         }
     }

@@ -27,8 +27,9 @@ def test_decode_bytes_by_hand():
     assert (x, y, live) == (1_843_200, 3_686_400, 2_097_152)
     assert a["bytes"]["total"] == x + y + live == 7_626_752
     assert a["bytes"]["apply"] == 7_626_752
-    # the one-launch step also reads the ids and the slot table
-    assert a["bytes"]["build_apply"] == 7_626_752 + 8 * 256 + 4 * 9 == 7_628_836
+    # ids, slot table and segments are metadata, not algorithmic bytes
+    assert a["bytes"]["build_apply"] == 7_626_752
+    assert a["bytes"]["build_shrink"] == x + 8 * 16 * 4096 * 2
     assert a["bytes"]["shrink"] == x + 8 * 16 * 4096 * 2
     assert a["bytes"]["expand"] == y + 8 * 16 * 4096 * 2
     assert a["flops"]["total"] == n * (2 * 16 * (4096 + 4096) + 4096)
