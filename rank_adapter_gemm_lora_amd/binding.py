@@ -65,7 +65,8 @@ def load(path: str | None = None):
     with _lock:
         if _lib is not None and path is None:
             return _lib
-        p = path or LIB_PATH
+        # another build of the same library (the host-sanitized CPU test build)
+        p = path or os.environ.get("RANK_ADAPTER_GEMM_LORA_LIB") or LIB_PATH
         if not os.path.exists(p):
             raise RuntimeError(f"HIP library not built: {p} is missing "
                                "(run `python -m rank_adapter_gemm_lora_amd.build`)")

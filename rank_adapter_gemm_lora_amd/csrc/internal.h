@@ -192,6 +192,7 @@ struct MergeArgs {
     int n_slices;
     int64_t slice_off[LORA_MAX_SLICES + 1];
     int tile0[LORA_MAX_SLICES + 1];   // first row tile of each slice; [n_slices] = total
+    int n_cu;                  // compute units of the device (sizes the persistent grid)
 };
 int merge_row_tiles(int64_t d);
 hipError_t launch_merge(int dtype, const MergeArgs &a, hipStream_t stream);

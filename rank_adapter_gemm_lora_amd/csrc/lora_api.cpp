@@ -580,6 +580,12 @@ lora_status lora_merge_slot(const lora_stack *st, int slot, void *W, int64_t ldw
     }
     if (tiles > 65535)
         return LORA_E_UNSUPPORTED;
+    if (st->n_cu == 0 &&
+        hipDeviceGetAttribute(&st->n_cu, hipDeviceAttributeMultiprocessorCount, st->device) != hipSuccess)
+        st->n_cu = 0;
+    if (st->n_cu < 1)
+        return LORA_E_HIP;
+    a.n_cu = st->n_cu;
     LORA_TRY(launch_merge(st->dtype == LORA_F32 ? DT_F32 : DT_BF16, a,
                           reinterpret_cast<hipStream_t>(stream)));
     return LORA_OK;

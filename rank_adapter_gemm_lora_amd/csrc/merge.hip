@@ -33,7 +33,6 @@ namespace {
 constexpr int kMergeRows = 64;
 constexpr int kMergeCols = 128;
 constexpr int kMergeThreads = 256;
-constexpr int kMergeCus = 256;       // compute units of the part
 constexpr int kMergeWgPerCu = 2;     // persistent bf16 workgroups per compute unit
 // Weights of at least this many 64 x 128 tiles take the persistent kernel
 // (measured: it wins on a 28672 x 4096 weight, 14336 tiles, and loses on a
@@ -463,8 +462,11 @@ hipError_t launch_merge(int dtype, const MergeArgs &a, hipStream_t stream)
         }
         return hipGetLastError();
     }
-    // persistent grid: kMergeWgPerCu workgroups per compute unit, each a run of tiles
-    const dim3 pgrid((unsigned)std::min<int64_t>(tiles, (int64_t)kMergeWgPerCu * kMergeCus));
+    // persistent grid: kMergeWgPerCu workgroups per compute unit of the device,
+    // each a run of tiles
+    if (a.n_cu < 1)
+        return hipErrorInvalidValue;
+    const dim3 pgrid((unsigned)std::min<int64_t>(tiles, (int64_t)kMergeWgPerCu * a.n_cu));
     switch (nkc) {
     case 1: hipLaunchKernelGGL(merge_bf16_stream_kernel<1>, pgrid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL(merge_bf16_stream_kernel<2>, pgrid, block, 0, stream, a); break;
