@@ -24,8 +24,11 @@
 //     operand repeats those 16 B values.  hi + lo carries v to about 16
 //     significant bits, so B v keeps fp32-level accuracy on bf16 inputs.
 //     Inside a wavefront's 64 columns, M-tile mt, index mu is column
-//     16 (mu / 4) + 4 mt + mu % 4, so the accumulators land on the lane's 16
-//     contiguous columns.  The N-tiles (16 rows each) are done one after the
+//     32 (mt / 2) + 8 (mu / 4) + 4 (mt % 2) + mu % 4, so the accumulators of
+//     lane group g land on columns [8 g, 8 g + 8) and [32 + 8 g, 40 + 8 g):
+//     each 16-byte y load or store instruction then covers whole 64-byte
+//     halves of the rows' 128 bytes (with 16 contiguous columns per lane, each
+//     instruction wrote every other 16 bytes of them).  The N-tiles (16 rows each) are done one after the
 //     other with four accumulators, which keeps the register count -- and so
 //     the number of workgroups resident per CU -- where a streaming kernel
 //     needs it.  B sits in LDS as the chunk's contiguous [256 columns][rp]
@@ -39,12 +42,20 @@
 // The tile code and expand_body live in expand_tiles.h (shared with the
 // one-launch kernels); this file holds the expand kernels: expand_kernel (one
 // 256-column chunk per workgroup), expand_kernel_bf16_short (its 16-row bf16
-// instance, built for six waves per SIMD) and expand_stream_kernel (several
-// chunks per workgroup, the next chunk's loads in flight).
+// instance, built for six waves per SIMD), expand_stream_kernel (several
+// chunks of one tile per workgroup, the next chunk's loads in flight) and
+// expand_run_kernel (16-row dense batches: a grid that fits the chip, each
+// workgroup a cost-balanced run of chunks with v prepared once per tile).
+#include <algorithm>
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "device_common.h"
 #include "internal.h"
 #include "mfma.h"
 #include "expand_tiles.h"
+#include "group.h"
 
 namespace lora {
 
@@ -73,6 +84,7 @@ __device__ void sgmv_expand_stream(const ApplyArgs &a, const int32_t *rows, int 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, m = lane & 15;
     const int rp = (r + 7) & ~7, nj = (r + 15) >> 4, ng = rp >> 3;
+    vs = static_cast<float *>(__builtin_assume_aligned(vs, 16));   // 16-byte operand reads
     const bool row_ok = m < cnt;
     const int64_t yrow = (int64_t)rows[min(m, cnt - 1)] * a.ldy;
     const int64_t bslot = (int64_t)s * a.b_slot_stride;
@@ -80,7 +92,7 @@ __device__ void sgmv_expand_stream(const ApplyArgs &a, const int32_t *rows, int 
     int bcolumn[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
-        bcolumn[mt] = 64 * wave + 16 * (m >> 2) + 4 * mt + (m & 3);
+        bcolumn[mt] = 64 * wave + 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
 
     // granules of chunk c's contiguous [ncol][rp] B block
     auto n_gran = [&](int c) {
@@ -88,10 +100,10 @@ __device__ void sgmv_expand_stream(const ApplyArgs &a, const int32_t *rows, int 
     };
     auto load_chunk = [&](int c, Vec8<DT_BF16> &ya, Vec8<DT_BF16> &yb, uint4 (&bg)[NG]) {
         const int64_t c0 = (int64_t)(ch0 + c) * kCols;
-        const int64_t cb = c0 + 64 * wave + 16 * g;
+        const int64_t cb = c0 + 64 * wave + 8 * g;   // lane's columns: [cb, cb + 8), [cb + 32, cb + 40)
         if (row_ok && cb < a.D) {
             ya.load(a.y, yrow + cb);
-            yb.load(a.y, yrow + cb + 8);
+            yb.load(a.y, yrow + cb + kHalf);
         }
         const int ngr = n_gran(c);
         const int64_t b0 = bslot + c0 * rp;
@@ -113,7 +125,7 @@ __device__ void sgmv_expand_stream(const ApplyArgs &a, const int32_t *rows, int 
     };
     auto compute = [&](int c, const Vec8<DT_BF16> &ya, const Vec8<DT_BF16> &yb) {
         const int64_t c0 = (int64_t)(ch0 + c) * kCols;
-        const int64_t cb = c0 + 64 * wave + 16 * g;
+        const int64_t cb = c0 + 64 * wave + 8 * g;
         if (c0 + 64 * wave >= a.D)
             return;   // (uniform per wavefront: D is whole 64-column blocks)
         const int qq = slice_of(a, c0 + 64 * wave);
@@ -123,27 +135,18 @@ __device__ void sgmv_expand_stream(const ApplyArgs &a, const int32_t *rows, int 
             acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int jc = 0; jc < nj; ++jc) {
             const int jo = jc * 16 + 8 * (g & 1);
-            // 8 ranks of row m: two 16-byte reads (ranks past r masked)
-            const float4 *vr = reinterpret_cast<const float4 *>(vs + m * P + qq * rp + jo);
-            const float4 va = vr[0], vb = vr[1];
-            const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-            float f[8];
+            // the four B operands read together (clamped address, selected
+            // after), ahead of v's reads
+            const bool bok = jo < rp;
+            const int bo = min(jo, rp - 8);
+            uint4 bop[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float v = (row_ok && jo + i < r) ? vv[i] : 0.f;
-                f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
-            }
-            uint4 vop;
-            vop.x = pack_bf16x2(f[0], f[1]);
-            vop.y = pack_bf16x2(f[2], f[3]);
-            vop.z = pack_bf16x2(f[4], f[5]);
-            vop.w = pack_bf16x2(f[6], f[7]);
+            for (int mt = 0; mt < 4; ++mt)
+                bop[mt] = *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * rp + bo);
+            const uint4 vop = v_operand(vs + m * P + qq * rp + jo, row_ok, r - jo, g >= 2);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const uint4 bop = jo < rp ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * rp + jo)
-                                          : make_uint4(0, 0, 0, 0);
-                acc[mt] = mfma_bf16_16x16x32(bop, vop, acc[mt]);
-            }
+            for (int mt = 0; mt < 4; ++mt)
+                acc[mt] = mfma_bf16_16x16x32(keep_if(bok, bop[mt]), vop, acc[mt]);
         }
         if (row_ok) {
             float f[16];
@@ -152,7 +155,7 @@ __device__ void sgmv_expand_stream(const ApplyArgs &a, const int32_t *rows, int 
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     f[4 * mt + i] = acc[mt][i];
-            merge16<DT_BF16>(a, yrow + cb, true, true, ya, yb, scale, f);
+            merge16<DT_BF16>(a, yrow + cb, true, true, ya, yb, scale, f, kHalf);
         }
     };
     // chunk c from (cy, cz) while chunk c + 1 loads into (ny, nz)
@@ -248,6 +251,273 @@ void expand_kernel_bf16_short(ApplyArgs a)
     expand_body<DT_BF16, 1, false>(a, blockIdx.y, blockIdx.x);
 }
 
+// ------------------------------------------------ SGMV, runs of chunks
+
+// The one-chunk expand's work (16-row MFMA tiles, every group dense) on a grid
+// that fits the chip at once, organised so that v is prepared once per tile
+// rather than once per 256-column chunk.  The units of work are the (tile,
+// chunk) pairs in tile-major order; workgroup w takes the contiguous run of
+// units whose cumulative cost at their start lies in [w T / G, (w + 1) T / G)
+// (T the total, G the grid), so a run crosses few tiles and all runs take
+// about the same time.  A unit's cost is a fixed share (its round trips:
+// measured per-unit times are mostly fixed) plus its y and B bytes; every
+// workgroup computes the costs and their prefix sums itself, in LDS, from the
+// tile headers.  For each tile of its run the workgroup stages the tile's v (the
+// k-split partials summed in split order, every slice) in LDS once, with the
+// first chunk's y and B loads in flight (only the slices the run touches);
+// each wavefront turns its slice's v
+// into the bf16 hi / lo MFMA operands in registers, and the chunks then only
+// stream B (LDS) and y (registers).  The arithmetic is the one-chunk kernel's
+// (same operands, same order), so the results are bit-identical to it.
+//
+// Dynamic LDS (offsets from the host): the slot table, v of the current tile
+// (the slices the run touches), one B chunk [256][rp], and the unit costs and
+// their prefix sums (2 tile_bound + 1 ints).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void expand_run_kernel(ApplyArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    int32_t *srank = reinterpret_cast<int32_t *>(lds + kExpandLdsTable);
+    float *sscale = reinterpret_cast<float *>(lds + kExpandLdsTable + 4 * kExpandTableSlots);
+    float *vs = reinterpret_cast<float *>(lds + a.lds_v_off);
+    uint16_t *bs = reinterpret_cast<uint16_t *>(lds + a.lds_b_off);
+    int32_t *cost = reinterpret_cast<int32_t *>(lds + a.lds_order_off);   // [tile_bound]
+    int32_t *cum = cost + a.tile_bound;                                   // [tile_bound + 1]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, m = lane & 15;
+    const int n_chunks = (int)((a.D + kCols - 1) / kCols);
+
+    // the batch's tile count, the slot table, every tile's (slot, rows) and
+    // the record of unit blockIdx.x (this workgroup's unit when every unit
+    // has its own workgroup), in one round trip (headers past the batch's
+    // tiles are read in bounds, unused)
+    const int t_first = (int)blockIdx.x / n_chunks;   // < tile_bound: the grid is at most the units' bound
+    const int4 h_first = *reinterpret_cast<const int4 *>(a.tiles + t_first);
+    const int32_t row_first = a.tiles[t_first].rows[m];
+    const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
+    int2 th[kRunHeadersPerThread];
+#pragma unroll
+    for (int i = 0; i < kRunHeadersPerThread; ++i) {
+        const int t = tid + i * 256;
+        const int4 hd = t < a.tile_bound ? *reinterpret_cast<const int4 *>(a.tiles + t)
+                                         : make_int4(0, 0, 0, 0);
+        th[i] = make_int2(hd.x, hd.z);
+    }
+    for (int e = tid; e < a.n_slots; e += blockDim.x) {
+        srank[e] = a.rank[e];
+        sscale[e] = a.scale[e];
+    }
+    lds_barrier();
+    const int n_units = n_tiles * n_chunks;
+    int u = (int)blockIdx.x, u_end = min(u + 1, n_units);   // one unit each, when they all fit
+    if (n_units > (int)gridDim.x) {   // (uniform)
+        // cost of one unit of each tile, in 64-byte units: a fixed share for
+        // the unit's round trips and work (measured: about 50 KB worth), y
+        // read and written (16 per row) and the B chunk (8 per rank)
+#pragma unroll
+        for (int i = 0; i < kRunHeadersPerThread; ++i) {
+            const int t = tid + i * 256;
+            if (t < n_tiles)
+                cost[t] = kRunUnitFixed + 16 * th[i].y + 8 * ((srank[th[i].x] + 7) & ~7);
+        }
+        lds_barrier();
+        // cum[t]: cost of all units of tiles 0 .. t - 1 (wavefront 0)
+        if (wave == 0) {
+            int carry = 0;
+            for (int t0 = 0; t0 < n_tiles; t0 += 64) {
+                const int t = t0 + lane;
+                const int inc = wave_scan_dpp(t < n_tiles ? cost[t] * n_chunks : 0);
+                if (t < n_tiles)
+                    cum[t + 1] = carry + inc;
+                carry += __builtin_amdgcn_readlane(inc, 63);
+            }
+            if (lane == 0)
+                cum[0] = 0;
+        }
+        lds_barrier();
+        // this workgroup's run: the units whose cumulative cost at their
+        // start lies in [w T / G, (w + 1) T / G)
+        const uint32_t total = (uint32_t)cum[n_tiles];
+        auto units_below = [&](uint64_t x) -> int {   // units starting below cost x
+            if (x >= total)
+                return n_units;
+            int lo = 0, hi = n_tiles;   // cum[lo] <= x < cum[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if ((uint32_t)cum[mid] <= x)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            const uint32_t c = (uint32_t)cost[lo];
+            return lo * n_chunks + (int)(((uint32_t)x - (uint32_t)cum[lo] + c - 1) / c);
+        };
+        u = units_below((uint64_t)blockIdx.x * total / gridDim.x);
+        u_end = units_below((uint64_t)(blockIdx.x + 1) * total / gridDim.x);
+    }
+    int bcolumn[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+        bcolumn[mt] = 64 * wave + 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
+
+    while (u < u_end) {
+        // the chunks [c_begin, c_end) of one tile
+        const int t = u / n_chunks, c_begin = u - t * n_chunks;
+        const int c_end = min(n_chunks, c_begin + (u_end - u));
+        u += c_end - c_begin;
+        int4 h = h_first;
+        int32_t my_row = row_first;
+        if (t != t_first) {   // (uniform)
+            h = *reinterpret_cast<const int4 *>(a.tiles + t);
+            my_row = a.tiles[t].rows[m];
+        }
+        lds_barrier();   // the slot table (first tile); the last tile's LDS reads are done
+        const int s = h.x, p0 = h.y, cnt = h.z;
+        const int r = srank[s];
+        const float scale = sscale[s];
+        if (r == 0)
+            continue;   // (uniform) slot emptied since the grouping was built: rows stay untouched
+        const int rp = (r + 7) & ~7, nj = (r + 15) >> 4;
+        const bool half_last = (rp & 15) != 0;   // the last 16-rank step holds 8 ranks
+        // the slices the run's chunks touch
+        const int q_lo = slice_of(a, (int64_t)c_begin * kCols);
+        const int nq = slice_of(a, min((int64_t)c_end * kCols, a.D) - 1) - q_lo + 1;
+        const int P = v_pitch(nq, rp);
+        const bool row_ok = m < cnt;
+        const int64_t yrow = (int64_t)(row_ok ? my_row : __shfl(my_row, 0)) * a.ldy;
+        const int64_t bslot = (int64_t)s * a.b_slot_stride;
+        int cur_q = -1;
+        uint4 vop[4];
+#pragma unroll
+        for (int jc = 0; jc < 4; ++jc)
+            vop[jc] = make_uint4(0, 0, 0, 0);
+        for (int c = c_begin; c < c_end; ++c) {
+            const int64_t c0 = (int64_t)c * kCols;
+            const int64_t cw = c0 + 64 * wave;        // this wavefront's 64 columns
+            const bool in_d = cw < a.D;               // (uniform per wavefront: whole 64-column blocks)
+            const int64_t cb = cw + 8 * g;            // lane's columns [cb, cb + 8), [cb + 32, cb + 40)
+            Vec8<DT_BF16> y0, y1;
+            if (in_d) {
+                y0.load(a.y, yrow + cb);
+                y1.load(a.y, yrow + cb + kHalf);
+            }
+            // the chunk's contiguous [ncol][rp] B block, global -> LDS, 16 bytes a lane
+            {
+                const int gpw = rp >> 3;
+                const int n_gran = (int)min((int64_t)kCols, a.D - c0) * gpw;
+                const uint16_t *src = static_cast<const uint16_t *>(a.B) + bslot + c0 * rp;
+                for (int i = 0; i < gpw; ++i) {
+                    const int e = i * kCols + tid;
+                    if (e < n_gran)
+                        __builtin_amdgcn_global_load_lds(
+                            (const __attribute__((address_space(1))) void *)(src + 8 * (int64_t)e),
+                            (__attribute__((address_space(3))) void *)(bs + 8 * (i * kCols + 64 * wave)), 16,
+                            0, 0);
+                }
+            }
+            if (c == c_begin) {
+                // v of the tile for those slices, summed over the k-splits in
+                // split order (its loads in flight with the first chunk's)
+                stage_v4(a, p0, cnt, r, q_lo, nq, vs);
+                lds_barrier();
+            }
+            // this wavefront's v operands, rebuilt when its slice changes
+            if (in_d) {
+                const int q = slice_of(a, cw);
+                if (q != cur_q) {
+                    cur_q = q;
+#pragma unroll
+                    for (int jc = 0; jc < 4; ++jc) {
+                        const int jo = jc * 16 + 8 * (g & 1);
+                        if (jc < nj)
+                            vop[jc] = v_operand(vs + m * P + (q - q_lo) * rp + jo, row_ok, r - jo, g >= 2);
+                    }
+                }
+            }
+            __syncthreads();   // the B chunk (and y) landed
+            if (in_d) {
+                f32x4_t acc[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int jc = 0; jc < 4; ++jc) {
+                    if (jc < nj) {
+                        const int jo = jc * 16 + 8 * (g & 1);
+                        const int bo = min(jo, rp - 8);
+                        uint4 bop[4];
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+                            bop[mt] = *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * rp + bo);
+                        // ranks past rp (only in a last step of 8 ranks) read as zero
+                        const bool bok = !(half_last && jc == nj - 1) || jo < rp;
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+                            acc[mt] = mfma_bf16_16x16x32(keep_if(bok, bop[mt]), vop[jc], acc[mt]);
+                    }
+                }
+                if (row_ok) {
+                    float f[16];
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            f[4 * mt + i] = acc[mt][i];
+                    merge16<DT_BF16>(a, yrow + cb, true, true, y0, y1, scale, f, kHalf);
+                }
+            }
+            lds_barrier();   // every wavefront is done with the chunk's B
+        }
+    }
+}
+
+// Workgroups of expand_run_kernel resident per CU at this dynamic LDS size
+// (0 on error), computed once per size.
+int run_occupancy(int lds_bytes)
+{
+    static std::mutex mu;
+    static std::vector<std::pair<int, int>> known;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto &e : known)
+        if (e.first == lds_bytes)
+            return e.second;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, expand_run_kernel, 256, lds_bytes) != hipSuccess)
+        return 0;
+    known.emplace_back(lds_bytes, occ);
+    return occ;
+}
+
+// LDS layout of expand_run_kernel: sets the offsets in b, returns the dynamic
+// LDS bytes.
+int run_layout(ApplyArgs &b, int max_tiles)
+{
+    const int rp_max = (b.r_max + 7) & ~7;
+    b.tile_bound = max_tiles;
+    b.lds_v_off = kExpandLdsTable + 8 * kExpandTableSlots;
+    const int v_bytes = (16 * (b.n_slices * rp_max + 4) * 4 + 15) & ~15;
+    b.lds_b_off = b.lds_v_off + v_bytes;
+    b.lds_order_off = b.lds_b_off + kCols * rp_max * 2;
+    return b.lds_order_off + ((4 * (2 * max_tiles + 1) + 15) & ~15);
+}
+
+// expand_run_kernel serves bf16 batches of 16-row tiles that are all MFMA
+// tiles, with at most 64 ranks (one B chunk in LDS; r_max a multiple of 4 for
+// the 16-byte v staging), a slot table that fits LDS and a tile bound its
+// setup covers, within the LDS budget.
+bool run_fits(const ApplyArgs &a, int max_tiles)
+{
+    if (!a.all_dense || a.n_slots > kExpandTableSlots || a.r_max > 64 || a.r_max % 4 != 0 ||
+        max_tiles > kRunHeadersPerThread * 256)
+        return false;
+    // the cumulative costs stay below 2^31
+    const int64_t n_chunks = (a.D + kCols - 1) / kCols;
+    if (n_chunks * max_tiles * (kRunUnitFixed + 16 * 16 + 8 * 64) >= ((int64_t)1 << 31))
+        return false;
+    ApplyArgs b = a;
+    return run_layout(b, max_tiles) <= kExpandLdsMax;
+}
+
 }  // namespace
 
 hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream)
@@ -282,8 +552,22 @@ hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream
             hipLaunchKernelGGL((expand_kernel<DT_BF16, 4, true>), grid, dim3(256), a.lds_bytes, stream, a);
         else if (tall)
             hipLaunchKernelGGL((expand_kernel<DT_BF16, 4, false>), grid, dim3(256), a.lds_bytes, stream, a);
-        else
+        else if (!run_fits(a, max_tiles))
             hipLaunchKernelGGL(expand_kernel_bf16_short, grid, dim3(256), a.lds_bytes, stream, a);
+        else {
+            // as many workgroups as are resident at once (a multiple of 8), at
+            // most one per unit of the tile bound
+            ApplyArgs b = a;
+            const int lds = run_layout(b, max_tiles);
+            const int occ = run_occupancy(lds);
+            if (occ < 1 || a.n_cu < 1)
+                return hipErrorInvalidConfiguration;
+            const int64_t units = (int64_t)grid.x * max_tiles;
+            int64_t g = std::min<int64_t>(units, (int64_t)occ * a.n_cu);
+            if (g >= 8)
+                g &= ~(int64_t)7;
+            hipLaunchKernelGGL(expand_run_kernel, dim3((unsigned)g), dim3(256), lds, stream, b);
+        }
     } else {
         hipLaunchKernelGGL((expand_kernel<DT_F32, 1, false>), grid, dim3(256), a.lds_bytes, stream, a);
     }

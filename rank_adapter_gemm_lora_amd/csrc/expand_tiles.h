@@ -34,6 +34,8 @@ struct KeepAll {
 };
 
 constexpr int kCols = kExpandCols;
+// MFMA expand: a lane's second 8 columns start kHalf columns after its first
+constexpr int kHalf = 32;
 
 __device__ __forceinline__ int slice_of(const ApplyArgs &a, int64_t c)
 {
@@ -127,6 +129,71 @@ __device__ __forceinline__ void stage_v_ks(const ApplyArgs &a, int p0, int cnt, 
     }
 }
 
+// stage_v_ks for stacks whose r_max is a multiple of 4 (so every 4-rank
+// group of a partial row is 16-byte aligned and inside its slice): thread t
+// takes 4-rank groups t, t + 256, ... of the tile's rows x slices, loads the
+// group of every split at once (one 16-byte load per split) and sums them in
+// split order -- the same sums as stage_v_ks, in one round trip for up to 256
+// groups (16 rows of rank 64 in one slice).  Ranks r .. round_up(r, 4) of the
+// staged rows hold whatever the partials hold there (never used: the operands
+// mask ranks past r).
+template <int KS>
+__device__ __forceinline__ void stage_v4_ks(const ApplyArgs &a, int p0, int cnt, int r, int q_lo,
+                                            int nq, float *vs)
+{
+    const int g4 = (r + 3) >> 2, per_row = nq * g4, total = cnt * per_row;
+    const int SR = a.n_slices * a.r_max;
+    const int rp8 = (r + 7) & ~7, P = v_pitch(nq, rp8);
+    const int64_t split = a.max_rows * (int64_t)SR;   // floats of one split
+    const uint32_t m_row = div_magic(per_row), m_g4 = div_magic(g4);   // total <= 2^14
+    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+        const int u = div_small(idx, m_row);
+        const int rem = idx - u * per_row;
+        const int qq = div_small(rem, m_g4);
+        const int k = rem - qq * g4;
+        // (a 32-bit offset from a per-split base, so each load takes its base
+        // from scalar registers)
+        const uint32_t off = (uint32_t)((p0 + u) * SR + (q_lo + qq) * a.r_max + 4 * k);
+        // batches of at most 8 splits (16 splits: two round trips), summed in
+        // split order
+        constexpr int kL = KS < 8 ? KS : 8;
+        float4 sum;
+#pragma unroll
+        for (int k0 = 0; k0 < KS; k0 += kL) {
+            float4 part[kL];
+#pragma unroll
+            for (int kk = 0; kk < kL; ++kk)
+                part[kk] = *reinterpret_cast<const float4 *>(a.vpart + (k0 + kk) * split + off);
+#pragma unroll
+            for (int kk = 0; kk < kL; ++kk) {
+                if (k0 + kk == 0) {
+                    sum = part[0];
+                } else {
+                    sum.x += part[kk].x;
+                    sum.y += part[kk].y;
+                    sum.z += part[kk].z;
+                    sum.w += part[kk].w;
+                }
+            }
+        }
+        *reinterpret_cast<float4 *>(vs + u * P + qq * rp8 + 4 * k) = sum;
+    }
+}
+
+// stage_v_ks by 4-rank groups (r_max a multiple of 4), for kernels with the
+// registers to hold a group of 8 splits in flight.
+__device__ __forceinline__ void stage_v4(const ApplyArgs &a, int p0, int cnt, int r, int q_lo, int nq,
+                                         float *vs)
+{
+    switch (a.ks) {
+    case 1: stage_v4_ks<1>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 2: stage_v4_ks<2>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 4: stage_v4_ks<4>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 8: stage_v4_ks<8>(a, p0, cnt, r, q_lo, nq, vs); break;
+    default: stage_v4_ks<16>(a, p0, cnt, r, q_lo, nq, vs); break;
+    }
+}
+
 template <bool COH = false>
 __device__ __forceinline__ void stage_v(const ApplyArgs &a, int p0, int cnt, int r, int q_lo,
                                         int nq, float *vs)
@@ -140,10 +207,36 @@ __device__ __forceinline__ void stage_v(const ApplyArgs &a, int p0, int cnt, int
     }
 }
 
+// The expand's MFMA operand of v for one lane: 8 ranks of one row, read from
+// LDS at vr (16-byte aligned) as two 16-byte reads, as bf16 hi parts (lo_half
+// false) or the bf16 parts of the rounding residuals (true).  Ranks at or past
+// n_valid (the rank minus the operand's first rank) and every rank of a row
+// past the tile give 0: the mask is applied to the packed words, so the reads
+// carry no condition (a select on each loaded value had the compiler split
+// them into single-float reads, one behind a branch).
+__device__ __forceinline__ uint4 v_operand(const float *vr, bool row_ok, int n_valid, bool lo_half)
+{
+    const float4 va = reinterpret_cast<const float4 *>(vr)[0];
+    const float4 vb = reinterpret_cast<const float4 *>(vr)[1];
+    const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t hi, lo;
+        split_pair(vv[2 * p], vv[2 * p + 1], hi, lo);
+        const uint32_t mask = ((row_ok & (2 * p < n_valid)) ? 0x0000ffffu : 0u) |
+                              ((row_ok & (2 * p + 1 < n_valid)) ? 0xffff0000u : 0u);
+        w[p] = (lo_half ? lo : hi) & mask;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// y at yi (8 columns, acc[0..7]) and yi + off1 (8 columns, acc[8..15]) +=
+// scale * acc, rounded once.
 template <int DT>
 __device__ __forceinline__ void merge16(const ApplyArgs &a, int64_t yi, bool h0, bool h1,
                                         const Vec8<DT> &y0, const Vec8<DT> &y1, float scale,
-                                        const float (&acc)[16])
+                                        const float (&acc)[16], int off1 = 8)
 {
     if (h0) {
         float f[8];
@@ -159,7 +252,7 @@ __device__ __forceinline__ void merge16(const ApplyArgs &a, int64_t yi, bool h0,
 #pragma unroll
         for (int c = 0; c < 8; ++c)
             f[c] = fmaf(scale, acc[8 + c], f[c]);
-        Vec8<DT>::store(a.y, yi + 8, f);
+        Vec8<DT>::store(a.y, yi + off1, f);
     }
 }
 
@@ -177,9 +270,15 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, m = lane & 15;
     const int n_nt = (cnt + 15) >> 4;
-    const int64_t cb = c0 + 64 * wave + 16 * g;      // lane's 16 columns
+    // lane's 16 columns: [cb, cb + 8) and [cb + 32, cb + 40), so that each
+    // 16-byte load or store of a row covers one contiguous 64-byte half of the
+    // wavefront's 128 bytes of that row
+    const int64_t cb = c0 + 64 * wave + 8 * g;
     const bool in_d = cb < a.D;                      // whole 64-column blocks (slices % 64 == 0)
     const int rp = (r + 7) & ~7, nj = (r + 15) >> 4;
+    // the host places v at a 16-byte boundary, and every operand read below
+    // starts at a multiple of 4 floats: 16-byte LDS reads
+    vs = static_cast<float *>(__builtin_assume_aligned(vs, 16));
 
     // y of this lane's rows
     Vec8<DT_BF16> y0[MT], y1[MT];
@@ -189,7 +288,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
         if (nt < n_nt && u < cnt && in_d) {
             const int64_t yi = (int64_t)rows[u] * a.ldy + cb;
             y0[nt].load(a.y, yi);
-            y1[nt].load(a.y, yi + 8);
+            y1[nt].load(a.y, yi + kHalf);
         }
     }
     // the B chunk: columns [c0, c0 + 256) of the slot, ranks [w0, w0 + wl) of
@@ -234,7 +333,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     int bcolumn[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
-        bcolumn[mt] = 64 * wave + 16 * (m >> 2) + 4 * mt + (m & 3);
+        bcolumn[mt] = 64 * wave + 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
 
     if constexpr (WO) {
         // windows outer, N-tiles inner: B is staged once per window, every N-tile's
@@ -261,28 +360,20 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                 const int u = 16 * nt + m;
                 for (int jc = w0 >> 4; jc < min(nj, (w0 + wl + 15) >> 4); ++jc) {
                     const int jo = jc * 16 + 8 * (g & 1);
-                    // 8 ranks of row u: two 16-byte reads (ranks past r masked)
-                    const float4 *vr = reinterpret_cast<const float4 *>(vs + u * P + qq * rp + jo);
-                    const float4 va = vr[0], vb = vr[1];
-                    const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-                    float f[8];
+                    // the four B operands read together from a clamped in-window
+                    // address (ranks past the window selected to zero afterwards),
+                    // so the reads overlap instead of each waiting behind a branch,
+                    // and ahead of v's reads
+                    const bool bok = jo < w0 + wl;
+                    const int bo = min(jo - w0, wl - 8);
+                    uint4 bop[4];
     #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float v = (u < cnt && jo + i < r) ? vv[i] : 0.f;
-                        f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
-                    }
-                    uint4 vop;
-                    vop.x = pack_bf16x2(f[0], f[1]);
-                    vop.y = pack_bf16x2(f[2], f[3]);
-                    vop.z = pack_bf16x2(f[4], f[5]);
-                    vop.w = pack_bf16x2(f[6], f[7]);
+                    for (int mt = 0; mt < 4; ++mt)
+                        bop[mt] = *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + bo);
+                    const uint4 vop = v_operand(vs + u * P + qq * rp + jo, u < cnt, r - jo, g >= 2);
     #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        const uint4 bop = jo < w0 + wl
-                                              ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + (jo - w0))
-                                              : make_uint4(0, 0, 0, 0);
-                        acc[nt][mt] = mfma_bf16_16x16x32(bop, vop, acc[nt][mt]);
-                    }
+                    for (int mt = 0; mt < 4; ++mt)
+                        acc[nt][mt] = mfma_bf16_16x16x32(keep_if(bok, bop[mt]), vop, acc[nt][mt]);
                 }
             }
         }
@@ -298,7 +389,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                         for (int i = 0; i < 4; ++i)
                             f[4 * mt + i] = acc[nt][mt][i];
                     merge16<DT_BF16>(a, (int64_t)rows[u] * a.ldy + cb, true, true, y0[nt], y1[nt], scale,
-                                     f);
+                                     f, kHalf);
                 }
             }
         }
@@ -326,28 +417,17 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                     continue;
                 for (int jc = w0 >> 4; jc < min(nj, (w0 + wl + 15) >> 4); ++jc) {
                     const int jo = jc * 16 + 8 * (g & 1);
-                    // 8 ranks of row u: two 16-byte reads (ranks past r masked)
-                    const float4 *vr = reinterpret_cast<const float4 *>(vs + u * P + qq * rp + jo);
-                    const float4 va = vr[0], vb = vr[1];
-                    const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-                    float f[8];
+                    // B operands as in the window-outer order above
+                    const bool bok = jo < w0 + wl;
+                    const int bo = min(jo - w0, wl - 8);
+                    uint4 bop[4];
     #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float v = (u < cnt && jo + i < r) ? vv[i] : 0.f;
-                        f[i] = (g < 2) ? v : v - bf16_lo(pack_bf16x2(v, 0.f));
-                    }
-                    uint4 vop;
-                    vop.x = pack_bf16x2(f[0], f[1]);
-                    vop.y = pack_bf16x2(f[2], f[3]);
-                    vop.z = pack_bf16x2(f[4], f[5]);
-                    vop.w = pack_bf16x2(f[6], f[7]);
+                    for (int mt = 0; mt < 4; ++mt)
+                        bop[mt] = *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + bo);
+                    const uint4 vop = v_operand(vs + u * P + qq * rp + jo, u < cnt, r - jo, g >= 2);
     #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        const uint4 bop = jo < w0 + wl
-                                              ? *reinterpret_cast<const uint4 *>(bs + bcolumn[mt] * wl + (jo - w0))
-                                              : make_uint4(0, 0, 0, 0);
-                        acc[mt] = mfma_bf16_16x16x32(bop, vop, acc[mt]);
-                    }
+                    for (int mt = 0; mt < 4; ++mt)
+                        acc[mt] = mfma_bf16_16x16x32(keep_if(bok, bop[mt]), vop, acc[mt]);
                 }
             }
             if (in_d && u < cnt && keep) {
@@ -358,7 +438,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
                     for (int i = 0; i < 4; ++i)
                         f[4 * mt + i] = acc[mt][i];
                 merge16<DT_BF16>(a, (int64_t)rows[u] * a.ldy + cb, true, true, y0[nt], y1[nt], scale,
-                                 f);
+                                 f, kHalf);
             }
         }
     }

@@ -90,6 +90,10 @@ struct ApplyArgs {
     int cpw;                   // expand: 256-column chunks per workgroup (1: one chunk)
     int32_t *sync;             // one-launch apply: timeouts, per-tile flags and counters
     int wait_limit;            // one-launch apply: polls before a wait gives up
+    int n_cu;                  // compute units of the device (persistent grids)
+    int all_dense;             // every tile of the batch is an MFMA (SGMV) tile
+    int tile_bound;            // run expand: tile bound of the launch
+    int lds_order_off;         // run expand: dynamic LDS byte offset of the unit costs
     // batch
     const int32_t *counts;
     const ShrinkTile *tiles;
@@ -110,6 +114,10 @@ hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream
 // workgroup); a.sync: kSyncFlags + max_tiles * kSyncTileInts ints, zeroed at
 // creation (per tile: the split flags, then the expand workgroups' counter)
 constexpr int kSyncTimeouts = 2, kSyncFlags = 16, kSyncTileInts = 32;
+// run expand: tile headers each thread reads (tile bounds up to 512), and a
+// unit's fixed cost in 64-byte units
+constexpr int kRunHeadersPerThread = 2;
+constexpr int kRunUnitFixed = 800;
 static_assert(kSyncTileInts > kMaxKSplit, "a tile's flags and counter");
 hipError_t launch_build_apply(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
                               hipStream_t stream);
@@ -280,6 +288,7 @@ struct lora_segments {
     int4 *binfo;
     // state of the last build
     int built;
+    int built_dense_min; // dense_min the tiles were cut with
     int64_t n_rows;
     int n_slots;
 };

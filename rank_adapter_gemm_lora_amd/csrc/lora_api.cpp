@@ -259,6 +259,11 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     a.tiles = seg->tiles;
     a.sync = seg->sync;
     a.wait_limit = seg->wait_limit;
+    if (st->n_cu == 0 &&
+        hipDeviceGetAttribute(&st->n_cu, hipDeviceAttributeMultiprocessorCount, st->device) != hipSuccess)
+        st->n_cu = 0;
+    a.n_cu = st->n_cu;
+    a.all_dense = a.mfma_ok && seg->built_dense_min <= 1 ? 1 : 0;
     return a;
 }
 
@@ -627,6 +632,7 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
                           : 0;
     seg->wait_limit = kWaitSpinsDefault;
     seg->built = 0;
+    seg->built_dense_min = 1;
     seg->n_rows = 0;
     seg->n_slots = 0;
     hipError_t e = hipSuccess;
@@ -730,6 +736,7 @@ SegBuildArgs make_seg_args(const lora_stack *st, const int32_t *ids, int64_t n_r
 void mark_built(lora_segments *seg, const lora_stack *st, int64_t n_rows)
 {
     seg->built = 1;
+    seg->built_dense_min = seg->dense_min;
     seg->n_rows = n_rows;
     seg->n_slots = st->n_slots;
 }
