@@ -802,7 +802,8 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, copy_mb, wor
              "build_shrink": ("build_shrink_kernel",),
              "build_apply": ("decode_kernel", "build_apply_kernel"),
              "apply": ("apply_kernel",),
-             "expand": ("expand_kernel", "expand_kernel_bf16_short", "expand_stream_kernel")}
+             "expand": ("expand_kernel", "expand_kernel_bf16_short", "expand_stream_kernel",
+                        "expand_run_kernel")}
 
     def bare(kname):
         head = kname.replace("(anonymous namespace)", "").split("(")[0].split("<")[0]
