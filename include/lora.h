@@ -305,21 +305,28 @@ lora_status lora_build_shrink(const lora_stack *st, const void *x, int64_t ldx,
  * lora_build_shrink followed by lora_add_expand: one call for a whole batch
  * (grouping, add_shrink, add_expand with the per-row merge), with the results
  * and segments of lora_build_segments + lora_apply (y bit-identical: the same
- * tile code on the same tile plan).  Decode-sized batches (those the fused
- * grouping serves, on 16-row tiles with one column chunk per expand
- * workgroup, whose grid of (k-splits + 256-column chunks) x tile bound is at
- * at most the workgroups the chip holds at once, plus a quarter) run as ONE
- * kernel (lora_build_apply_plan tells which): shrink and expand workgroups both
- * group the ids in LDS, and each expand workgroup waits for the shrink
- * workgroups of its tile through per-tile flags in the segments object
- * (device-coherent stores and loads of v; every launch leaves the flags zero,
- * so captured graphs replay correctly).  A wait that never ends is impossible
- * by construction (an expand workgroup waits only on earlier-dispatched
- * shrink workgroups that wait on nothing); as a guard, a wait bounded at
- * well under a second gives up and is reported by lora_get_device_status.
- * Calls on one segments object must not overlap (the flags are per object).
- * n_rows == 0 only writes the (empty) segments.  Errors: LORA_E_ARG,
- * LORA_E_HIP.
+ * tile arithmetic on the same tile plan).  Decode-sized batches run as ONE
+ * kernel (lora_build_apply_plan tells which):
+ *   - bf16 stacks of one slice with r_max <= 16, <= 63 slots and <= 256 rows
+ *     (the decode batches): every workgroup groups the ids itself, and the
+ *     shrink workgroups hand v to the expand workgroups as tagged 32-bit
+ *     words in the segments object (value and launch tag in one device-scope
+ *     atomic access, per-tile epochs: nothing is cleared between launches);
+ *   - other batches the fused grouping serves on 16-row tiles, whose grid of
+ *     (k-splits + 256-column chunks) x tile bound is at most the workgroups
+ *     the chip holds at once plus a quarter: v stored device-coherent and
+ *     handed over through per-tile flags that the tile's last expand
+ *     workgroup clears.
+ * In both, captured graphs replay correctly for any adapter mix.  A wait that
+ * never ends is impossible by construction (an expand workgroup waits only on
+ * earlier-dispatched shrink workgroups that wait on nothing); as a guard the
+ * waits are bounded (lora_segments_set_wait_limit), a workgroup whose wait
+ * gives up leaves its rows of y untouched, and from then on every one-launch
+ * call on the segments object leaves y untouched until lora_get_device_status
+ * reports the timeout (LORA_E_HIP) and resets the hand-over state.  Other
+ * batches take 2, 3 or 5 launches.  Calls on one segments object must not
+ * overlap (the hand-over state is per object).  n_rows == 0 only writes the
+ * (empty) segments.  Errors: LORA_E_ARG, LORA_E_HIP.
  */
 lora_status lora_build_apply(const lora_stack *st, void *y, int64_t ldy, const void *x,
                              int64_t ldx, const int32_t *ids, int64_t n_rows, lora_segments *seg,
