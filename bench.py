@@ -57,9 +57,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATE_BYTES = 512 << 20       # 2x the 256 MB MALL
 DEFAULT_WORKLOAD = "decode_bgmv"
 KERNEL_SOURCES = ("seg_build.hip", "shrink.hip", "expand.hip", "expand_tiles.h", "group.h",
-                  "mfma.h", "device_common.h", "internal.h")
+                  "mfma.h", "device_common.h", "internal.h", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = KERNEL_SOURCES + ("decode.hip",)
 
 
 def log(msg):

@@ -44,6 +44,19 @@ __device__ __forceinline__ int div_small(int n, uint32_t m)
 // relative change below 2^-22, far inside the output's rounding).
 __device__ __forceinline__ float v_word(float x) { return __uint_as_float(__float_as_uint(x) & ~1u); }
 
+// Workgroups go to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), each
+// XCD with its own L2.  xcd_major(b, n) numbers the n workgroups of a 1-D grid
+// so that each XCD holds one contiguous range: XCD x gets [x q + min(x, rem),
+// + q + (x < rem)) for n = 8 q + rem.  Work handed out in index order then
+// keeps neighbouring work items (the chunks of one tile, tiles of one slot)
+// in one L2.  A bijection on [0, n) whatever the placement, so only speed
+// depends on the round-robin.
+__device__ __forceinline__ int xcd_major(int b, int n)
+{
+    const int x = b & 7, q = n >> 3, rem = n & 7;
+    return x * q + min(x, rem) + (b >> 3);
+}
+
 // Workgroup barrier that orders LDS only: waits for this wavefront's LDS
 // stores (lgkmcnt), not for its global loads, so loads issued ahead of the
 // barrier stay in flight across it.  __syncthreads() is a full release fence

@@ -288,9 +288,9 @@ void expand_run_kernel(ApplyArgs a)
     const int n_chunks = (int)((a.D + kCols - 1) / kCols);
 
     // the batch's tile count, the slot table, every tile's (slot, rows) and
-    // the record of unit blockIdx.x (this workgroup's unit when every unit
-    // has its own workgroup), in one round trip (headers past the batch's
-    // tiles are read in bounds, unused)
+    // the record of tile blockIdx.x / chunks (a guess at the first tile of
+    // this workgroup's run: reread when wrong), in one round trip (headers
+    // past the batch's tiles are read in bounds, unused)
     const int t_first = (int)blockIdx.x / n_chunks;   // < tile_bound: the grid is at most the units' bound
     const int4 h_first = *reinterpret_cast<const int4 *>(a.tiles + t_first);
     const int32_t row_first = a.tiles[t_first].rows[m];
@@ -309,7 +309,15 @@ void expand_run_kernel(ApplyArgs a)
     }
     lds_barrier();
     const int n_units = n_tiles * n_chunks;
-    int u = (int)blockIdx.x, u_end = min(u + 1, n_units);   // one unit each, when they all fit
+    // one unit each when they all fit: numbered XCD-major over ceil(units / 8)
+    // workgroups per XCD, so each XCD takes one contiguous stretch of units
+    // (a tile's chunks and the tiles of a slot share an L2); the rest idle
+    int u, u_end;
+    {
+        const int per = (n_units + 7) >> 3, j = (int)blockIdx.x >> 3;
+        u = j < per ? min(((int)blockIdx.x & 7) * per + j, n_units) : n_units;
+        u_end = min(u + 1, n_units);
+    }
     if (n_units > (int)gridDim.x) {   // (uniform)
         // cost of one unit of each tile, in 64-byte units: a fixed share for
         // the unit's round trips and work (measured: about 50 KB worth), y
@@ -336,8 +344,12 @@ void expand_run_kernel(ApplyArgs a)
         }
         lds_barrier();
         // this workgroup's run: the units whose cumulative cost at their
-        // start lies in [w T / G, (w + 1) T / G)
+        // start lies in [w T / G, (w + 1) T / G), with w numbered XCD-major so
+        // that the runs of one XCD are one contiguous stretch of tiles: a
+        // tile's v partials and the B chunks its slot's tiles share are then
+        // read into one L2
         const uint32_t total = (uint32_t)cum[n_tiles];
+        const int w = xcd_major((int)blockIdx.x, (int)gridDim.x);
         auto units_below = [&](uint64_t x) -> int {   // units starting below cost x
             if (x >= total)
                 return n_units;
@@ -352,8 +364,8 @@ void expand_run_kernel(ApplyArgs a)
             const uint32_t c = (uint32_t)cost[lo];
             return lo * n_chunks + (int)(((uint32_t)x - (uint32_t)cum[lo] + c - 1) / c);
         };
-        u = units_below((uint64_t)blockIdx.x * total / gridDim.x);
-        u_end = units_below((uint64_t)(blockIdx.x + 1) * total / gridDim.x);
+        u = units_below((uint64_t)w * total / gridDim.x);
+        u_end = units_below((uint64_t)(w + 1) * total / gridDim.x);
     }
     int bcolumn[4];
 #pragma unroll

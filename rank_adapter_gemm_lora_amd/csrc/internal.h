@@ -129,7 +129,7 @@ hipError_t launch_apply(int dtype, const ApplyArgs &a, int max_tiles, hipStream_
 int apply_wgs_per_cu(int dtype, int lds_bytes);
 // One-launch decode (decode.hip): grouping, shrink and expand of a batch of at
 // most kDecodeMaxRows rows over at most kDecodeMaxSlots slots (bf16, one
-// slice, rank <= 16), v handed over as tagged 64-bit words.
+// slice, rank <= 16), v handed over as tagged 32-bit words.
 constexpr int kDecodeMaxRows = 256;
 constexpr int kDecodeMaxSlots = 63;
 constexpr int kDecodeMaxKs = 8;
