@@ -123,6 +123,9 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
     }
 }
 
+// 16 zero bytes: the source of operand granules that lie outside the data.
+__device__ const uint4 g_zero_granule = {0u, 0u, 0u, 0u};
+
 // 16-row SGMV tile (batches up to 4096 rows): M = the tile's rows, N = up to
 // kNT N-tiles (slice, 16-rank chunk) per pass over the k-range, K = k; the
 // four wavefronts split the workgroup's k-range and their partial tiles are
@@ -169,16 +172,30 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
         for (int tt = 0; tt < NTV; ++tt)
             acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+        // Granules past the wavefront's k-range (and of dropped N-tiles) are
+        // read from a zero granule: the choice is made on the address, so
+        // no select waits on a loaded value and the next step's loads stay in
+        // flight while this step's products run.
+        // (The address passes through an empty asm statement, opaque to the
+        // optimizer, which would otherwise turn the choice of address back
+        // into a branch around the load or a select of two loaded values.)
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        typedef const __attribute__((address_space(1))) u32x4 *G16;   // global: no flat loads
+        const uint64_t X = (uint64_t)a.x, Ap = (uint64_t)a.A, Z = (uint64_t)&g_zero_granule;
+        auto gload = [](uint64_t addr) {
+            asm("" : "+v"(addr));
+            const u32x4 v = *(G16)addr;
+            return make_uint4(v.x, v.y, v.z, v.w);
+        };
         auto load_step = [&](int64_t u0, uint4 (&xs)[kSt], uint4 (&as)[NTV][kSt]) {
 #pragma unroll
             for (int st = 0; st < kSt; ++st) {
                 const int64_t unit = u0 + 4 * st + g;   // lanes g = 0..3: 64 contiguous bytes of a row
                 const bool ok = unit < we;
-                const int64_t cu = min(unit, g8 - 1);
-                xs[st] = keep_if(ok, load16(a.x, xrow + cu * 8));
+                xs[st] = gload(ok ? X + 2 * (xrow + unit * 8) : Z);
 #pragma unroll
                 for (int tt = 0; tt < NTV; ++tt)
-                    as[tt][st] = keep_if(ok && aok[tt], load16(a.A, arow[tt] + cu * 8));
+                    as[tt][st] = gload(ok && aok[tt] ? Ap + 2 * (arow[tt] + unit * 8) : Z);
             }
         };
         auto mma_step = [&](const uint4 (&xs)[kSt], const uint4 (&as)[NTV][kSt]) {
@@ -188,19 +205,30 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
                 for (int tt = 0; tt < NTV; ++tt)
                     acc[tt] = mfma_bf16_16x16x32(xs[st], as[tt][st], acc[tt]);
         };
+        // Two register buffers, one step of loads in flight behind the
+        // products.  No load sits under a condition inside the loop: where a
+        // load may or may not have been issued, the wait before a product
+        // has to assume it was not, and then waits for the loads in flight
+        // too.  The last one or two steps are peeled off instead.
         const int64_t n_steps = (we - wb + 4 * kSt - 1) / (4 * kSt);
+        constexpr int kStep = 4 * kSt;   // 8-element units per step
         uint4 xa[kSt], aa[NTV][kSt], xb[kSt], ab[NTV][kSt];
-        if (n_steps > 0)
+        if (n_steps > 0) {
             load_step(wb, xa, aa);
-        for (int64_t i = 0; i < n_steps; i += 2) {
-            if (i + 1 < n_steps)
-                load_step(wb + (i + 1) * 4 * kSt, xb, ab);
-            mma_step(xa, aa);
-            if (i + 1 >= n_steps)
-                break;
-            if (i + 2 < n_steps)
-                load_step(wb + (i + 2) * 4 * kSt, xa, aa);
-            mma_step(xb, ab);
+            int64_t i = 0;
+            for (; i + 2 < n_steps; i += 2) {
+                load_step(wb + (i + 1) * kStep, xb, ab);
+                mma_step(xa, aa);
+                load_step(wb + (i + 2) * kStep, xa, aa);
+                mma_step(xb, ab);
+            }
+            if (i + 1 < n_steps) {
+                load_step(wb + (i + 1) * kStep, xb, ab);
+                mma_step(xa, aa);
+                mma_step(xb, ab);
+            } else {
+                mma_step(xa, aa);
+            }
         }
 
         // fixed-order sum of the four k-quarters
@@ -265,7 +293,6 @@ static_assert(kNT * 64 == 256, "one reduction entry per thread");
 constexpr int kTallSlots = 3;
 constexpr int kBlkUnits = 8;   // 8-element k units per block
 
-__device__ const uint4 g_zero_granule = {0u, 0u, 0u, 0u};
 
 // s_waitcnt immediate: vector-memory count <= n and no LDS access outstanding (the
 // reads of a slot are done before a copy may overwrite it); exports not waited on.
