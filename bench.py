@@ -580,6 +580,9 @@ def bench_sweep(steps, warmup, out=None, md=None) -> list:
                 emit(line, out)
     if md:
         with open(md, "w") as f:
+            f.write("# One q-proj LoRA layer against its base GEMM (MI355X, bf16, HBM-cold rotation)\n\n"
+                    f"Command: `python3 bench.py --sweep --steps {steps} --warmup {warmup} --sweep-md <file>`\n"
+                    "(LoRA step = one lora_build_apply; base = torch's bf16 GEMM of the same shape)\n")
             f.write(sweep_markdown(lines))
     return lines
 

@@ -564,21 +564,27 @@ hipError_t launch_expand(int dtype, const ApplyArgs &a, int max_tiles, hipStream
             hipLaunchKernelGGL((expand_kernel<DT_BF16, 4, true>), grid, dim3(256), a.lds_bytes, stream, a);
         else if (tall)
             hipLaunchKernelGGL((expand_kernel<DT_BF16, 4, false>), grid, dim3(256), a.lds_bytes, stream, a);
-        else if (!run_fits(a, max_tiles))
-            hipLaunchKernelGGL(expand_kernel_bf16_short, grid, dim3(256), a.lds_bytes, stream, a);
         else {
             // as many workgroups as are resident at once (a multiple of 8), at
             // most one per unit of the tile bound
             ApplyArgs b = a;
-            const int lds = run_layout(b, max_tiles);
-            const int occ = run_occupancy(lds);
-            if (occ < 1 || a.n_cu < 1)
-                return hipErrorInvalidConfiguration;
+            const int lds = run_fits(a, max_tiles) ? run_layout(b, max_tiles) : 0;
+            const int occ = lds > 0 ? run_occupancy(lds) : 0;
             const int64_t units = (int64_t)grid.x * max_tiles;
-            int64_t g = std::min<int64_t>(units, (int64_t)occ * a.n_cu);
-            if (g >= 8)
-                g &= ~(int64_t)7;
-            hipLaunchKernelGGL(expand_run_kernel, dim3((unsigned)g), dim3(256), lds, stream, b);
+            const int64_t resident = (int64_t)occ * a.n_cu;
+            // the one-chunk kernel for stacks of rank <= 32, whose v takes at
+            // most two rank steps (measured faster there: q-proj at 256 rows
+            // x 100 adapters, rank 16 13.2 -> 8.0 us, rank 32 14.7 -> 10.7 us;
+            // 4096 rows up to 6 % faster); runs pay from rank 64 (MLP gate/up
+            // 28.4 -> 25.7 us, down 9.5 -> 8.3 us)
+            if (occ < 1 || a.n_cu < 1 || a.r_max <= 32) {
+                hipLaunchKernelGGL(expand_kernel_bf16_short, grid, dim3(256), a.lds_bytes, stream, a);
+            } else {
+                int64_t g = std::min<int64_t>(units, resident);
+                if (g >= 8)
+                    g &= ~(int64_t)7;
+                hipLaunchKernelGGL(expand_run_kernel, dim3((unsigned)g), dim3(256), lds, stream, b);
+            }
         }
     } else {
         hipLaunchKernelGGL((expand_kernel<DT_F32, 1, false>), grid, dim3(256), a.lds_bytes, stream, a);
