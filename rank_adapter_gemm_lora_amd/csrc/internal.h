@@ -178,6 +178,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 int decode_wgs_per_cu(int ks, int cpw);
 // Tiles of one batch never exceed ceil(rows / 16) plus one ragged tile per group.
 int max_tiles_for(int64_t n_rows, int n_slots);
+int grid_tiles(int64_t n_rows, int n_slots, int sgmv_rows, int dense_min);
 int decode_ks(int64_t k);
 bool decode_fits(const lora_stack *st, int64_t n_rows, int cpw, int vt_tiles);
 DecodeArgs decode_args_for(const lora_stack *st, const int32_t *ids, int64_t n_rows, const void *x,
@@ -289,6 +290,7 @@ struct lora_segments {
     // state of the last build
     int built;
     int built_dense_min; // dense_min the tiles were cut with
+    int built_sgmv_rows; // dense tile height the tiles were cut with (16 or 64)
     int64_t n_rows;
     int n_slots;
 };

@@ -234,7 +234,10 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     a.b_slot_stride = st->D * st->rp_max;
     a.vpart = st->vpart;
     a.max_rows = st->max_rows;
-    a.sgmv_rows = sgmv_rows_for(st, seg->n_rows);
+    // the tile height the batch was grouped with (the stack that built the
+    // segments may differ from this one: one grouping per batch serves every
+    // projection)
+    a.sgmv_rows = seg->built ? seg->built_sgmv_rows : sgmv_rows_for(st, seg->n_rows);
     a.ks = choose_ks(st->k, seg->n_rows, a.sgmv_rows);
     a.mfma_ok = stack_has_mfma_path(st) ? 1 : 0;
     // v staging sized for this batch's dense tile height (16 rows up to 4096
@@ -334,6 +337,18 @@ bool lora::y_ok(const lora_stack *st, const void *y, int64_t ldy)
 int lora::max_tiles_for(int64_t n_rows, int n_slots)
 {
     return (int)((n_rows + kBgmvTileRows - 1) / kBgmvTileRows + std::min<int64_t>(n_slots, n_rows));
+}
+
+// Tile bound of the shrink and expand grids of a built batch: with 64-row
+// dense tiles and every group dense (dense_min 1), a group of c rows gives
+// ceil(c / 64) tiles, so the batch at most ceil(n / 64) + (groups) tiles;
+// otherwise groups may be cut into 16-row tiles.  Shapes and the segments
+// object's policy only, never the mix.
+int lora::grid_tiles(int64_t n_rows, int n_slots, int sgmv_rows, int dense_min)
+{
+    if (sgmv_rows == kSgmvTileRows && dense_min <= 1)
+        return (int)((n_rows + kSgmvTileRows - 1) / kSgmvTileRows + std::min<int64_t>(n_slots, n_rows));
+    return max_tiles_for(n_rows, n_slots);
 }
 
 lora_status lora::status_of(hipError_t e) { return from_hip(e); }
@@ -633,6 +648,7 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     seg->wait_limit = kWaitSpinsDefault;
     seg->built = 0;
     seg->built_dense_min = 1;
+    seg->built_sgmv_rows = kBgmvTileRows;
     seg->n_rows = 0;
     seg->n_slots = 0;
     hipError_t e = hipSuccess;
@@ -737,6 +753,7 @@ void mark_built(lora_segments *seg, const lora_stack *st, int64_t n_rows)
 {
     seg->built = 1;
     seg->built_dense_min = seg->dense_min;
+    seg->built_sgmv_rows = sgmv_rows_for(st, n_rows);
     seg->n_rows = n_rows;
     seg->n_slots = st->n_slots;
 }
@@ -886,7 +903,7 @@ lora_status lora_add_shrink(const lora_stack *st, const void *x, int64_t ldx,
     a.x = x;
     a.ldx = ldx;
     LORA_TRY(launch_shrink(st->dtype == LORA_BF16 ? DT_BF16 : DT_F32, a,
-                           max_tiles_for(seg->n_rows, st->n_slots),
+                           grid_tiles(seg->n_rows, st->n_slots, a.sgmv_rows, seg->built_dense_min),
                            reinterpret_cast<hipStream_t>(stream)));
     return LORA_OK;
 }
@@ -905,7 +922,7 @@ lora_status lora_add_expand(const lora_stack *st, void *y, int64_t ldy, const lo
     a.y = y;
     a.ldy = ldy;
     LORA_TRY(launch_expand(st->dtype == LORA_BF16 ? DT_BF16 : DT_F32, a,
-                           max_tiles_for(seg->n_rows, st->n_slots),
+                           grid_tiles(seg->n_rows, st->n_slots, a.sgmv_rows, seg->built_dense_min),
                            reinterpret_cast<hipStream_t>(stream)));
     return LORA_OK;
 }

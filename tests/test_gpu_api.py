@@ -301,3 +301,33 @@ def test_segments_across_builders(n, n_slots):
         tile = 16 if n <= 4096 else 64
         assert ns == int(np.sum((cnt[dense] + tile - 1) // tile))
         assert nb == int(np.sum((cnt[~dense & (cnt > 0)] + 15) // 16))
+
+
+@pytest.mark.parametrize("build_with", ["narrow", "wide"])
+def test_segments_shared_across_stacks(build_with):
+    """One grouping per batch serves every projection (page "LoRA hot-loading
+    and adapter routing", batched multi-adapter execution: the row groups are
+    formed once per batch).  At 2000 rows a rank-8 q-proj stack cuts dense
+    groups into 16-row tiles and a rank-64 stack with a wide output into
+    64-row tiles; segments built with either stack are applied with both, and
+    each result matches the oracle for its own stack (the apply follows the
+    tile height the segments were built with)."""
+    n, n_slots = 2000, 6
+    ids = synth.make_random(7, n_rows=n, k=64, slice_d=[64], n_slots=n_slots,
+                            ranks=[8] * n_slots, r_max=8, p_none=0.1).ids
+    narrow = synth.make_random(11, n_rows=n, k=512, slice_d=[512], n_slots=n_slots,
+                               ranks=[8, 4, 8, 8, 1, 8], r_max=8, ids=ids)
+    wide = synth.make_random(12, n_rows=n, k=512, slice_d=[4608], n_slots=n_slots,
+                             ranks=[64, 32, 16, 64, 8, 40], r_max=64, ids=ids)
+    ra, rb = GpuRun(narrow), GpuRun(wide)
+    try:
+        builder = ra if build_with == "narrow" else rb
+        note(f"shared segments: built with the {build_with} stack")
+        builder.build()
+        for run, p in ((ra, narrow), (rb, wide)):
+            lb.lora_apply(run.stack, run.y.data_ptr(), p.ldy, run.x.data_ptr(), p.ldx, builder.seg,
+                          run.stream)
+            check_against_oracle(p, run.y_host(), what=f"{p.slice_d} on {build_with} segments")
+    finally:
+        ra.close()
+        rb.close()
