@@ -64,6 +64,11 @@ EDGE_CASES = {
     # 64-row dense tiles below 4096 rows: a wide output at r_max >= 32
     "tall_wide_d": dict(n_rows=1100, k=256, slice_d=[8192], n_slots=4, ranks=[32, 16, 8, 32],
                         r_max=32, p_none=0.05),
+    # the run expand (16-row dense tiles, r_max 64) on grids smaller than one
+    # workgroup per XCD: one 256-column chunk, then two
+    "run_one_chunk": dict(n_rows=20, k=64, slice_d=[256], n_slots=2, ranks=[64, 40], r_max=64),
+    "run_two_chunks": dict(n_rows=40, k=128, slice_d=[448, 64], n_slots=3, ranks=[64, 64, 33],
+                           r_max=64, p_none=0.1),
 }
 
 
@@ -331,3 +336,25 @@ def test_segments_shared_across_stacks(build_with):
     finally:
         ra.close()
         rb.close()
+
+
+def test_tall_batch_with_vector_tiles():
+    """Above 4096 rows dense groups take 64-row tiles; with dense_min above the
+    smaller groups' sizes those groups take 16-row vector tiles in the same
+    batch, so the launch grids keep the 16-row tile bound (the 64-row bound
+    holds only when every group is dense)."""
+    n_slots = 6
+    probs = np.array([0.5, 0.3, 0.17, 0.015, 0.01, 0.005])
+    p = synth.make_random(21, n_rows=4500, k=256, slice_d=[256], n_slots=n_slots,
+                          ranks=[16, 8, 16, 4, 16, 8], r_max=16, id_probs=probs, p_none=0.02,
+                          name="tall_mixed")
+    counts = np.bincount(p.ids[p.ids >= 0], minlength=n_slots)
+    dense_min = 200
+    assert (counts >= dense_min).any() and ((counts > 0) & (counts < dense_min)).any(), counts
+    for dt in ("bf16", "f32"):
+        q = p if dt == "bf16" else synth.make_random(21, n_rows=4500, k=256, slice_d=[256],
+                                                     n_slots=n_slots, ranks=[16, 8, 16, 4, 16, 8],
+                                                     r_max=16, id_probs=probs, p_none=0.02,
+                                                     dtype="f32", name="tall_mixed")
+        note(f"tall batch with vector tiles, {dt}")
+        _run_and_check(q, dense_min=dense_min, what=f"tall_mixed/{dt}")
