@@ -921,7 +921,72 @@ def main(argv=None):
         emit({"metric": gu["metric"], "value": round(rows / (ms * 1e-3), 1), "unit": "tokens/s",
               "ms_per_step": round(ms, 5), "config": {"workload": "mlp_layer (gate/up + down)",
                                                       "valid_rows": rows}}, args.out)
+        emit(bench_mlp_layer_one_grouping(args.steps, args.warmup), args.out)
     return 0
+
+
+def bench_mlp_layer_one_grouping(steps: int, warmup: int) -> dict:
+    """One MLP layer as a serving loop runs it: the batch is grouped once
+    (inside the gate/up shrink, lora_build_shrink) and the down projection
+    reuses those segments (page "LoRA hot-loading and adapter routing", batched
+    multi-adapter execution: the groups are formed once per batch).  Per step:
+    lora_build_shrink + lora_add_expand on the gate/up stack, then
+    lora_add_shrink + lora_add_expand on the down stack with the same segments
+    object, over rotating buffer sets of both workloads."""
+    import torch
+    from rank_adapter_gemm_lora_amd import binding as lb
+    from rank_adapter_gemm_lora_amd import synth
+
+    pg, pd = synth.make_workload("mlp_gate_up"), synth.make_workload("mlp_down")
+    assert (pg.ids == pd.ids).all() and pg.n_slots == pd.n_slots and pg.n_rows == pd.n_rows
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)
+    sh = stream.cuda_stream
+
+    def staged(p):
+        raw = (lambda a: a.view(np.int16)) if p.dtype == "bf16" else (lambda a: a)
+        dA = [None if p.ranks[s] == 0 else torch.from_numpy(raw(np.ascontiguousarray(p.A[s]))).to(dev)
+              for s in range(p.n_slots)]
+        dB = [None if p.ranks[s] == 0 else torch.from_numpy(raw(np.ascontiguousarray(p.B[s]))).to(dev)
+              for s in range(p.n_slots)]
+        return dA, dB
+
+    (gA, gB), (dA, dB) = staged(pg), staged(pd)
+    torch.cuda.synchronize()
+    n_sets = max(2, math.ceil(ROTATE_BYTES / (set_bytes(pg) + set_bytes(pd))))
+    with torch.cuda.stream(stream):
+        sets = [(BufferSet(pg, lb, torch, dev, sh, gA, gB, None),
+                 BufferSet(pd, lb, torch, dev, sh, dA, dB, None)) for _ in range(n_sets)]
+    torch.cuda.synchronize()
+    del gA, gB, dA, dB
+
+    def layer(pair):
+        g, d = pair
+        lb.lora_build_shrink(g.stack, g.x.data_ptr(), pg.ldx, g.ids.data_ptr(), pg.n_rows, g.seg, sh)
+        lb.lora_add_expand(g.stack, g.y.data_ptr(), pg.ldy, g.seg, sh)
+        lb.lora_add_shrink(d.stack, d.x.data_ptr(), pd.ldx, g.seg, sh)
+        lb.lora_add_expand(d.stack, d.y.data_ptr(), pd.ldy, g.seg, sh)
+
+    for i in range(warmup):
+        layer(sets[i % n_sets])
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        layer(sets[(warmup + i) % n_sets])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    for g, d in sets:
+        g.close(lb)
+        d.close(lb)
+    rows = int((pg.ids >= 0).sum())
+    return {"metric": "LoRA-applied tokens/s per layer", "value": round(rows / (ms * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(ms, 5), "steps": steps, "warmup": warmup,
+            "config": {"workload": "mlp_layer (gate/up + down, one grouping)", "valid_rows": rows,
+                       "buffer_sets": n_sets}}
 
 
 def emit(line, out):
