@@ -14,6 +14,12 @@ Functions follow the pages:
   id").  Stable counting sort; rows without a valid adapter go last.
 * :func:`apply_rows` -- y_i + (alpha/r) * B_a (A_a x_i) per row, in double
   (Multi-LoRA page, section 2 per-row equation and section 3.1 LoRA math).
+* :func:`apply_grouped` -- the same result computed the way the hot-loading
+  page's batched-execution section runs a batch: the rows are gathered into
+  one group per adapter id, each group's inputs go through the adapter's two
+  factors as whole matrices (numpy matmul in double), and the scaled delta is
+  added into the group's rows of the base output.  A second algorithm for the
+  same quantity, used to pin :func:`apply_rows`.
 """
 from __future__ import annotations
 
@@ -180,4 +186,40 @@ def merge(dtype: str, k: int, slice_d, rank: int, alpha: float, A, B, W, sign: i
                           _ptr(B), _ptr(W), W.shape[1], int(sign), _ptr(out), int(n_threads))
     if rc != 0:
         raise ValueError("oracle_merge: bad argument")
+    return out
+
+
+def apply_grouped(dtype: str, k: int, slice_d, slot_rank, slot_alpha, A, B, ids, x, y_in) -> np.ndarray:
+    """fp64 adapted output of every row, shape [n, D], grouped per adapter.
+
+    Page "LoRA hot-loading and adapter routing", batched multi-adapter
+    execution section: one group of row indices per adapter id in the batch;
+    for each group the inputs are gathered, passed through the adapter's
+    shrink and expand factors, scaled by alpha / r and added into those rows of
+    the base output; rows without an adapter (id -1, or an id naming no loaded
+    adapter) keep the base output.  Arguments as :func:`apply_rows` (bf16 as
+    uint16 bit patterns); x [n, >= k], y_in [n, >= D].
+    """
+    from .compare import to_f64
+    slice_d = [int(d) for d in slice_d]
+    D = sum(slice_d)
+    n = len(ids)
+    xf = to_f64(np.asarray(x)[:, :k], dtype)
+    out = to_f64(np.asarray(y_in)[:, :D], dtype).copy()
+    groups = {}
+    for i in range(n):
+        s = int(ids[i])
+        if 0 <= s < len(slot_rank) and int(slot_rank[s]) > 0:
+            groups.setdefault(s, []).append(i)
+    for s, rows in groups.items():
+        r = int(slot_rank[s])
+        scale = float(slot_alpha[s]) / r
+        a = to_f64(np.asarray(A[s]), dtype).reshape(len(slice_d), r, k)
+        b = to_f64(np.asarray(B[s]), dtype).reshape(D, r)
+        xg = xf[rows]                        # the group's inputs, [n_g, k]
+        off = 0
+        for q, d in enumerate(slice_d):
+            v = xg @ a[q].T                  # shrink: [n_g, r]
+            out[rows, off:off + d] += scale * (v @ b[off:off + d].T)   # expand, scaled
+            off += d
     return out

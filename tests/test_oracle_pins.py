@@ -15,6 +15,10 @@ re-types its loops: each one evaluates the same quantity another way.
   untouched none / bad rows;
 * segments: numpy's stable argsort of the routing key;
 * parameter count: r(d + k) with the values the pages print;
+* grouped = per row: the batch run the way the hot-loading page's batched
+  execution runs it (rows gathered per adapter id, each group through the
+  factors as whole matrices with numpy's matmul, scattered back) equals the
+  per-row oracle;
 * merge / unmerge: the merged weight equals numpy's W + (alpha/r) B A per
   slice, merge + unmerge cancel, and serving the merged weight reproduces
   the per-row apply (page "LoRA serving", section 1, merge vs adapter).
@@ -207,6 +211,19 @@ def pin_segments_stable_sort(lib):
         np.testing.assert_array_equal(seg["counts"], [int(ok.sum()), len(act), n_bad])
 
 
+def pin_grouped_equals_per_row(lib):
+    """The per-row oracle equals the grouped algorithm on every row (adapter
+    rows to 1e-12 of the output's scale, untouched rows exactly)."""
+    for p in _small_problems() + [synth.make_workload("tiny_ref")]:
+        want = oracle.apply_grouped(p.dtype, p.k, p.slice_d, p.ranks, p.alphas, p.A, p.B, p.ids,
+                                    p.x, p.y)
+        got = _run(lib, p)
+        tol = 1e-12 * max(1.0, float(np.max(np.abs(want))))
+        np.testing.assert_allclose(got, want, rtol=0, atol=tol, err_msg=p.name)
+        keep = ~_valid(p.ids, p.ranks)
+        np.testing.assert_array_equal(got[keep], want[keep], err_msg=p.name)
+
+
 def pin_param_count(lib):
     g = json.load(open(os.path.join(GOLDEN, "param_count.json")))
     got = oracle.param_count(g["rank"], g["k"], [g["d"]], lib=lib)
@@ -276,7 +293,8 @@ def pin_merge_serves_apply(lib):
 
 
 PINS = [pin_golden_worked, pin_dense_delta, pin_merged_weight, pin_rank1_closed_form,
-        pin_invariants, pin_segments_stable_sort, pin_param_count, pin_merge_dense,
+        pin_invariants, pin_segments_stable_sort, pin_grouped_equals_per_row, pin_param_count,
+        pin_merge_dense,
         pin_merge_unmerge_cancel, pin_merge_serves_apply]
 
 
