@@ -232,7 +232,8 @@ __device__ __forceinline__ uint32_t *class_words(const DecodeArgs &a)
 // Prefetch into L2 (through this XCD) what the k-split's shrink workgroups
 // will read: rows [16 t, 16 t + 16) of x and a 1/T share of every slot's A
 // over the split's k-range, one 4-byte load per 128-byte line (the L2 line),
-// at most one per thread.  Issued after every other load of the workgroup's
+// at most one per thread.  In the operand image a slot's k-range is one
+// contiguous run of 2 lines per 8-element unit (16 rank rows x 16 bytes).  Issued after every other load of the workgroup's
 // start (vector loads complete in order, so waiting for those does not wait
 // for this one) and consumed at the end.  Threads without a line load the
 // split's first line of x row 0 again.  Returns the address to load.
@@ -244,20 +245,20 @@ __device__ __forceinline__ const uint32_t *dec_prefetch(const DecodeArgs &a, int
     const int lpr = (int)(g8 / a.ks) >> 3;      // 128-byte lines per row in the split (>= 2)
     const uint32_t m_lpr = div_magic(lpr);
     const int nx = kT * lpr;
-    const int ar = a.n_slots * a.r_max;
-    const int per = (ar + a.tiles_bound - 1) / a.tiles_bound;
-    const int r0 = t * per, r1 = min(ar, r0 + per);
-    const int na = max(0, r1 - r0) * lpr;
-    const uint16_t *X = static_cast<const uint16_t *>(a.x), *A = static_cast<const uint16_t *>(a.A);
+    const int lps = (int)(g8 / a.ks) * 2;       // image lines of one slot in the split
+    const int total = a.n_slots * lps;
+    const int per = (total + a.tiles_bound - 1) / a.tiles_bound;
+    const uint16_t *X = static_cast<const uint16_t *>(a.x), *A = static_cast<const uint16_t *>(a.A_img);
     const uint16_t *p = X + u0 * 8;
     const int e = tid < nx ? tid : tid - nx;
-    const int q = div_small(e, m_lpr), rem = e - q * lpr;
     if (tid < nx) {
+        const int q = div_small(e, m_lpr), rem = e - q * lpr;
         const int row = kT * t + q;
         if (row < a.n)
             p = X + (int64_t)row * a.ldx + (u0 + rem * 8) * 8;
-    } else if (e < na) {
-        p = A + (int64_t)(r0 + q) * a.k + (u0 + rem * 8) * 8;
+    } else if (e < per && t * per + e < total) {
+        const int li = t * per + e, s = li / lps, off = li - s * lps;
+        p = A + (int64_t)s * kImgRows * a.k + u0 * 128 + (int64_t)off * 64;
     }
     return reinterpret_cast<const uint32_t *>(p);
 }
@@ -271,10 +272,9 @@ __device__ __forceinline__ void dec_shrink(const DecodeArgs &a, int t, int ks, c
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t xrow = (int64_t)L.rows[min(m, P.cnt - 1)] * a.ldx;   // rows past cnt: dropped
-    // A row m of the slot (rank rows past r_max are read from row r_max - 1
-    // and dropped; rows in [r, r_max) are zero in the pool)
-    const bool a_ok = m < a.r_max;
-    const int64_t arow = ((int64_t)P.s * a.r_max + min(m, a.r_max - 1)) * a.k;
+    // A from the slot's operand image (16 rank rows, zero past the rank):
+    // lane (g, m) of unit u at element 128 u + 8 m, one kilobyte per load
+    const int64_t arow = (int64_t)P.s * kImgRows * a.k + m * 8;
     const int64_t g8 = a.k >> 3;
     const int64_t wb = g8 * ks / a.ks + (g8 / a.ks / 4) * wave;   // this wavefront's k-quarter
     const int steps = (int)(g8 / a.ks / 16);                      // MFMA steps of 32 k per wavefront
@@ -288,7 +288,7 @@ __device__ __forceinline__ void dec_shrink(const DecodeArgs &a, int t, int ks, c
             const bool ok = s0 + st < steps;
             const int64_t cu = ok ? unit : wb + g;   // clamped: in bounds, dropped
             xs[st] = keep_if(ok, load16(a.x, xrow + cu * 8));
-            as[st] = keep_if(ok && a_ok, load16(a.A, arow + cu * 8));
+            as[st] = keep_if(ok, load16(a.A_img, arow + cu * 128));
         }
 #pragma unroll
         for (int st = 0; st < CH; ++st)

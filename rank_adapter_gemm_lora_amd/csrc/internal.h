@@ -67,6 +67,7 @@ struct SegBuildArgs {
 struct ApplyArgs {
     // stack
     const void *A;             // pool [n_slots][n_slices][r_max][k]
+    const void *A_img;         // operand image of the pool (MFMA stacks), see kImgRows
     const void *B;             // pool, slot s: [D][rp_s] at s * b_slot_stride
     const int32_t *rank;       // [n_slots]
     const float *scale;        // [n_slots] alpha / rank
@@ -146,7 +147,7 @@ struct DecodeArgs {
     int n_slots;
     const int32_t *slot_rank;
     const float *slot_scale;
-    const void *A;            // pool [n_slots][r_max][k]
+    const void *A_img;        // operand image of the pool: slot s at s * 16 * k
     const void *B;            // pool, slot s at s * b_slot_stride: [D][rp_s]
     int64_t b_slot_stride;
     int r_max;
@@ -221,6 +222,7 @@ struct GatherJob {
 };
 struct GatherArgs {
     void *A_pool;
+    void *A_img;       // the pool's operand image, or null
     void *B_pool;
     int32_t *rank_tab;
     float *scale_tab;
@@ -234,6 +236,26 @@ struct GatherArgs {
     GatherJob job[kGatherJobs];
 };
 hipError_t launch_gather_load(const GatherArgs &g, hipStream_t stream);
+
+// The operand image of the A pool, kept beside it for stacks with the MFMA
+// path: per (slot, slice, 16-rank chunk) one block of 16 x k elements in which
+// the 16-byte granule of rank row 16 jc + m and 8-element k unit u sits at
+// granule index 16 u + m (zero for rows at or past r_max).  A matrix-core
+// operand of 16 rank rows x 4 consecutive units (lane 16 g + m: row m, unit
+// u + g) is then one contiguous kilobyte, where the pool's row-major layout
+// spreads it over 16 rows, 64 bytes each.
+constexpr int kImgRows = 16;
+struct ImageArgs {
+    const void *A_pool;
+    void *A_img;
+    int64_t k;
+    int n_slices;
+    int r_max;
+    int n_jobs;
+    int slot[kGatherJobs];
+};
+// Rebuild the image of the listed slots from their pool regions (bf16).
+hipError_t launch_build_image(const ImageArgs &g, hipStream_t stream);
 // Record a host-gathered load in the stack's host state (after the launch).
 void note_loaded(lora_stack *st, int slot, int rank, float alpha);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
@@ -256,6 +278,7 @@ struct lora_stack {
     int64_t D;
     int64_t max_rows;
     void *A_pool;
+    void *A_img;              // operand image of A_pool (stacks with the MFMA path), else null
     void *B_pool;
     int32_t *d_rank;
     float *d_scale;

@@ -79,6 +79,7 @@ void free_stack(lora_stack *st)
     if (!st)
         return;
     (void)hipFree(st->A_pool);
+    (void)hipFree(st->A_img);
     (void)hipFree(st->B_pool);
     (void)hipFree(st->d_rank);
     (void)hipFree(st->d_scale);
@@ -220,6 +221,7 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     ApplyArgs a;
     std::memset(&a, 0, sizeof a);
     a.A = st->A_pool;
+    a.A_img = st->A_img;
     a.B = st->B_pool;
     a.rank = st->d_rank;
     a.scale = st->d_scale;
@@ -310,6 +312,19 @@ lora_status lora::load_slot(lora_stack *st, int slot, int rank, float alpha, con
     else
         LORA_TRY(hipMemcpy2DAsync(b_dst, (size_t)rp * es, B, (size_t)rank * es, (size_t)rank * es,
                                   st->D, kind, s));
+    if (st->A_img) {
+        // the slot's operand image, from the region just written
+        ImageArgs im;
+        std::memset(&im, 0, sizeof im);
+        im.A_pool = st->A_pool;
+        im.A_img = st->A_img;
+        im.k = st->k;
+        im.n_slices = st->n_slices;
+        im.r_max = st->r_max;
+        im.n_jobs = 1;
+        im.slot[0] = slot;
+        LORA_TRY(launch_build_image(im, s));
+    }
     LORA_TRY(launch_set_slot(st->d_rank, st->d_scale, slot, rank, alpha / (float)rank, s));
     if (sync)
         LORA_TRY(hipStreamSynchronize(s));
@@ -375,7 +390,7 @@ int lora::decode_ks(int64_t k)
 // the hand-over state holds vt_tiles tiles.
 bool lora::decode_fits(const lora_stack *st, int64_t n_rows, int cpw, int vt_tiles)
 {
-    if (st->dtype != LORA_BF16 || st->n_slices != 1 || st->r_max > 16 || st->D % 64 != 0 ||
+    if (st->dtype != LORA_BF16 || !st->A_img || st->n_slices != 1 || st->r_max > 16 || st->D % 64 != 0 ||
         n_rows < 1 || n_rows > kDecodeMaxRows || st->n_slots > kDecodeMaxSlots || decode_ks(st->k) == 0)
         return false;
     const int64_t tiles = max_tiles_for(n_rows, st->n_slots);
@@ -402,7 +417,7 @@ DecodeArgs lora::decode_args_for(const lora_stack *st, const int32_t *ids, int64
     a.n_slots = st->n_slots;
     a.slot_rank = st->d_rank;
     a.slot_scale = st->d_scale;
-    a.A = st->A_pool;
+    a.A_img = st->A_img;
     a.B = st->B_pool;
     a.b_slot_stride = st->D * st->rp_max;
     a.r_max = st->r_max;
@@ -463,7 +478,7 @@ lora_status lora_stack_create(lora_stack **out, lora_dtype dtype, int n_slots, i
     lora_stack *st = new (std::nothrow) lora_stack();
     if (!st)
         return LORA_E_NOMEM;
-    st->A_pool = st->B_pool = nullptr;
+    st->A_pool = st->A_img = st->B_pool = nullptr;
     st->d_rank = nullptr;
     st->d_scale = nullptr;
     st->vpart = nullptr;
@@ -492,15 +507,21 @@ lora_status lora_stack_create(lora_stack **out, lora_dtype dtype, int n_slots, i
     st->h_alpha.assign(n_slots, 0.f);
 
     const size_t a_bytes = (size_t)n_slots * n_slices * r_max * k * st->esize;
+    // the operand image pads each slice's ranks to whole 16-row chunks
+    const size_t img_bytes = stack_has_mfma_path(st)
+                                 ? (size_t)n_slots * n_slices * round_up(r_max, kImgRows) * k * st->esize
+                                 : 0;
     const size_t b_bytes = (size_t)n_slots * D * st->rp_max * st->esize;
     const size_t v_bytes = (size_t)max_rows * n_slices * r_max * sizeof(float);
     hipError_t e = hipSuccess;
     if (e == hipSuccess) e = hipMalloc(&st->A_pool, a_bytes);
+    if (e == hipSuccess && img_bytes) e = hipMalloc(&st->A_img, img_bytes);
     if (e == hipSuccess) e = hipMalloc(&st->B_pool, b_bytes);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->d_rank), sizeof(int32_t) * n_slots);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->d_scale), sizeof(float) * n_slots);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&st->vpart), kMaxKSplit * v_bytes);
     if (e == hipSuccess) e = hipMemset(st->A_pool, 0, a_bytes);
+    if (e == hipSuccess && img_bytes) e = hipMemset(st->A_img, 0, img_bytes);
     if (e == hipSuccess) e = hipMemset(st->B_pool, 0, b_bytes);
     if (e == hipSuccess) e = hipMemset(st->d_rank, 0, sizeof(int32_t) * n_slots);
     if (e == hipSuccess) e = hipMemset(st->d_scale, 0, sizeof(float) * n_slots);

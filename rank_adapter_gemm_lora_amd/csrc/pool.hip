@@ -1,7 +1,8 @@
 // pool.hip -- stream-ordered maintenance of the adapter pool: zero-filling a
 // slot's region before a load, writing the device slot table (rank, scale) so
-// that load -> apply -> evict on one stream need no host sync, and loading
-// several adapters at once straight from mapped pinned host memory.
+// that load -> apply -> evict on one stream need no host sync, loading
+// several adapters at once straight from mapped pinned host memory, and
+// rebuilding a loaded slot's operand image of A.
 #include "internal.h"
 
 namespace lora {
@@ -74,14 +75,62 @@ __global__ __launch_bounds__(256) void gather_load_kernel(GatherArgs g)
     }
 }
 
+// One slot per blockIdx.y: its operand image, granule by granule, from its
+// pool region [n_slices][r_max][k] (bf16).  Image granule d of the slot is
+// (slice q, rank chunk jc, k unit u, row m) with d = ((q * njm + jc) * ku + u)
+// * 16 + m; rows at or past r_max are zero.  Writes are contiguous, reads
+// gather 16 rows: a one-time cost per loaded adapter.
+__global__ __launch_bounds__(256) void build_image_kernel(ImageArgs g)
+{
+    const int slot = g.slot[blockIdx.y];
+    const int64_t ku = g.k >> 3;
+    const int njm = (g.r_max + kImgRows - 1) / kImgRows;
+    const int64_t n = (int64_t)g.n_slices * njm * ku * kImgRows;
+    const uint16_t *src = static_cast<const uint16_t *>(g.A_pool) + (int64_t)slot * g.n_slices * g.r_max * g.k;
+    uint4 *dst = static_cast<uint4 *>(g.A_img) + (int64_t)slot * n;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < n; d += stride) {
+        const int m = (int)(d & (kImgRows - 1));
+        const int64_t rest = d / kImgRows;
+        const int64_t u = rest % ku, qj = rest / ku;
+        const int jc = (int)(qj % njm), q = (int)(qj / njm);
+        const int row = jc * kImgRows + m;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < g.r_max)
+            v = *reinterpret_cast<const uint4 *>(src + ((int64_t)q * g.r_max + row) * g.k + u * 8);
+        dst[d] = v;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_build_image(const ImageArgs &g, hipStream_t stream)
+{
+    if (g.n_jobs <= 0 || !g.A_img)
+        return hipSuccess;
+    hipLaunchKernelGGL(build_image_kernel, dim3(64, g.n_jobs), dim3(256), 0, stream, g);
+    return hipGetLastError();
+}
 
 hipError_t launch_gather_load(const GatherArgs &g, hipStream_t stream)
 {
     if (g.n_jobs <= 0)
         return hipSuccess;
     hipLaunchKernelGGL(gather_load_kernel, dim3(64, g.n_jobs), dim3(256), 0, stream, g);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !g.A_img)
+        return e;
+    // the image is rebuilt from the pool just written (same stream)
+    ImageArgs im;
+    im.A_pool = g.A_pool;
+    im.A_img = g.A_img;
+    im.k = g.k;
+    im.n_slices = g.n_slices;
+    im.r_max = g.r_max;
+    im.n_jobs = g.n_jobs;
+    for (int i = 0; i < g.n_jobs; ++i)
+        im.slot[i] = g.job[i].slot;
+    return launch_build_image(im, stream);
 }
 
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream)

@@ -125,6 +125,7 @@ lora_status load_all(lora_residency *m, const std::vector<std::pair<int, int64_t
         lora::GatherArgs g;
         std::memset(&g, 0, sizeof g);
         g.A_pool = st->A_pool;
+        g.A_img = st->A_img;
         g.B_pool = st->B_pool;
         g.rank_tab = st->d_rank;
         g.scale_tab = st->d_scale;

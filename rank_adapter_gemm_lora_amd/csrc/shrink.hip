@@ -156,16 +156,19 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
     auto pass = [&](int t0, auto ntv_tag) {
         constexpr int NTV = decltype(ntv_tag)::value;
         constexpr int kSt = NTV == 1 ? 4 : 2;   // register buffers: 2 x kSt x (1 + NTV) granules
+        // A comes from the pool's operand image: the N-tile's block of 16 rank
+        // rows, lane (g, m) of unit u at element 128 u + 8 m of the block, so
+        // each load instruction reads one contiguous kilobyte.  Rank rows past
+        // r are zero in the image; N-tiles past the last read the zero granule.
+        const int njm = (a.r_max + kImgRows - 1) / kImgRows;
         int64_t arow[NTV];
         bool aok[NTV];
 #pragma unroll
         for (int tt = 0; tt < NTV; ++tt) {
             const int t = min(t0 + tt, NT - 1);   // N-tiles past the last repeat it
             const int q = t / nj, jc = t - q * nj;
-            const int j = jc * 16 + m;
-            aok[tt] = t0 + tt < NT && j < r;
-            // rank rows past r (and N-tiles past the last) read the pool's start, dropped
-            arow[tt] = aok[tt] ? (((int64_t)s * a.n_slices + q) * a.r_max + j) * a.k : 0;
+            aok[tt] = t0 + tt < NT;
+            arow[tt] = ((((int64_t)s * a.n_slices + q) * njm + jc) * kImgRows) * a.k + m * 8;
         }
         f32x4_t acc[NTV];
 #pragma unroll
@@ -181,7 +184,7 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
         // into a branch around the load or a select of two loaded values.)
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         typedef const __attribute__((address_space(1))) u32x4 *G16;   // global: no flat loads
-        const uint64_t X = (uint64_t)a.x, Ap = (uint64_t)a.A, Z = (uint64_t)&g_zero_granule;
+        const uint64_t X = (uint64_t)a.x, Ap = (uint64_t)a.A_img, Z = (uint64_t)&g_zero_granule;
         auto gload = [](uint64_t addr) {
             asm("" : "+v"(addr));
             const u32x4 v = *(G16)addr;
@@ -195,7 +198,7 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
                 xs[st] = gload(ok ? X + 2 * (xrow + unit * 8) : Z);
 #pragma unroll
                 for (int tt = 0; tt < NTV; ++tt)
-                    as[tt][st] = gload(ok && aok[tt] ? Ap + 2 * (arow[tt] + unit * 8) : Z);
+                    as[tt][st] = gload(ok && aok[tt] ? Ap + 2 * (arow[tt] + unit * 128) : Z);
             }
         };
         auto mma_step = [&](const uint4 (&xs)[kSt], const uint4 (&as)[NTV][kSt]) {
