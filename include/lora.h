@@ -88,7 +88,10 @@ typedef enum lora_path { LORA_PATH_BGMV = 0, LORA_PATH_SGMV = 1 } lora_path;
  * writes columns [off_q, off_q + slice_d[q]) of y, each slice with its own A_q
  * and B_q, all sharing the row's adapter id and scale.  max_rows bounds
  * n_rows of every lora_apply on this stack (it sizes the stack's fp32 scratch
- * for v).  The physical layout of the pool is private.
+ * for v).  The physical layout of the pool is private; bf16 stacks whose
+ * slices are whole 64-column blocks also keep a second, operand-ordered copy
+ * of A (about n_slots * n_slices * round_up(r_max, 16) * k * 2 bytes more),
+ * rebuilt in stream order by every load.
  *
  *   out       receives the new stack (set to NULL on failure)
  *   dtype     element type of weights, x and y

@@ -158,8 +158,10 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
         constexpr int kSt = NTV == 1 ? 4 : 2;   // register buffers: 2 x kSt x (1 + NTV) granules
         // A comes from the pool's operand image: the N-tile's block of 16 rank
         // rows, lane (g, m) of unit u at element 128 u + 8 m of the block, so
-        // each load instruction reads one contiguous kilobyte.  Rank rows past
-        // r are zero in the image; N-tiles past the last read the zero granule.
+        // each load instruction reads one contiguous kilobyte (less the rows
+        // past r).  Rank rows past r and N-tiles past the last read the zero
+        // granule instead (the image holds zeros there too, but reading them
+        // would cost bandwidth).
         const int njm = (a.r_max + kImgRows - 1) / kImgRows;
         int64_t arow[NTV];
         bool aok[NTV];
@@ -167,7 +169,7 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
         for (int tt = 0; tt < NTV; ++tt) {
             const int t = min(t0 + tt, NT - 1);   // N-tiles past the last repeat it
             const int q = t / nj, jc = t - q * nj;
-            aok[tt] = t0 + tt < NT;
+            aok[tt] = t0 + tt < NT && jc * kImgRows + m < r;
             arow[tt] = ((((int64_t)s * a.n_slices + q) * njm + jc) * kImgRows) * a.k + m * 8;
         }
         f32x4_t acc[NTV];
