@@ -126,26 +126,117 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 // 16 zero bytes: the source of operand granules that lie outside the data.
 __device__ const uint4 g_zero_granule = {0u, 0u, 0u, 0u};
 
+// Products of one 16-row operand set with NTV N-tiles (slice, 16-rank chunk)
+// t0 .. t0 + NTV - 1 of slot s over the k units [wb, we): acc[tt] receives
+// the 16 x 16 tile of N-tile t0 + tt (lane (g, m): rows 4 g + i, rank row m).
+// xrow is the element offset of this lane's x row (lane m: row m of the set).
+// kSt 8-element k groups per lane per step (4 for one N-tile, 2 for kNT: the
+// two register buffers, loads of step i + 1 in flight during the MFMAs of step
+// i, then fit without spilling).  Every load reads an in-bounds address and
+// no branch surrounds a load.  (Measured: branches around the loads, or a
+// select of "load or zero" on a runtime tile count, made the compiler drain
+// the loads in flight at every step.)
+template <int NTV>
+__device__ __forceinline__ void shrink_stream(const ApplyArgs &a, int64_t xrow, int s, int r, int nj,
+                                              int NT, int t0, int64_t wb, int64_t we,
+                                              f32x4_t (&acc)[NTV])
+{
+    constexpr int kSt = NTV == 1 ? 4 : 2;   // register buffers: 2 x kSt x (1 + NTV) granules
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15, g = lane >> 4;
+    // A comes from the pool's operand image: the N-tile's block of 16 rank
+    // rows, lane (g, m) of unit u at element 128 u + 8 m of the block, so
+    // each load instruction reads one contiguous kilobyte (less the rows
+    // past r).  Rank rows past r and N-tiles past the last read the zero
+    // granule instead (the image holds zeros there too, but reading them
+    // would cost bandwidth).
+    const int njm = (a.r_max + kImgRows - 1) / kImgRows;
+    int64_t arow[NTV];
+    bool aok[NTV];
+#pragma unroll
+    for (int tt = 0; tt < NTV; ++tt) {
+        const int t = min(t0 + tt, NT - 1);   // N-tiles past the last repeat it
+        const int q = t / nj, jc = t - q * nj;
+        aok[tt] = t0 + tt < NT && jc * kImgRows + m < r;
+        arow[tt] = ((((int64_t)s * a.n_slices + q) * njm + jc) * kImgRows) * a.k + m * 8;
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTV; ++tt)
+        acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Granules past the k-range (and of dropped N-tiles) are read from a zero
+    // granule: the choice is made on the address, so no select waits on a
+    // loaded value and the next step's loads stay in flight while this step's
+    // products run.  (The address passes through an empty asm statement,
+    // opaque to the optimizer, which would otherwise turn the choice of
+    // address back into a branch around the load or a select of two loaded
+    // values.)
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(1))) u32x4 *G16;   // global: no flat loads
+    const uint64_t X = (uint64_t)a.x, Ap = (uint64_t)a.A_img, Z = (uint64_t)&g_zero_granule;
+    auto gload = [](uint64_t addr) {
+        asm("" : "+v"(addr));
+        const u32x4 v = *(G16)addr;
+        return make_uint4(v.x, v.y, v.z, v.w);
+    };
+    auto load_step = [&](int64_t u0, uint4 (&xs)[kSt], uint4 (&as)[NTV][kSt]) {
+#pragma unroll
+        for (int st = 0; st < kSt; ++st) {
+            const int64_t unit = u0 + 4 * st + g;   // lanes g = 0..3: 64 contiguous bytes of a row
+            const bool ok = unit < we;
+            xs[st] = gload(ok ? X + 2 * (xrow + unit * 8) : Z);
+#pragma unroll
+            for (int tt = 0; tt < NTV; ++tt)
+                as[tt][st] = gload(ok && aok[tt] ? Ap + 2 * (arow[tt] + unit * 128) : Z);
+        }
+    };
+    auto mma_step = [&](const uint4 (&xs)[kSt], const uint4 (&as)[NTV][kSt]) {
+#pragma unroll
+        for (int st = 0; st < kSt; ++st)
+#pragma unroll
+            for (int tt = 0; tt < NTV; ++tt)
+                acc[tt] = mfma_bf16_16x16x32(xs[st], as[tt][st], acc[tt]);
+    };
+    // Two register buffers, one step of loads in flight behind the products.
+    // No load sits under a condition inside the loop: where a load may or may
+    // not have been issued, the wait before a product has to assume it was
+    // not, and then waits for the loads in flight too.  The last one or two
+    // steps are peeled off instead.
+    const int64_t n_steps = (we - wb + 4 * kSt - 1) / (4 * kSt);
+    constexpr int kStep = 4 * kSt;   // 8-element units per step
+    uint4 xa[kSt], aa[NTV][kSt], xb[kSt], ab[NTV][kSt];
+    if (n_steps > 0) {
+        load_step(wb, xa, aa);
+        int64_t i = 0;
+        for (; i + 2 < n_steps; i += 2) {
+            load_step(wb + (i + 1) * kStep, xb, ab);
+            mma_step(xa, aa);
+            load_step(wb + (i + 2) * kStep, xa, aa);
+            mma_step(xb, ab);
+        }
+        if (i + 1 < n_steps) {
+            load_step(wb + (i + 1) * kStep, xb, ab);
+            mma_step(xa, aa);
+            mma_step(xb, ab);
+        } else {
+            mma_step(xa, aa);
+        }
+    }
+}
+
 // 16-row SGMV tile (batches up to 4096 rows): M = the tile's rows, N = up to
 // kNT N-tiles (slice, 16-rank chunk) per pass over the k-range, K = k; the
 // four wavefronts split the workgroup's k-range and their partial tiles are
 // summed in LDS in wavefront order.  A pass handles NTV N-tiles, a template
 // parameter: 1 when the whole rank is one N-tile (rank <= 16, one slice: the
-// common decode shape loads nothing it drops), else kNT.  kSt 8-element k
-// groups per lane per step (4 for one N-tile, 2 for kNT: the two register
-// buffers, loads of step i + 1 in flight during the MFMAs of step i, then fit
-// without spilling).  Every load reads an in-bounds address (clamped unit;
-// rank rows past r read from the pool's start) and its value is selected
-// afterwards, so no branch surrounds a load.  (Measured: branches around the
-// loads, or a select of "load or zero" on a runtime tile count, made the
-// compiler drain the loads in flight at every step.)
+// common decode shape loads nothing it drops), else kNT.
 template <bool COH>
 __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s, int r, int p0,
                                  int cnt, int ks)
 {
     __shared__ f32x4_t red[4][kNT * 64];   // [wave][tt * 64 + lane]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
+    const int m = lane & 15;
     const int64_t xrow = (int64_t)rows[min(m, cnt - 1)] * a.ldx;   // clamp: dropped later
     const int nj = (r + 15) >> 4;
     const int NT = a.n_slices * nj;
@@ -155,87 +246,8 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 
     auto pass = [&](int t0, auto ntv_tag) {
         constexpr int NTV = decltype(ntv_tag)::value;
-        constexpr int kSt = NTV == 1 ? 4 : 2;   // register buffers: 2 x kSt x (1 + NTV) granules
-        // A comes from the pool's operand image: the N-tile's block of 16 rank
-        // rows, lane (g, m) of unit u at element 128 u + 8 m of the block, so
-        // each load instruction reads one contiguous kilobyte (less the rows
-        // past r).  Rank rows past r and N-tiles past the last read the zero
-        // granule instead (the image holds zeros there too, but reading them
-        // would cost bandwidth).
-        const int njm = (a.r_max + kImgRows - 1) / kImgRows;
-        int64_t arow[NTV];
-        bool aok[NTV];
-#pragma unroll
-        for (int tt = 0; tt < NTV; ++tt) {
-            const int t = min(t0 + tt, NT - 1);   // N-tiles past the last repeat it
-            const int q = t / nj, jc = t - q * nj;
-            aok[tt] = t0 + tt < NT && jc * kImgRows + m < r;
-            arow[tt] = ((((int64_t)s * a.n_slices + q) * njm + jc) * kImgRows) * a.k + m * 8;
-        }
         f32x4_t acc[NTV];
-#pragma unroll
-        for (int tt = 0; tt < NTV; ++tt)
-            acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        // Granules past the wavefront's k-range (and of dropped N-tiles) are
-        // read from a zero granule: the choice is made on the address, so
-        // no select waits on a loaded value and the next step's loads stay in
-        // flight while this step's products run.
-        // (The address passes through an empty asm statement, opaque to the
-        // optimizer, which would otherwise turn the choice of address back
-        // into a branch around the load or a select of two loaded values.)
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        typedef const __attribute__((address_space(1))) u32x4 *G16;   // global: no flat loads
-        const uint64_t X = (uint64_t)a.x, Ap = (uint64_t)a.A_img, Z = (uint64_t)&g_zero_granule;
-        auto gload = [](uint64_t addr) {
-            asm("" : "+v"(addr));
-            const u32x4 v = *(G16)addr;
-            return make_uint4(v.x, v.y, v.z, v.w);
-        };
-        auto load_step = [&](int64_t u0, uint4 (&xs)[kSt], uint4 (&as)[NTV][kSt]) {
-#pragma unroll
-            for (int st = 0; st < kSt; ++st) {
-                const int64_t unit = u0 + 4 * st + g;   // lanes g = 0..3: 64 contiguous bytes of a row
-                const bool ok = unit < we;
-                xs[st] = gload(ok ? X + 2 * (xrow + unit * 8) : Z);
-#pragma unroll
-                for (int tt = 0; tt < NTV; ++tt)
-                    as[tt][st] = gload(ok && aok[tt] ? Ap + 2 * (arow[tt] + unit * 128) : Z);
-            }
-        };
-        auto mma_step = [&](const uint4 (&xs)[kSt], const uint4 (&as)[NTV][kSt]) {
-#pragma unroll
-            for (int st = 0; st < kSt; ++st)
-#pragma unroll
-                for (int tt = 0; tt < NTV; ++tt)
-                    acc[tt] = mfma_bf16_16x16x32(xs[st], as[tt][st], acc[tt]);
-        };
-        // Two register buffers, one step of loads in flight behind the
-        // products.  No load sits under a condition inside the loop: where a
-        // load may or may not have been issued, the wait before a product
-        // has to assume it was not, and then waits for the loads in flight
-        // too.  The last one or two steps are peeled off instead.
-        const int64_t n_steps = (we - wb + 4 * kSt - 1) / (4 * kSt);
-        constexpr int kStep = 4 * kSt;   // 8-element units per step
-        uint4 xa[kSt], aa[NTV][kSt], xb[kSt], ab[NTV][kSt];
-        if (n_steps > 0) {
-            load_step(wb, xa, aa);
-            int64_t i = 0;
-            for (; i + 2 < n_steps; i += 2) {
-                load_step(wb + (i + 1) * kStep, xb, ab);
-                mma_step(xa, aa);
-                load_step(wb + (i + 2) * kStep, xa, aa);
-                mma_step(xb, ab);
-            }
-            if (i + 1 < n_steps) {
-                load_step(wb + (i + 1) * kStep, xb, ab);
-                mma_step(xa, aa);
-                mma_step(xb, ab);
-            } else {
-                mma_step(xa, aa);
-            }
-        }
-
+        shrink_stream<NTV>(a, xrow, s, r, nj, NT, t0, wb, we, acc);
         // fixed-order sum of the four k-quarters
 #pragma unroll
         for (int tt = 0; tt < NTV; ++tt)
@@ -264,7 +276,7 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
     for (int t0 = 0; t0 < NT; t0 += kNT) {
         // (uniform) one N-tile (rank <= 16, one slice: the common decode
         // shape) or a full pass; a partial last pass loads its empty N-tiles
-        // from row r - 1 and drops them
+        // from the zero granule and drops them
         if (NT - t0 == 1)
             pass(t0, std::integral_constant<int, 1>());
         else
