@@ -205,6 +205,64 @@ def test_hot_swap_in_stream_order():
     check_against_oracle(p2, y2, what="after swap")
 
 
+SHRINK_SWAPS = {
+    # multi-slice stack on the matrix-core path: rank 64 -> 8 and 64 -> 40 (not a
+    # multiple of 16) in slots whose operand image held the larger adapters
+    "mfma_two_slices": dict(n_rows=300, k=256, slice_d=[128, 192], n_slots=3, ranks=[64, 64, 32],
+                            r_max=64, swaps={0: 8, 1: 40}),
+    # decode-kernel shape (one slice, r_max 16, <= 256 rows): the kernel reads all
+    # 16 rank rows of a slot's image, so rows past a smaller rank must be zero
+    "decode_rank16_to_4": dict(n_rows=200, k=512, slice_d=[512], n_slots=4, ranks=[16] * 4,
+                               r_max=16, swaps={1: 4, 2: 12}),
+}
+
+
+@pytest.mark.parametrize("mode", ["split", "build_apply"])
+@pytest.mark.parametrize("case", list(SHRINK_SWAPS))
+def test_reload_smaller_rank_clears_operand_rows(case, mode):
+    """Evict and reload slots with a smaller rank in stream order; the rank rows
+    the earlier adapters held must read as zero afterwards (pool and image).
+    build_apply runs the decode kernel on the decode shape."""
+    c = dict(SHRINK_SWAPS[case])
+    swaps = c.pop("swaps")
+    p = synth.make_random(41, dtype="bf16", p_none=0.05, **c)
+    note(f"reload smaller rank {case} {mode}")
+    run = GpuRun(p)
+
+    def step():
+        if mode == "split":
+            run.build()
+            run.apply()
+        else:
+            run.build_apply()
+
+    try:
+        step()
+        y1 = run.y.clone()
+        new = {}
+        for slot, rank in swaps.items():
+            q = synth.make_random(43 + slot, n_rows=1, k=p.k, slice_d=p.slice_d, n_slots=1,
+                                  ranks=[rank], r_max=p.r_max, dtype="bf16")
+            lb.lora_evict_slot(run.stack, slot, run.stream)
+            run.load(slot, q.A[0], q.B[0], 3.0 + slot, from_device=True)
+            new[slot] = (q.A[0], q.B[0], rank)
+        step()
+        y2 = run.y_host()
+        y1h = y1.cpu().numpy().view(np.uint16)
+    finally:
+        run.close()
+    check_against_oracle(p, y1h, what=f"{case} before reload")
+    p2 = synth.Problem(**{**p.__dict__})
+    p2.A, p2.B = list(p.A), list(p.B)
+    p2.ranks, p2.alphas = p.ranks.copy(), p.alphas.copy()
+    for slot, (A2, B2, rank) in new.items():
+        p2.A[slot], p2.B[slot] = A2, B2
+        p2.ranks[slot] = rank
+        p2.alphas[slot] = 3.0 + slot
+    p2.y = y1h
+    check_against_oracle(p2, y2, what=f"{case} after reload")
+
+
 def test_evicted_after_build_leaves_rows_untouched():
     p = synth.make_random(31, n_rows=120, k=128, slice_d=[128], n_slots=3, ranks=[16] * 3,
                           r_max=16)
