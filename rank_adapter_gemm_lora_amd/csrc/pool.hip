@@ -121,7 +121,7 @@ hipError_t launch_gather_load(const GatherArgs &g, hipStream_t stream)
     if (e != hipSuccess || !g.A_img)
         return e;
     // the image is rebuilt from the pool just written (same stream)
-    ImageArgs im;
+    ImageArgs im{};
     im.A_pool = g.A_pool;
     im.A_img = g.A_img;
     im.k = g.k;
