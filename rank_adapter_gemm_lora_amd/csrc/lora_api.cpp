@@ -55,10 +55,18 @@ int sgmv_rows_for(const lora_stack *st, int64_t n_rows)
 
 // k-splits of the shrink: about 256 tile workgroups in all (tile_rows-row
 // tiles), at least 512 k per split, at most kMaxKSplit, a power of two.
-int choose_ks(int64_t k, int64_t n_rows, int tile_rows)
+// Batches of 64-row tiles whose v is small (vrow = slices x r_max <= 48
+// floats a row, so each extra split adds little to what every expand chunk
+// rereads) take at least two: one split per tile leaves ~one long stream per
+// workgroup.  Measured with two against one (k = 4096): q/k/v prefill, 35 K
+// rows, rank 16: step 305.5 -> 298.0 us (four splits: the expand +8.6 us);
+// 12 K rows, rank 16: 99.2 -> 94.6 us; 20 K rows, three slices of rank 8:
+// 193.5 -> 191.5 us; but 16 K rows at rank 64 (vrow 64): 172.6 -> 180.9 us.
+int choose_ks(int64_t k, int64_t n_rows, int tile_rows, int64_t vrow)
 {
     int64_t ks = std::max<int64_t>(1, k / 512);
-    ks = std::min<int64_t>(ks, std::max<int64_t>(1, 256 * tile_rows / std::max<int64_t>(1, n_rows)));
+    const int64_t least = (tile_rows == kSgmvTileRows && vrow <= 48) ? 2 : 1;
+    ks = std::min<int64_t>(ks, std::max<int64_t>(least, 256 * tile_rows / std::max<int64_t>(1, n_rows)));
     ks = std::min<int64_t>(ks, kMaxKSplit);
     // powers of two keep blocks of one split on one XCD
     int64_t p = 1;
@@ -240,7 +248,7 @@ ApplyArgs make_args(const lora_stack *st, const lora_segments *seg)
     // segments may differ from this one: one grouping per batch serves every
     // projection)
     a.sgmv_rows = seg->built ? seg->built_sgmv_rows : sgmv_rows_for(st, seg->n_rows);
-    a.ks = choose_ks(st->k, seg->n_rows, a.sgmv_rows);
+    a.ks = choose_ks(st->k, seg->n_rows, a.sgmv_rows, (int64_t)st->n_slices * st->r_max);
     a.mfma_ok = stack_has_mfma_path(st) ? 1 : 0;
     // v staging sized for this batch's dense tile height (16 rows up to 4096
     // rows): a smaller footprint lets more expand workgroups share a CU
@@ -791,7 +799,7 @@ bool fused_build_pays(const lora_stack *st, int64_t n_rows)
 {
     if (n_rows <= 0 || n_rows > kFusedMaxRows)
         return false;
-    return (int64_t)choose_ks(st->k, n_rows, sgmv_rows_for(st, n_rows)) *
+    return (int64_t)choose_ks(st->k, n_rows, sgmv_rows_for(st, n_rows), (int64_t)st->n_slices * st->r_max) *
                max_tiles_for(n_rows, st->n_slots) <=
            kFusedMaxBlocks;
 }
