@@ -238,15 +238,16 @@ __device__ __forceinline__ uint32_t *class_words(const DecodeArgs &a)
 // every other load of the workgroup's start (vector loads complete in order,
 // so waiting for those does not wait for this one) and consumed at the end.  Threads without a line load the
 // split's first line of x row 0 again.  Returns the address to load.
+template <int KS>
 __device__ __forceinline__ const uint32_t *dec_prefetch(const DecodeArgs &a, int t, int ks)
 {
     const int tid = threadIdx.x;
     const int64_t g8 = a.k >> 3;
-    const int64_t u0 = g8 * ks / a.ks;          // the split's first 8-element unit
-    const int lpr = (int)(g8 / a.ks) >> 3;      // 128-byte lines per row in the split (>= 2)
+    const int64_t u0 = g8 / KS * ks;            // the split's first 8-element unit
+    const int lpr = (int)(g8 / KS) >> 3;        // 128-byte lines per row in the split (>= 2)
     const uint32_t m_lpr = div_magic(lpr);
     const int nx = kT * lpr;
-    const int lps = (int)(g8 / a.ks) * 2;       // image lines of one slot in the split
+    const int lps = (int)(g8 / KS) * 2;         // image lines of one slot in the split
     const int total = a.n_slots * lps;
     const int per = (total + a.tiles_bound - 1) / a.tiles_bound;
     const uint16_t *X = static_cast<const uint16_t *>(a.x), *A = static_cast<const uint16_t *>(a.A_img);
@@ -277,8 +278,8 @@ __device__ __forceinline__ void dec_shrink(const DecodeArgs &a, int t, int ks, c
     // lane (g, m) of unit u at element 128 u + 8 m, one kilobyte per load
     const int64_t arow = (int64_t)P.s * kImgRows * a.k + m * 8;
     const int64_t g8 = a.k >> 3;
-    const int64_t wb = g8 * ks / a.ks + (g8 / a.ks / 4) * wave;   // this wavefront's k-quarter
-    const int steps = (int)(g8 / a.ks / 16);                      // MFMA steps of 32 k per wavefront
+    const int64_t wb = g8 / KS * ks + (g8 / KS / 4) * wave;   // this wavefront's k-quarter
+    const int steps = (int)(g8 / KS / 16);                    // MFMA steps of 32 k per wavefront
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     constexpr int CH = 4;   // steps per batch of loads
     uint4 xs[CH], as[CH];
@@ -441,10 +442,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     __shared__ DecLds L;
     const int tid = threadIdx.x, lane = tid & 63;
     const int b = blockIdx.x;
-    const int n_prod = a.ks * a.tiles_bound;
+    // (KS is the launch's a.ks: divisions by it are shifts, not the long
+    // integer division sequence a runtime divisor costs at every workgroup's start)
+    const int n_prod = KS * a.tiles_bound;
     const bool prod = b < n_prod;
-    const int t = prod ? b / a.ks : (b - n_prod) / a.ncg;
-    const int part = prod ? b - t * a.ks : b - n_prod - t * a.ncg;   // k-split or column group
+    const int t = prod ? b / KS : (b - n_prod) / a.ncg;
+    const int part = prod ? b - t * KS : b - n_prod - t * a.ncg;   // k-split or column group
     // everything that depends on nothing, in one batch of loads (the prefetch
     // last: it is the one left in flight)
     const int id = a.ids[min(tid, a.n - 1)];   // (rows past n: key -1 below)
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
         a.poison ? __hip_atomic_load(a.poison, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
     // (every workgroup issues the load, expand workgroups at the ids, so the
     // count of loads in flight is the same on every path)
-    const uint32_t pf = *(prod ? dec_prefetch(a, t, part) : reinterpret_cast<const uint32_t *>(a.ids));
+    const uint32_t pf = *(prod ? dec_prefetch<KS>(a, t, part) : reinterpret_cast<const uint32_t *>(a.ids));
     DecPlan P;
     dec_group(a, t, id, rk_l, L, P);
     const bool tile_ok = t < P.n_tiles;

@@ -40,6 +40,15 @@ __device__ __forceinline__ int div_small(int n, uint32_t m)
     return (int)(((uint64_t)(uint32_t)n * m) >> 24);
 }
 
+// First 8-element unit of k-split i of n units split d ways, n * i / d, for a
+// power-of-two d (every launch's split count is one): a shift.  Division by a
+// runtime 64-bit value would expand into a long instruction sequence at the
+// start of every workgroup.
+__device__ __forceinline__ int64_t split_begin(int64_t n, int i, int d)
+{
+    return (n * i) >> __builtin_ctz((unsigned)d);
+}
+
 // A k-split partial of v as stored: its lowest fraction bit cleared (a
 // relative change below 2^-22, far inside the output's rounding).
 __device__ __forceinline__ float v_word(float x) { return __uint_as_float(__float_as_uint(x) & ~1u); }

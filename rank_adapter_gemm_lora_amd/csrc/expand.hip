@@ -364,8 +364,13 @@ void expand_run_kernel(ApplyArgs a)
             const uint32_t c = (uint32_t)cost[lo];
             return lo * n_chunks + (int)(((uint32_t)x - (uint32_t)cum[lo] + c - 1) / c);
         };
-        u = units_below((uint64_t)w * total / gridDim.x);
-        u_end = units_below((uint64_t)(w + 1) * total / gridDim.x);
+        // floor(w T / G) in 32-bit arithmetic (w <= G < 2^16, so w (T mod G)
+        // fits): a 64-bit division by the runtime G would cost a long
+        // instruction sequence at every workgroup's start
+        const uint32_t G = gridDim.x, q = total / G, rm = total - q * G;
+        auto share = [&](uint32_t v) -> uint64_t { return (uint64_t)(v * q + v * rm / G); };
+        u = units_below(share((uint32_t)w));
+        u_end = units_below(share((uint32_t)w + 1));
     }
     int bcolumn[4];
 #pragma unroll

@@ -69,7 +69,7 @@ __device__ void bgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t g8 = a.k >> 3;                       // 8-element groups along k
-    const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
+    const int64_t gb = split_begin(g8, ks, a.ks), ge = split_begin(g8, ks + 1, a.ks);
 
     // wavefront w owns rows w, w + 4, w + 8, w + 12, two at a time
     for (int pair = 0; pair < 2; ++pair) {
@@ -241,7 +241,7 @@ __device__ void sgmv_shrink_tile(const ApplyArgs &a, const int32_t *rows, int s,
     const int nj = (r + 15) >> 4;
     const int NT = a.n_slices * nj;
     const int64_t g8 = a.k >> 3;
-    const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
+    const int64_t gb = split_begin(g8, ks, a.ks), ge = split_begin(g8, ks + 1, a.ks);
     const int64_t wb = gb + (ge - gb) * wave / 4, we = gb + (ge - gb) * (wave + 1) / 4;
 
     auto pass = [&](int t0, auto ntv_tag) {
@@ -330,7 +330,7 @@ __device__ __forceinline__ void tall_pass(const ApplyArgs &a, const int64_t (&xs
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t g8 = a.k >> 3;
-    const int64_t gb = g8 * ks / a.ks, ge = g8 * (ks + 1) / a.ks;
+    const int64_t gb = split_begin(g8, ks, a.ks), ge = split_begin(g8, ks + 1, a.ks);
     const int nb = (int)((ge - gb + kBlkUnits - 1) / kBlkUnits);
     const uint16_t *X = static_cast<const uint16_t *>(a.x);
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(256) void build_apply_kernel(ApplyArgs a, SegBuildA
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // expand staging
     const int tid = threadIdx.x, b = blockIdx.x;
     const bool prod = b < n_prod;
-    const int t = prod ? b / a.ks : (b - n_prod) / n_chunks;
+    const int t = prod ? b >> __builtin_ctz((unsigned)a.ks) : (b - n_prod) / n_chunks;   // (a.ks: a power of two)
     const int ks = prod ? b - t * a.ks : 0;
     const int N = sb.n_slots;
     // a wait of an earlier launch gave up: leave y untouched until the host
@@ -788,7 +788,7 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyArgs a, int n_prod, int
     if (threadIdx.x == 0)
         gave_up = 0;   // ordered before any use by the barriers of the tile code
     if (b < n_prod) {
-        const int t = b / a.ks, ks = b - t * a.ks;
+        const int t = b >> __builtin_ctz((unsigned)a.ks), ks = b - t * a.ks;   // (a.ks: a power of two)
         if (shrink_body<DT, 1, true>(a, ks, t)) {
             const TileSync sy(a, t, n_chunks, &gave_up);
             sy.publish(ks);
@@ -803,11 +803,15 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyArgs a, int n_prod, int
     }
 }
 
+// The kernels take k-split boundaries with split_begin: the split count
+// must be a power of two (choose_ks and decode_ks only produce such).
+bool ks_ok(int ks) { return ks >= 1 && ks <= kMaxKSplit && (ks & (ks - 1)) == 0; }
+
 }  // namespace
 
 hipError_t launch_apply(int dtype, const ApplyArgs &a, int max_tiles, hipStream_t stream)
 {
-    if (max_tiles <= 0 || a.sgmv_rows != kBgmvTileRows || a.cpw != 1 || a.ks > kMaxKSplit || !a.sync)
+    if (max_tiles <= 0 || a.sgmv_rows != kBgmvTileRows || a.cpw != 1 || !ks_ok(a.ks) || !a.sync)
         return hipErrorInvalidValue;
     const int n_chunks = (int)((a.D + kCols - 1) / kCols);
     const int n_prod = a.ks * max_tiles;
@@ -835,7 +839,7 @@ hipError_t launch_build_apply(int dtype, const ApplyArgs &a, const SegBuildArgs 
                               hipStream_t stream)
 {
     if (max_tiles <= 0 || sb.n > kGroupRows || sb.sgmv_rows != kBgmvTileRows || a.cpw != 1 ||
-        a.ks > kMaxKSplit || !a.sync)
+        !ks_ok(a.ks) || !a.sync)
         return hipErrorInvalidValue;
     const int n_chunks = (int)((a.D + kCols - 1) / kCols);
     const int n_prod = a.ks * max_tiles;
@@ -863,6 +867,8 @@ hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream
 {
     if (max_tiles <= 0)
         return hipSuccess;
+    if (!ks_ok(a.ks))
+        return hipErrorInvalidValue;
     const dim3 grid(a.ks, max_tiles);
     const bool tall = a.sgmv_rows > kBgmvTileRows;   // 64-row dense tiles
     if (dtype == DT_BF16) {
@@ -879,7 +885,7 @@ hipError_t launch_shrink(int dtype, const ApplyArgs &a, int max_tiles, hipStream
 hipError_t launch_build_shrink(int dtype, const ApplyArgs &a, const SegBuildArgs &sb, int max_tiles,
                                hipStream_t stream)
 {
-    if (max_tiles <= 0 || sb.n > kGroupRows || sb.sgmv_rows != kBgmvTileRows)
+    if (max_tiles <= 0 || sb.n > kGroupRows || sb.sgmv_rows != kBgmvTileRows || !ks_ok(a.ks))
         return hipErrorInvalidValue;
     const dim3 grid(a.ks, max_tiles);
     if (dtype == DT_BF16)
