@@ -307,10 +307,14 @@ __device__ __forceinline__ void dec_shrink(const DecodeArgs &a, int t, int ks, c
 }
 
 // Expand of tile (s, rows) over column group cg (CPW quads of 64 columns per
-// wavefront).  Returns false when the wait gave up.
+// wavefront).  Once every thread's v is in LDS, thread 0 counts the workgroup
+// on the tile's counter at `count` (its previous value into `seen`), so the
+// count's round trip overlaps the products and y's merge.  Returns false when
+// the wait gave up.
 template <int KS, int CPW>
 __device__ __forceinline__ bool dec_expand(const DecodeArgs &a, int t, int cg, const DecPlan &P,
-                                           DecLds &L, uint32_t tag, float scale, int r)
+                                           DecLds &L, uint32_t tag, float scale, int r, int32_t *count,
+                                           int &seen)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -388,6 +392,12 @@ __device__ __forceinline__ bool dec_expand(const DecodeArgs &a, int t, int cg, c
         L.gave_up = 1;
     lds_barrier();
     const bool give_up = L.gave_up != 0;
+    // every thread is done with its v words: this workgroup counts itself
+    if (tid == 0) {
+        if (give_up && a.timeouts)
+            __hip_atomic_fetch_add(a.timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        seen = __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // v operand: row n, K = [16 ranks of hi | the same 16 of lo]; lane group g
     // takes ranks 8 (g & 1) .. + 7 of hi (g < 2) or lo (g >= 2)
     const float4 va = *reinterpret_cast<const float4 *>(&L.vs[n][8 * (g & 1)]);
@@ -473,13 +483,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     } else if (tile_ok && poisoned == 0) {
         const int r = __shfl(rk_l, P.s);
         const float scale = __shfl(sc_l, P.s);
-        const bool ok = dec_expand<KS, CPW>(a, t, part, P, L, tag, scale, r);
+        int seen = -1;
+        dec_expand<KS, CPW>(a, t, part, P, L, tag, scale, r, st + kDecCount, seen);
+        // every expand workgroup of the tile counted itself once done with its
+        // v: the last to count advances the tile's epoch
         if (tid == 0) {
-            if (!ok && a.timeouts)
-                __hip_atomic_fetch_add(a.timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // every expand workgroup of the tile is done with its v: the last
-            // advances the tile's epoch
-            const int seen = __hip_atomic_fetch_add(st + kDecCount, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (seen == a.ncg - 1) {
                 __hip_atomic_store(st + kDecCount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(st + kDecEpoch + kClass, epoch + 1, __ATOMIC_RELAXED,
