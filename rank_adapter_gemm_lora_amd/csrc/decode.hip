@@ -236,8 +236,9 @@ __device__ __forceinline__ uint32_t *class_words(const DecodeArgs &a)
 // contiguous run of 2 lines per 8-element unit (16 rank rows x 16 bytes; this
 // kernel serves r_max <= 16, so each slot is one 16-row block).  Issued after
 // every other load of the workgroup's start (vector loads complete in order,
-// so waiting for those does not wait for this one) and consumed at the end.  Threads without a line load the
-// split's first line of x row 0 again.  Returns the address to load.
+// so waiting for those does not wait for this one) and consumed at the end.
+// Threads without a line load the split's first line of x row 0 again.
+// Returns the address to load.
 template <int KS>
 __device__ __forceinline__ const uint32_t *dec_prefetch(const DecodeArgs &a, int t, int ks)
 {

@@ -688,7 +688,8 @@ lora_status lora_segments_create(lora_segments **out, int64_t max_rows, int n_sl
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->tiles), sizeof(ShrinkTile) * seg->max_tiles);
     const int64_t n_chunks = (max_rows + kChunkRows - 1) / kChunkRows;
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->keys), sizeof(int32_t) * max_rows);
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->chunk), sizeof(int32_t) * n_chunks * (n_slots + 1));
+    if (e == hipSuccess)
+        e = hipMalloc(reinterpret_cast<void **>(&seg->chunk), sizeof(int32_t) * n_chunks * (n_slots + 1));
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->chunk_bad), sizeof(int32_t) * n_chunks);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&seg->binfo), sizeof(int4) * (n_slots + 1));
     const size_t sync_ints = kSyncFlags + (size_t)seg->max_tiles * kSyncTileInts;
