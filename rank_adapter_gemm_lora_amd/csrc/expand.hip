@@ -210,7 +210,8 @@ __global__ __launch_bounds__(256) void expand_stream_kernel(ApplyArgs a)
     const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
     const bool table = a.n_slots <= kExpandTableSlots;
     if (table) {
-        for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x) {
+#pragma unroll 1
+        for (int e = threadIdx.x; e < a.n_slots; e += kApplyThreads) {
             srank[e] = a.rank[e];
             sscale[e] = a.scale[e];
         }
@@ -253,6 +254,12 @@ void expand_kernel_bf16_short(ApplyArgs a)
 
 // ------------------------------------------------ SGMV, runs of chunks
 
+// s_waitcnt immediates (gfx9 encoding, vmcnt split over bits 3:0 and 15:14):
+// this wavefront's LDS accesses drained, or its vector-memory accesses drained
+// (global-to-LDS copies included); the other counters are not waited on.
+constexpr int kWaitLds = 0xC07F;
+constexpr int kWaitVm = 0x0F70;
+
 // The one-chunk expand's work (16-row MFMA tiles, every group dense) on a grid
 // that fits the chip at once, organised so that v is prepared once per tile
 // rather than once per 256-column chunk.  The units of work are the (tile,
@@ -267,7 +274,9 @@ void expand_kernel_bf16_short(ApplyArgs a)
 // first chunk's y and B loads in flight (only the slices the run touches);
 // each wavefront turns its slice's v
 // into the bf16 hi / lo MFMA operands in registers, and the chunks then only
-// stream B (LDS) and y (registers).  The arithmetic is the one-chunk kernel's
+// stream B (LDS) and y (registers).  Each wavefront copies into LDS and reads
+// only its own 64 columns of a B chunk, so past the tile's v the wavefronts
+// run their chunks without waiting for each other.  The arithmetic is the one-chunk kernel's
 // (same operands, same order), so the results are bit-identical to it.
 //
 // Dynamic LDS (offsets from the host): the slot table, v of the current tile
@@ -303,7 +312,8 @@ void expand_run_kernel(ApplyArgs a)
                                          : make_int4(0, 0, 0, 0);
         th[i] = make_int2(hd.x, hd.z);
     }
-    for (int e = tid; e < a.n_slots; e += blockDim.x) {
+#pragma unroll 1
+    for (int e = tid; e < a.n_slots; e += kApplyThreads) {
         srank[e] = a.rank[e];
         sscale[e] = a.scale[e];
     }
@@ -418,19 +428,20 @@ void expand_run_kernel(ApplyArgs a)
                 y0.load(a.y, yrow + cb);
                 y1.load(a.y, yrow + cb + kHalf);
             }
-            // the chunk's contiguous [ncol][rp] B block, global -> LDS, 16 bytes a lane
-            {
+            // this wavefront's 64 columns of the chunk's [ncol][rp] B block (one
+            // contiguous 128 rp bytes), global -> LDS, 16 bytes a lane, into the
+            // part of the block that only this wavefront reads: no workgroup
+            // barrier orders B, and the wavefronts do not wait for each other
+            // between chunks.  Its LDS reads of the last chunk are done first.
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            if (in_d) {
                 const int gpw = rp >> 3;
-                const int n_gran = (int)min((int64_t)kCols, a.D - c0) * gpw;
-                const uint16_t *src = static_cast<const uint16_t *>(a.B) + bslot + c0 * rp;
-                for (int i = 0; i < gpw; ++i) {
-                    const int e = i * kCols + tid;
-                    if (e < n_gran)
-                        __builtin_amdgcn_global_load_lds(
-                            (const __attribute__((address_space(1))) void *)(src + 8 * (int64_t)e),
-                            (__attribute__((address_space(3))) void *)(bs + 8 * (i * kCols + 64 * wave)), 16,
-                            0, 0);
-                }
+                const uint16_t *src = static_cast<const uint16_t *>(a.B) + bslot + cw * rp + 8 * lane;
+                uint16_t *dst = bs + 64 * wave * rp;
+                for (int i = 0; i < gpw; ++i)
+                    __builtin_amdgcn_global_load_lds(
+                        (const __attribute__((address_space(1))) void *)(src + 512 * i),
+                        (__attribute__((address_space(3))) void *)(dst + 512 * i), 16, 0, 0);
             }
             if (c == c_begin) {
                 // v of the tile for those slices, summed over the k-splits in
@@ -451,7 +462,11 @@ void expand_run_kernel(ApplyArgs a)
                     }
                 }
             }
-            __syncthreads();   // the B chunk (and y) landed
+            // this wavefront's B columns landed in LDS, and its y in registers
+            // (waited on every path: otherwise the compiler, which does not know
+            // in_d to be uniform, drains the last chunk's y stores before the
+            // next chunk's loads)
+            __builtin_amdgcn_s_waitcnt(kWaitVm);
             if (in_d) {
                 f32x4_t acc[4];
 #pragma unroll
@@ -483,7 +498,6 @@ void expand_run_kernel(ApplyArgs a)
                     merge16<DT_BF16>(a, yrow + cb, true, true, y0, y1, scale, f, kHalf);
                 }
             }
-            lds_barrier();   // every wavefront is done with the chunk's B
         }
     }
 }

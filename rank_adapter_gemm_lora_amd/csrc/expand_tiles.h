@@ -78,8 +78,9 @@ __device__ __forceinline__ float load_v(const float *p)
 // per thread in flight (8 / KS elements, every split of each; 16 splits go in
 // two batches of 8) before the first add, so a tile's v costs one round trip
 // per pass.  Indexes past the tile are clamped to its last element (read, not
-// stored).
-template <int KS, bool COH>
+// stored).  NT: the workgroup's thread count when fixed at compile time (the
+// 64-row tiles measured faster so), else 0 (read at run time).
+template <int KS, bool COH, int NT>
 __device__ __forceinline__ void stage_v_ks(const ApplyArgs &a, int p0, int cnt, int r, int q_lo,
                                            int nq, float *vs)
 {
@@ -89,11 +90,11 @@ __device__ __forceinline__ void stage_v_ks(const ApplyArgs &a, int p0, int cnt, 
     const int rp8 = (r + 7) & ~7, P = v_pitch(nq, rp8);
     const int64_t split = a.max_rows * (int64_t)SR;
     const uint32_t m_pitch = div_magic(pitch), m_r = div_magic(r);   // cnt * pitch <= 2^14
-    for (int base = 0; base < total; base += kE * (int)blockDim.x) {
+    for (int base = 0; base < total; base += kE * (NT > 0 ? NT : (int)blockDim.x)) {
         const float *src[kE];
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
-            const int idx = min(base + e * (int)blockDim.x + (int)threadIdx.x, total - 1);
+            const int idx = min(base + e * (NT > 0 ? NT : (int)blockDim.x) + (int)threadIdx.x, total - 1);
             const int u = div_small(idx, m_pitch);
             const int rem = idx - u * pitch;
             const int qq = div_small(rem, m_r);
@@ -117,7 +118,7 @@ __device__ __forceinline__ void stage_v_ks(const ApplyArgs &a, int p0, int cnt, 
         }
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
-            const int idx = base + e * (int)blockDim.x + (int)threadIdx.x;
+            const int idx = base + e * (NT > 0 ? NT : (int)blockDim.x) + (int)threadIdx.x;
             if (idx < total) {
                 // (the decomposition again: cheaper than holding it across the loads)
                 const int u = div_small(idx, m_pitch);
@@ -146,7 +147,8 @@ __device__ __forceinline__ void stage_v4_ks(const ApplyArgs &a, int p0, int cnt,
     const int rp8 = (r + 7) & ~7, P = v_pitch(nq, rp8);
     const int64_t split = a.max_rows * (int64_t)SR;   // floats of one split
     const uint32_t m_row = div_magic(per_row), m_g4 = div_magic(g4);   // total <= 2^14
-    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+#pragma unroll 1
+    for (int idx = threadIdx.x; idx < total; idx += kApplyThreads) {
         const int u = div_small(idx, m_row);
         const int rem = idx - u * per_row;
         const int qq = div_small(rem, m_g4);
@@ -194,16 +196,16 @@ __device__ __forceinline__ void stage_v4(const ApplyArgs &a, int p0, int cnt, in
     }
 }
 
-template <bool COH = false>
+template <bool COH = false, int NT = 0>
 __device__ __forceinline__ void stage_v(const ApplyArgs &a, int p0, int cnt, int r, int q_lo,
                                         int nq, float *vs)
 {
     switch (a.ks) {
-    case 1: stage_v_ks<1, COH>(a, p0, cnt, r, q_lo, nq, vs); break;
-    case 2: stage_v_ks<2, COH>(a, p0, cnt, r, q_lo, nq, vs); break;
-    case 4: stage_v_ks<4, COH>(a, p0, cnt, r, q_lo, nq, vs); break;
-    case 8: stage_v_ks<8, COH>(a, p0, cnt, r, q_lo, nq, vs); break;
-    default: stage_v_ks<16, COH>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 1: stage_v_ks<1, COH, NT>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 2: stage_v_ks<2, COH, NT>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 4: stage_v_ks<4, COH, NT>(a, p0, cnt, r, q_lo, nq, vs); break;
+    case 8: stage_v_ks<8, COH, NT>(a, p0, cnt, r, q_lo, nq, vs); break;
+    default: stage_v_ks<16, COH, NT>(a, p0, cnt, r, q_lo, nq, vs); break;
     }
 }
 
@@ -325,7 +327,7 @@ __device__ void sgmv_expand_tile(const ApplyArgs &a, const int32_t *rows, int s,
     const int nq = slice_of(a, min(c0 + kCols, a.D) - 1) - q_lo + 1;
     const int P = v_pitch(nq, rp);
     wait();
-    stage_v<COH>(a, p0, cnt, r, q_lo, nq, vs);
+    stage_v<COH, (MT == 4 ? kApplyThreads : 0)>(a, p0, cnt, r, q_lo, nq, vs);
     __syncthreads();   // B (first window) and v staged
     const bool keep = v_read();   // false: the wait gave up, y stays untouched
     const int qq = slice_of(a, c0 + 64 * wave) - q_lo;
@@ -587,7 +589,8 @@ __device__ __forceinline__ bool expand_body(const ApplyArgs &a, int t, int chunk
     const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
     const bool table = a.n_slots <= kExpandTableSlots;
     if (table) {
-        for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x) {
+#pragma unroll 1
+        for (int e = threadIdx.x; e < a.n_slots; e += kApplyThreads) {
             srank[e] = a.rank[e];
             sscale[e] = a.scale[e];
         }

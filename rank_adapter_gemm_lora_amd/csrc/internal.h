@@ -16,6 +16,7 @@ enum : int { DT_F32 = 0, DT_BF16 = 1 };   // element types of x, y and the pool
 constexpr int kBgmvTileRows = 16;   // rows per BGMV shrink tile (small groups)
 constexpr int kSgmvTileRows = 64;   // rows per SGMV shrink tile (dense groups, MFMA)
 constexpr int kExpandCols = 256;    // output columns per expand workgroup
+constexpr int kApplyThreads = 256;  // threads of every shrink / expand / decode workgroup
 constexpr int kExpandLdsTable = 256;   // expand LDS: row indices first, then the slot table
 constexpr int kExpandTableSlots = 256; // slot table in LDS up to this many slots
 constexpr int kExpandLdsMax = 65536;   // dynamic LDS of one expand workgroup, at most

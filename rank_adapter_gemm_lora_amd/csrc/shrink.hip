@@ -575,7 +575,8 @@ __device__ __forceinline__ bool shrink_body(const ApplyArgs &a, int ks, int t)
     const int4 h = *reinterpret_cast<const int4 *>(T);
     const int32_t my_row = threadIdx.x < kSgmvTileRows ? T->rows[threadIdx.x] : 0;
     const int n_tiles = a.counts[kCntSgmv] + a.counts[kCntBgmv];
-    for (int e = threadIdx.x; e < a.n_slots; e += blockDim.x)
+#pragma unroll 1
+    for (int e = threadIdx.x; e < a.n_slots; e += kApplyThreads)
         rank[e] = a.rank[e];
     if (t >= n_tiles)
         return false;
